@@ -1,0 +1,184 @@
+/*
+ * libtpfuse — fused tensor-parallel Linear (GEMM + cross-shard reduction) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One GPU holds all p shards of a tensor-parallel layer ("simulated ranks"):
+ * the library computes every shard's local GEMM with bf16 matrix-core tiles,
+ * keeps each shard's fp32 local output (the message a rank would send) in a
+ * caller-provided workspace, and produces the cross-shard sum in the layout
+ * that the collective's semantics require.  The output is split into
+ * contiguous row chunks; the reduction of chunk c overlaps the GEMM of later
+ * chunks (a persistent kernel with per-chunk ready counters, or two HIP
+ * streams with per-chunk events).  The sum over shards is a left fold in
+ * shard order k = 0..p-1 in fp32, rounded once to the output type, so results
+ * are bit-identical for every chunk count and every scheduler.
+ *
+ * Sources (web pages, cited by title and section):
+ *  - ai-infra-kb M027 "compute-communication fusion" page, §01 (row-parallel
+ *    Linear: Y = Y_0 + Y_1; AllReduce vs ReduceScatter layouts; AllGather
+ *    then MatMul), §02 (MatMul->AllReduce chunked along output rows, the
+ *    reduction of chunk 1 overlapping the GEMM of chunk 2; AllGather->MatMul
+ *    computing once enough input blocks have arrived), §03 (same chunk order
+ *    on every rank, a ready signal per chunk, a final wait for all chunks),
+ *    §04 (measure the whole GEMM and the whole collective separately),
+ *    §06 (record workspace peak).
+ *  - cnblogs tensor-parallel tutorial (列并行与行并行的前向/反向传播), §2.3 / §三
+ *    (column shards, backward dX = sum_k dY_k A_k^T), §2.4 / §四 (row shards,
+ *    Y = sum_k X_k A_k), §2.5-2.7 (AllReduce, AllGather, ReduceScatter).
+ *
+ * Conventions for every call:
+ *  - All matrices are row-major and contiguous; inputs are bfloat16.
+ *  - Every device pointer must be 16-byte aligned; the reduction length and
+ *    the output width must be multiples of 8 elements.
+ *  - Pointer arrays (X[], W[], slices[]) are host arrays read during the call
+ *    only; the device buffers they name are owned by the caller.  The library
+ *    never allocates or frees caller memory.  Outputs must not alias inputs
+ *    or each other.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream) after any work already on it; the call returns without waiting.
+ *    Internal forks onto the handle's side stream join back into `stream`
+ *    before the call returns, so callers see single-stream semantics.
+ *  - A handle runs at most one call at a time; use one handle per concurrent
+ *    stream.
+ *  - Return value: TPF_OK (0) or a negative TPF_ERR_* code; the message of
+ *    the last failure on the calling thread is tpf_last_error().  Argument
+ *    checks run on the host before anything is enqueued; a failed check
+ *    enqueues nothing.  Arguments are checked before the handle, so the
+ *    checks work without a GPU.
+ */
+#ifndef TPFUSE_H
+#define TPFUSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TPF_VERSION 100          /* 1.0.0 */
+#define TPF_MAX_SHARDS 16        /* largest p accepted */
+#define TPF_MAX_CHUNKS 64        /* largest n_chunks accepted */
+
+/* Status codes. */
+#define TPF_OK 0
+#define TPF_ERR_INVALID_ARG -1   /* null pointer, unknown enum, bad handle */
+#define TPF_ERR_SHAPE -2         /* non-positive size, p or n_chunks out of range, M % p != 0 where required */
+#define TPF_ERR_ALIGNMENT -3     /* pointer not 16-byte aligned, N or K not a multiple of 8 */
+#define TPF_ERR_WORKSPACE -4     /* workspace missing or smaller than tpf_workspace_size() */
+#define TPF_ERR_UNSUPPORTED -5   /* valid request this build cannot run */
+#define TPF_ERR_HIP -6           /* a HIP runtime call failed (message in tpf_last_error) */
+#define TPF_ERR_TIMEOUT -7       /* a bounded wait inside the persistent kernel gave up */
+
+/* Output element type (inputs are always bfloat16). */
+#define TPF_BF16 0
+#define TPF_F32 1
+
+/* Schedulers.  Every scheduler computes the same bits. */
+#define TPF_SCHED_AUTO 0         /* library's choice (currently PERSISTENT) */
+#define TPF_SCHED_PERSISTENT 1   /* one persistent kernel: work queue + per-chunk ready counters */
+#define TPF_SCHED_TWO_STREAM 2   /* per-chunk GEMM launches, reductions on a side stream after per-chunk events */
+#define TPF_SCHED_UNFUSED 3      /* whole GEMM, then the whole reduction (the serial baseline) */
+#define TPF_SCHED_GEMM_ONLY 4    /* measurement: only the shard GEMMs (partials into the workspace; for
+                                    AllGather->MatMul: only the GEMM over an already gathered X) */
+#define TPF_SCHED_REDUCE_ONLY 5  /* measurement: only the reduction of partials already in the workspace
+                                    (for AllGather->MatMul: only the gather copy) */
+
+/* Output semantics of the column-parallel backward. */
+#define TPF_ALLREDUCE 0          /* one full [M, K_in] result */
+#define TPF_REDUCESCATTER 1      /* p row slices [M/p, K_in] */
+
+/* Operation ids for tpf_workspace_size. */
+#define TPF_OP_MATMUL_ALLREDUCE 0
+#define TPF_OP_MATMUL_REDUCESCATTER 1
+#define TPF_OP_ALLGATHER_MATMUL 2
+#define TPF_OP_MATMUL_DX 3
+
+typedef struct tpf_context* tpf_handle;
+
+/* Create a handle bound to HIP device `device`.  The handle owns a side
+ * stream (default priority), a pool of events and a small device control
+ * block (counters, status word); these are allocated here and released by
+ * tpf_destroy.  Returns TPF_ERR_HIP if the device cannot be used. */
+int tpf_create(tpf_handle* h, int device);
+
+/* Release a handle after all work enqueued with it has finished (the call
+ * synchronises the handle's side stream).  NULL is accepted. */
+int tpf_destroy(tpf_handle h);
+
+/* Bytes of workspace a call needs (0 if none), a pure function of its
+ * arguments.  For the reducing operations it is p * M * N * 4: one fp32
+ * local output [M, N] per shard (N = output width: N for the row-parallel
+ * ops, K_in for tpf_matmul_dx).  `K` is the per-shard reduction length.
+ * AllGather->MatMul needs none.  Returns 0 for invalid arguments. */
+size_t tpf_workspace_size(int op, int p, int64_t M, int64_t N, int64_t K, int n_chunks, int sched);
+
+/* MatMul -> AllReduce (row-parallel Linear, M027 page §01-§03; cnblogs §2.4).
+ *   X[k]: [M, K_shard] bf16, W[k]: [K_shard, N] bf16, k = 0..p-1.
+ *   Y:    [M, N], y_dtype (TPF_BF16 or TPF_F32).
+ *   Y = sum_{k=0}^{p-1} X[k] W[k], summed in fp32 in shard order, rounded once.
+ *   n_chunks in [1, min(M, TPF_MAX_CHUNKS)]: chunk c covers rows
+ *   [c*floor(M/n), (c+1)*floor(M/n)), the last chunk also takes the remainder.
+ *   ws/ws_bytes: at least tpf_workspace_size(TPF_OP_MATMUL_ALLREDUCE, ...). */
+int tpf_matmul_allreduce(tpf_handle h, int p, int64_t M, int64_t N, int64_t K_shard,
+                         const void* const* X, const void* const* W, void* Y, int y_dtype,
+                         int n_chunks, int sched, void* ws, size_t ws_bytes, void* stream);
+
+/* MatMul -> ReduceScatter (M027 page §01; cnblogs §2.7).
+ *   Same operands as tpf_matmul_allreduce; M % p == 0.
+ *   Y_slices[r] ([M/p, N], y_dtype), r = 0..p-1, receives rows
+ *   [r*M/p, (r+1)*M/p) of sum_k X[k] W[k]. */
+int tpf_matmul_reducescatter(tpf_handle h, int p, int64_t M, int64_t N, int64_t K_shard,
+                             const void* const* X, const void* const* W, void* const* Y_slices,
+                             int y_dtype, int n_chunks, int sched, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* AllGather -> MatMul (M027 page §01-§02; cnblogs §2.3, §2.6).
+ *   X_slices[r]: [M/p, K] bf16 (sequence slices, r = 0..p-1), M % p == 0.
+ *   W: [K, N_shard] bf16 (this rank's column shard).
+ *   X_gathered: [M, K] bf16 output, the slices concatenated in rank order.
+ *   Y: [M, N_shard] y_dtype output, Y = X_gathered W (no reduction).
+ *   Chunk c's GEMM starts once every slice overlapping its rows has landed
+ *   in X_gathered.  Needs no workspace (ws may be NULL). */
+int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_t K,
+                         const void* const* X_slices, const void* W, void* X_gathered, void* Y,
+                         int y_dtype, int n_chunks, int sched, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Column-parallel backward input gradient (cnblogs §三, §6.1, §6.4).
+ *   dY[k]: [M, N_shard] bf16, W[k]: [K_in, N_shard] bf16 (the forward's
+ *   column shard, used transposed), k = 0..p-1.
+ *   dX = sum_k dY[k] W[k]^T, summed in fp32 in shard order, rounded once.
+ *   sem == TPF_ALLREDUCE:     dX[0] is one [M, K_in] buffer.
+ *   sem == TPF_REDUCESCATTER: dX[r] ([M/p, K_in]) receives rows [r*M/p, (r+1)*M/p); M % p == 0.
+ *   ws_bytes >= tpf_workspace_size(TPF_OP_MATMUL_DX, p, M, K_in, N_shard, ...). */
+int tpf_matmul_dx(tpf_handle h, int sem, int p, int64_t M, int64_t K_in, int64_t N_shard,
+                  const void* const* dY, const void* const* W, void* const* dX, int dx_dtype,
+                  int n_chunks, int sched, void* ws, size_t ws_bytes, void* stream);
+
+/* Wait for the handle's work on `stream` to finish and report whether a
+ * bounded wait inside the persistent kernel gave up since the last query
+ * (TPF_ERR_TIMEOUT; the outputs of that call are then undefined).  Clears
+ * the flag.  Synchronises `stream`. */
+int tpf_sync_status(tpf_handle h, void* stream);
+
+/* Debug: bound the persistent kernel's waits to `spins` polls (0 restores
+ * the default).  With `unreachable` != 0 every wait targets a count that is
+ * never reached, so each wait ends by its bound: used to test the timeout
+ * path without any kernel hanging. */
+int tpf_debug_set_wait(tpf_handle h, int64_t spins, int unreachable);
+
+/* Static text for a status code. */
+const char* tpf_status_string(int code);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* tpf_last_error(void);
+
+/* TPF_VERSION of the built library. */
+int tpf_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPFUSE_H */

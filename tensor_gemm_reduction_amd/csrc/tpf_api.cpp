@@ -1,0 +1,550 @@
+// C ABI of libtpfuse: argument checks, workspace sizing, handles and the three
+// schedulers (persistent, two-stream, unfused) plus the measurement modes.
+//
+// Chunking follows the M027 page §02-§03: the output rows are cut into
+// contiguous chunks processed in the same order everywhere; each chunk's
+// reduction may start as soon as that chunk's shard GEMMs are done, while the
+// GEMMs of later chunks continue.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/tpfuse.h"
+#include "tpf_internal.hpp"
+
+using namespace tpf;
+
+static_assert(TPF_MAX_SHARDS == kMaxShards, "shard limit mismatch");
+static_assert(TPF_MAX_CHUNKS == kMaxChunks, "chunk limit mismatch");
+
+struct tpf_context {
+  int device = 0;
+  int num_cus = 0;
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  hipEvent_t ev_chunk[kMaxChunks] = {};
+  hipEvent_t ev_slice[kMaxShards] = {};
+  Ctrl* ctrl = nullptr;
+  int64_t spin_limit = 0;
+  int unreachable = 0;
+};
+
+namespace {
+
+constexpr int64_t kDefaultSpinLimit = (int64_t)1 << 26;   // polls; each poll sleeps ~100 cycles
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TPF_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define TPF_HIP(call)                                  \
+  do {                                                 \
+    hipError_t e_ = (call);                            \
+    if (e_ != hipSuccess) return hip_fail(e_, #call);  \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_sched(int s) { return s >= TPF_SCHED_AUTO && s <= TPF_SCHED_REDUCE_ONLY; }
+bool valid_dtype(int d) { return d == TPF_BF16 || d == TPF_F32; }
+
+int out_kind(int dtype) { return dtype == TPF_F32 ? OUT_F32 : OUT_BF16; }
+
+// Tile configuration from the op's total shape only.
+int pick_cfg(int64_t M) { return M <= 64 ? CFG_SMALL : CFG_LARGE; }
+
+// Common checks of sizes, chunking, dtype and scheduler.
+int check_common(int p, int64_t M, int64_t N, int64_t K, int n_chunks, int dtype, int sched, bool need_div) {
+  if (p < 1 || p > kMaxShards) return fail(TPF_ERR_SHAPE, "p must be in [1, " + std::to_string(kMaxShards) + "]");
+  if (M <= 0 || N <= 0 || K <= 0) return fail(TPF_ERR_SHAPE, "M, N and K must be positive");
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(TPF_ERR_SHAPE, "M, N and K must fit in 31 bits");
+  if (M * N > ((int64_t)1 << 40) || M * K > ((int64_t)1 << 40) || N * K > ((int64_t)1 << 40))
+    return fail(TPF_ERR_SHAPE, "operand too large");
+  if (need_div && M % p != 0) return fail(TPF_ERR_SHAPE, "M must be divisible by p for this layout");
+  if (n_chunks < 1 || n_chunks > kMaxChunks || n_chunks > M)
+    return fail(TPF_ERR_SHAPE, "n_chunks must be in [1, min(M, " + std::to_string(kMaxChunks) + ")]");
+  if (N % 8 != 0 || K % 8 != 0) return fail(TPF_ERR_ALIGNMENT, "N and K must be multiples of 8");
+  if (!valid_dtype(dtype)) return fail(TPF_ERR_INVALID_ARG, "unknown output dtype");
+  if (!valid_sched(sched)) return fail(TPF_ERR_INVALID_ARG, "unknown scheduler");
+  return TPF_OK;
+}
+
+int check_ptrs(const void* const* arr, int count, const char* name) {
+  if (!arr) return fail(TPF_ERR_INVALID_ARG, std::string(name) + " array is NULL");
+  for (int i = 0; i < count; ++i) {
+    if (!arr[i]) return fail(TPF_ERR_INVALID_ARG, std::string(name) + "[" + std::to_string(i) + "] is NULL");
+    if (!aligned16(arr[i]))
+      return fail(TPF_ERR_ALIGNMENT, std::string(name) + "[" + std::to_string(i) + "] is not 16-byte aligned");
+  }
+  return TPF_OK;
+}
+
+int check_ptr(const void* ptr, const char* name) {
+  if (!ptr) return fail(TPF_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned16(ptr)) return fail(TPF_ERR_ALIGNMENT, std::string(name) + " is not 16-byte aligned");
+  return TPF_OK;
+}
+
+size_t partial_bytes(int p, int64_t M, int64_t N) { return (size_t)p * (size_t)M * (size_t)N * sizeof(float); }
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return TPF_OK;
+  if (!ws) return fail(TPF_ERR_WORKSPACE, "workspace is NULL but " + std::to_string(need) + " bytes are needed");
+  if (!aligned16(ws)) return fail(TPF_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(TPF_ERR_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, needs " + std::to_string(need));
+  return TPF_OK;
+}
+
+int check_handle(tpf_handle h) {
+  if (!h) return fail(TPF_ERR_INVALID_ARG, "handle is NULL");
+  return TPF_OK;
+}
+
+int resolve_sched(int sched) { return sched == TPF_SCHED_AUTO ? TPF_SCHED_PERSISTENT : sched; }
+
+// A reducing op (row-parallel AR/RS, or dX with either semantic).
+struct ReduceCall {
+  int p, M, N, K;
+  int bl;                       // B_KN (forward weights) or B_NK (dX: weights used transposed)
+  const void* const* A;
+  const void* const* B;
+  ReduceOut ro;
+  int n_chunks, sched;
+  float* P;
+};
+
+int set_device(tpf_handle h) {
+  TPF_HIP(hipSetDevice(h->device));
+  return TPF_OK;
+}
+
+int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
+  int st = set_device(h);
+  if (st) return st;
+  const int cfg = pick_cfg(rc.M);
+  GemmOperands g{};
+  for (int k = 0; k < rc.p; ++k) {
+    g.A[k] = reinterpret_cast<const __bf16*>(rc.A[k]);
+    g.B[k] = reinterpret_cast<const __bf16*>(rc.B[k]);
+  }
+  g.lda = rc.K;
+  g.ldb = rc.bl == B_KN ? rc.N : rc.K;
+  g.dst = rc.P;
+  g.dst_shard_stride = (int64_t)rc.M * rc.N;
+  g.ldd = rc.N;
+  g.dst_dtype = OUT_F32;
+  g.M = rc.M;
+  g.N = rc.N;
+  g.K = rc.K;
+  g.nshard = rc.p;
+  ChunkGeom ch{rc.n_chunks, rc.M / rc.n_chunks, rc.M};
+  const int64_t stride = (int64_t)rc.M * rc.N;
+
+  switch (rc.sched) {
+    case TPF_SCHED_GEMM_ONLY:
+      TPF_HIP(launch_gemm_rows(cfg, rc.bl, g, 0, rc.M, stream));
+      return TPF_OK;
+    case TPF_SCHED_REDUCE_ONLY:
+      TPF_HIP(launch_reduce_rows(rc.P, stride, rc.p, 0, rc.M, rc.N, rc.ro, h->num_cus, stream));
+      return TPF_OK;
+    case TPF_SCHED_UNFUSED:
+      TPF_HIP(launch_gemm_rows(cfg, rc.bl, g, 0, rc.M, stream));
+      TPF_HIP(launch_reduce_rows(rc.P, stride, rc.p, 0, rc.M, rc.N, rc.ro, h->num_cus, stream));
+      return TPF_OK;
+    case TPF_SCHED_TWO_STREAM: {
+      TPF_HIP(hipEventRecord(h->ev_fork, stream));
+      TPF_HIP(hipStreamWaitEvent(h->side, h->ev_fork, 0));
+      for (int c = 0; c < ch.n; ++c) {
+        TPF_HIP(launch_gemm_rows(cfg, rc.bl, g, ch.row0(c), ch.row1(c), stream));
+        TPF_HIP(hipEventRecord(h->ev_chunk[c], stream));
+        TPF_HIP(hipStreamWaitEvent(h->side, h->ev_chunk[c], 0));
+        TPF_HIP(launch_reduce_rows(rc.P, stride, rc.p, ch.row0(c), ch.row1(c), rc.N, rc.ro, h->num_cus, h->side));
+      }
+      TPF_HIP(hipEventRecord(h->ev_join, h->side));
+      TPF_HIP(hipStreamWaitEvent(stream, h->ev_join, 0));
+      return TPF_OK;
+    }
+    case TPF_SCHED_PERSISTENT: {
+      FusedArgs a{};
+      a.g = g;
+      a.ro = rc.ro;
+      a.P = rc.P;
+      a.p_stride = stride;
+      a.p = rc.p;
+      // Reduce tasks of about 64 Ki elements per shard (256 KiB of fp32 partials each).
+      a.reduce_rows = std::max(1, (int)(65536 / rc.N));
+      a.gather = 0;
+      a.ch = ch;
+      a.ctrl = h->ctrl;
+      a.spin_limit = h->spin_limit > 0 ? h->spin_limit : kDefaultSpinLimit;
+      a.unreachable = h->unreachable;
+      const int bm = cfg_bm(cfg), bn = cfg_bn(cfg);
+      const int tiles_n = (rc.N + bn - 1) / bn;
+      // Queue order: G0, G1, R0, G2, R1, ..., G(n-1), R(n-2), R(n-1).
+      int nseg = 0, t = 0;
+      auto add_seg = [&](int kind, int idx, int count) {
+        a.seg_start[nseg] = t;
+        a.seg_info[nseg] = kind | (idx << 4);
+        t += count;
+        ++nseg;
+      };
+      auto gemm_count = [&](int c) { return rc.p * ((ch.row1(c) - ch.row0(c) + bm - 1) / bm) * tiles_n; };
+      auto red_count = [&](int c) { return (ch.row1(c) - ch.row0(c) + a.reduce_rows - 1) / a.reduce_rows; };
+      for (int c = 0; c < ch.n; ++c) a.gemm_tasks[c] = gemm_count(c);
+      add_seg(TK_GEMM, 0, gemm_count(0));
+      for (int c = 1; c < ch.n; ++c) {
+        add_seg(TK_GEMM, c, gemm_count(c));
+        add_seg(TK_REDUCE, c - 1, red_count(c - 1));
+      }
+      add_seg(TK_REDUCE, ch.n - 1, red_count(ch.n - 1));
+      a.nseg = nseg;
+      a.seg_start[nseg] = t;
+      const int grid = std::min(t, h->num_cus);
+      TPF_HIP(launch_fused(cfg, rc.bl, a, grid, stream));
+      return TPF_OK;
+    }
+  }
+  return fail(TPF_ERR_INVALID_ARG, "unknown scheduler");
+}
+
+}  // namespace
+
+extern "C" {
+
+int tpf_version(void) { return TPF_VERSION; }
+
+const char* tpf_last_error(void) { return g_last_error.c_str(); }
+
+const char* tpf_status_string(int code) {
+  switch (code) {
+    case TPF_OK: return "success";
+    case TPF_ERR_INVALID_ARG: return "invalid argument";
+    case TPF_ERR_SHAPE: return "invalid shape";
+    case TPF_ERR_ALIGNMENT: return "misaligned pointer or size";
+    case TPF_ERR_WORKSPACE: return "workspace missing or too small";
+    case TPF_ERR_UNSUPPORTED: return "unsupported request";
+    case TPF_ERR_HIP: return "HIP runtime error";
+    case TPF_ERR_TIMEOUT: return "bounded wait timed out";
+    default: return "unknown status";
+  }
+}
+
+int tpf_create(tpf_handle* out, int device) {
+  if (!out) return fail(TPF_ERR_INVALID_ARG, "handle pointer is NULL");
+  *out = nullptr;
+  int count = 0;
+  TPF_HIP(hipGetDeviceCount(&count));
+  if (device < 0 || device >= count) return fail(TPF_ERR_INVALID_ARG, "no such device");
+  tpf_context* h = new (std::nothrow) tpf_context();
+  if (!h) return fail(TPF_ERR_INVALID_ARG, "out of host memory");
+  h->device = device;
+  auto cleanup = [&](int code) {
+    tpf_destroy(h);
+    return code;
+  };
+  hipError_t e = hipSetDevice(device);
+  if (e != hipSuccess) return cleanup(hip_fail(e, "hipSetDevice"));
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return cleanup(hip_fail(e, "hipGetDeviceProperties"));
+  h->num_cus = prop.multiProcessorCount;
+  e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+  if (e != hipSuccess) return cleanup(hip_fail(e, "hipStreamCreateWithFlags"));
+  e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming);
+  for (int c = 0; c < kMaxChunks && e == hipSuccess; ++c) e = hipEventCreateWithFlags(&h->ev_chunk[c], hipEventDisableTiming);
+  for (int s = 0; s < kMaxShards && e == hipSuccess; ++s) e = hipEventCreateWithFlags(&h->ev_slice[s], hipEventDisableTiming);
+  if (e != hipSuccess) return cleanup(hip_fail(e, "hipEventCreateWithFlags"));
+  e = hipMalloc(reinterpret_cast<void**>(&h->ctrl), sizeof(Ctrl));
+  if (e != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(control block)"));
+  e = hipMemset(h->ctrl, 0, sizeof(Ctrl));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return cleanup(hip_fail(e, "hipMemset(control block)"));
+  *out = h;
+  return TPF_OK;
+}
+
+int tpf_destroy(tpf_handle h) {
+  if (!h) return TPF_OK;
+  (void)hipSetDevice(h->device);
+  if (h->side) (void)hipStreamSynchronize(h->side);
+  if (h->ctrl) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(h->ctrl);
+  }
+  for (auto& ev : h->ev_chunk)
+    if (ev) (void)hipEventDestroy(ev);
+  for (auto& ev : h->ev_slice)
+    if (ev) (void)hipEventDestroy(ev);
+  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+  if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+  if (h->side) (void)hipStreamDestroy(h->side);
+  delete h;
+  return TPF_OK;
+}
+
+size_t tpf_workspace_size(int op, int p, int64_t M, int64_t N, int64_t K, int n_chunks, int sched) {
+  const bool div = op == TPF_OP_MATMUL_REDUCESCATTER || op == TPF_OP_ALLGATHER_MATMUL;
+  std::string saved = g_last_error;
+  int st = check_common(p, M, N, K, n_chunks, TPF_BF16, sched, div);
+  g_last_error = saved;
+  if (st != TPF_OK) return 0;
+  switch (op) {
+    case TPF_OP_MATMUL_ALLREDUCE:
+    case TPF_OP_MATMUL_REDUCESCATTER:
+    case TPF_OP_MATMUL_DX:
+      return partial_bytes(p, M, N);
+    case TPF_OP_ALLGATHER_MATMUL:
+      return 0;
+    default:
+      return 0;
+  }
+}
+
+int tpf_matmul_allreduce(tpf_handle h, int p, int64_t M, int64_t N, int64_t K_shard, const void* const* X,
+                         const void* const* W, void* Y, int y_dtype, int n_chunks, int sched, void* ws,
+                         size_t ws_bytes, void* stream) {
+  int st = check_common(p, M, N, K_shard, n_chunks, y_dtype, sched, false);
+  if (st) return st;
+  if ((st = check_ptrs(X, p, "X"))) return st;
+  if ((st = check_ptrs(W, p, "W"))) return st;
+  if ((st = check_ptr(Y, "Y"))) return st;
+  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, M, N)))) return st;
+  if ((st = check_handle(h))) return st;
+  ReduceCall rc{};
+  rc.p = p;
+  rc.M = (int)M;
+  rc.N = (int)N;
+  rc.K = (int)K_shard;
+  rc.bl = B_KN;
+  rc.A = X;
+  rc.B = W;
+  rc.ro.y[0] = Y;
+  rc.ro.scatter = 0;
+  rc.ro.rows_per_slice = (int)M;
+  rc.ro.dtype = out_kind(y_dtype);
+  rc.n_chunks = n_chunks;
+  rc.sched = resolve_sched(sched);
+  rc.P = reinterpret_cast<float*>(ws);
+  return run_reduce_call(h, rc, reinterpret_cast<hipStream_t>(stream));
+}
+
+int tpf_matmul_reducescatter(tpf_handle h, int p, int64_t M, int64_t N, int64_t K_shard, const void* const* X,
+                             const void* const* W, void* const* Y_slices, int y_dtype, int n_chunks, int sched,
+                             void* ws, size_t ws_bytes, void* stream) {
+  int st = check_common(p, M, N, K_shard, n_chunks, y_dtype, sched, true);
+  if (st) return st;
+  if ((st = check_ptrs(X, p, "X"))) return st;
+  if ((st = check_ptrs(W, p, "W"))) return st;
+  if ((st = check_ptrs(Y_slices, p, "Y_slices"))) return st;
+  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, M, N)))) return st;
+  if ((st = check_handle(h))) return st;
+  ReduceCall rc{};
+  rc.p = p;
+  rc.M = (int)M;
+  rc.N = (int)N;
+  rc.K = (int)K_shard;
+  rc.bl = B_KN;
+  rc.A = X;
+  rc.B = W;
+  for (int r = 0; r < p; ++r) rc.ro.y[r] = Y_slices[r];
+  rc.ro.scatter = 1;
+  rc.ro.rows_per_slice = (int)(M / p);
+  rc.ro.dtype = out_kind(y_dtype);
+  rc.n_chunks = n_chunks;
+  rc.sched = resolve_sched(sched);
+  rc.P = reinterpret_cast<float*>(ws);
+  return run_reduce_call(h, rc, reinterpret_cast<hipStream_t>(stream));
+}
+
+int tpf_matmul_dx(tpf_handle h, int sem, int p, int64_t M, int64_t K_in, int64_t N_shard, const void* const* dY,
+                  const void* const* W, void* const* dX, int dx_dtype, int n_chunks, int sched, void* ws,
+                  size_t ws_bytes, void* stream) {
+  if (sem != TPF_ALLREDUCE && sem != TPF_REDUCESCATTER) return fail(TPF_ERR_INVALID_ARG, "unknown semantic");
+  const bool rs = sem == TPF_REDUCESCATTER;
+  int st = check_common(p, M, K_in, N_shard, n_chunks, dx_dtype, sched, rs);
+  if (st) return st;
+  if ((st = check_ptrs(dY, p, "dY"))) return st;
+  if ((st = check_ptrs(W, p, "W"))) return st;
+  if ((st = check_ptrs(dX, rs ? p : 1, "dX"))) return st;
+  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, M, K_in)))) return st;
+  if ((st = check_handle(h))) return st;
+  ReduceCall rc{};
+  rc.p = p;
+  rc.M = (int)M;
+  rc.N = (int)K_in;        // output width
+  rc.K = (int)N_shard;     // reduction length per shard
+  rc.bl = B_NK;
+  rc.A = dY;
+  rc.B = W;
+  for (int r = 0; r < (rs ? p : 1); ++r) rc.ro.y[r] = dX[r];
+  rc.ro.scatter = rs ? 1 : 0;
+  rc.ro.rows_per_slice = rs ? (int)(M / p) : (int)M;
+  rc.ro.dtype = out_kind(dx_dtype);
+  rc.n_chunks = n_chunks;
+  rc.sched = resolve_sched(sched);
+  rc.P = reinterpret_cast<float*>(ws);
+  return run_reduce_call(h, rc, reinterpret_cast<hipStream_t>(stream));
+}
+
+int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_t K, const void* const* X_slices,
+                         const void* W, void* X_gathered, void* Y, int y_dtype, int n_chunks, int sched, void* ws,
+                         size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_common(p, M, N_shard, K, n_chunks, y_dtype, sched, true);
+  if (st) return st;
+  if ((st = check_ptrs(X_slices, p, "X_slices"))) return st;
+  if ((st = check_ptr(W, "W"))) return st;
+  if ((st = check_ptr(X_gathered, "X_gathered"))) return st;
+  if ((st = check_ptr(Y, "Y"))) return st;
+  if ((st = check_handle(h))) return st;
+  if ((st = set_device(h))) return st;
+  hipStream_t stream_ = reinterpret_cast<hipStream_t>(stream);
+  const int Mi = (int)M, Ni = (int)N_shard, Ki = (int)K;
+  const int cfg = pick_cfg(M);
+  GemmOperands g{};
+  g.A[0] = reinterpret_cast<const __bf16*>(X_gathered);
+  g.B[0] = reinterpret_cast<const __bf16*>(W);
+  g.lda = Ki;
+  g.ldb = Ni;
+  g.dst = Y;
+  g.dst_shard_stride = 0;
+  g.ldd = Ni;
+  g.dst_dtype = out_kind(y_dtype);
+  g.M = Mi;
+  g.N = Ni;
+  g.K = Ki;
+  g.nshard = 1;
+  const int slice_rows = Mi / p;
+  const int64_t slice_bytes = (int64_t)slice_rows * Ki * 2;
+  char* xg = reinterpret_cast<char*>(X_gathered);
+  ChunkGeom ch{n_chunks, Mi / n_chunks, Mi};
+  const int s = resolve_sched(sched);
+  switch (s) {
+    case TPF_SCHED_GEMM_ONLY:
+      TPF_HIP(launch_gemm_rows(cfg, B_KN, g, 0, Mi, stream_));
+      return TPF_OK;
+    case TPF_SCHED_REDUCE_ONLY:
+      for (int r = 0; r < p; ++r)
+        TPF_HIP(launch_copy(reinterpret_cast<const char*>(X_slices[r]), xg + r * slice_bytes, slice_bytes, h->num_cus,
+                            stream_));
+      return TPF_OK;
+    case TPF_SCHED_UNFUSED:
+      for (int r = 0; r < p; ++r)
+        TPF_HIP(launch_copy(reinterpret_cast<const char*>(X_slices[r]), xg + r * slice_bytes, slice_bytes, h->num_cus,
+                            stream_));
+      TPF_HIP(launch_gemm_rows(cfg, B_KN, g, 0, Mi, stream_));
+      return TPF_OK;
+    case TPF_SCHED_TWO_STREAM: {
+      // Slices are copied on the side stream in rank order; chunk c's GEMM
+      // waits for the last slice under its rows.
+      TPF_HIP(hipEventRecord(h->ev_fork, stream_));
+      TPF_HIP(hipStreamWaitEvent(h->side, h->ev_fork, 0));
+      for (int r = 0; r < p; ++r) {
+        TPF_HIP(launch_copy(reinterpret_cast<const char*>(X_slices[r]), xg + r * slice_bytes, slice_bytes, h->num_cus,
+                            h->side));
+        TPF_HIP(hipEventRecord(h->ev_slice[r], h->side));
+      }
+      int waited = -1;
+      for (int c = 0; c < ch.n; ++c) {
+        const int last = (ch.row1(c) - 1) / slice_rows;
+        if (last > waited) {
+          TPF_HIP(hipStreamWaitEvent(stream_, h->ev_slice[last], 0));
+          waited = last;
+        }
+        TPF_HIP(launch_gemm_rows(cfg, B_KN, g, ch.row0(c), ch.row1(c), stream_));
+      }
+      return TPF_OK;
+    }
+    case TPF_SCHED_PERSISTENT: {
+      FusedArgs a{};
+      a.g = g;
+      a.p = 1;
+      a.gather = 1;
+      for (int r = 0; r < p; ++r) a.src[r] = reinterpret_cast<const char*>(X_slices[r]);
+      a.gathered = xg;
+      a.slice_bytes = slice_bytes;
+      a.slice_rows = slice_rows;
+      // Copy tasks of 256 KiB (rounded to 16 bytes).
+      const int64_t seg = std::min<int64_t>(slice_bytes, (int64_t)256 * 1024);
+      a.copy_seg_bytes = (seg + 15) / 16 * 16;
+      a.copy_segs = (int)((slice_bytes + a.copy_seg_bytes - 1) / a.copy_seg_bytes);
+      a.ch = ch;
+      a.ctrl = h->ctrl;
+      a.spin_limit = h->spin_limit > 0 ? h->spin_limit : kDefaultSpinLimit;
+      a.unreachable = h->unreachable;
+      const int bm = cfg_bm(cfg), bn = cfg_bn(cfg);
+      const int tiles_n = (Ni + bn - 1) / bn;
+      int nseg = 0, t = 0;
+      auto add_seg = [&](int kind, int idx, int count) {
+        a.seg_start[nseg] = t;
+        a.seg_info[nseg] = kind | (idx << 4);
+        t += count;
+        ++nseg;
+      };
+      // Copies of the slices under chunk c+1 are queued before chunk c's
+      // GEMM tiles, so the next transfer overlaps the current GEMM.
+      int copied = -1;
+      auto copy_upto = [&](int slice) {
+        while (copied < slice) {
+          ++copied;
+          add_seg(TK_COPY, copied, a.copy_segs);
+        }
+      };
+      copy_upto((ch.row1(0) - 1) / slice_rows);
+      for (int c = 0; c < ch.n; ++c) {
+        if (c + 1 < ch.n) copy_upto((ch.row1(c + 1) - 1) / slice_rows);
+        const int cnt = ((ch.row1(c) - ch.row0(c) + bm - 1) / bm) * tiles_n;
+        a.gemm_tasks[c] = cnt;
+        add_seg(TK_GEMM, c, cnt);
+      }
+      copy_upto(p - 1);
+      a.nseg = nseg;
+      a.seg_start[nseg] = t;
+      const int grid = std::min(t, h->num_cus);
+      TPF_HIP(launch_fused(cfg, B_KN, a, grid, stream_));
+      return TPF_OK;
+    }
+  }
+  return fail(TPF_ERR_INVALID_ARG, "unknown scheduler");
+}
+
+int tpf_sync_status(tpf_handle h, void* stream) {
+  int st = check_handle(h);
+  if (st) return st;
+  if ((st = set_device(h))) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int status = 0;
+  TPF_HIP(hipStreamSynchronize(s));
+  TPF_HIP(hipMemcpy(&status, &h->ctrl->status, sizeof(int), hipMemcpyDeviceToHost));
+  if (status) {
+    TPF_HIP(launch_clear_status(h->ctrl, s));
+    TPF_HIP(hipStreamSynchronize(s));
+    return fail(TPF_ERR_TIMEOUT, "a bounded wait in the persistent kernel gave up");
+  }
+  return TPF_OK;
+}
+
+int tpf_debug_set_wait(tpf_handle h, int64_t spins, int unreachable) {
+  int st = check_handle(h);
+  if (st) return st;
+  if (spins < 0) return fail(TPF_ERR_INVALID_ARG, "spins must be >= 0");
+  h->spin_limit = spins;
+  h->unreachable = unreachable ? 1 : 0;
+  return TPF_OK;
+}
+
+}  // extern "C"

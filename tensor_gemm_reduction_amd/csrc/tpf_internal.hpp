@@ -1,0 +1,93 @@
+// Host/device shared descriptions of a launch.  Plain structs passed by value
+// as kernel arguments (all well under the 4 KiB kernel-argument limit).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tpf_device.hpp"
+
+namespace tpf {
+
+constexpr int kMaxShards = 16;
+constexpr int kMaxChunks = 64;
+// GEMM and reduce segments per chunk, plus one copy segment per slice.
+constexpr int kMaxSegs = 2 * kMaxChunks + kMaxShards + 2;
+
+// Device control block owned by a handle.  All counters are zero between
+// calls: the last workgroup of the persistent kernel to finish clears them.
+struct Ctrl {
+  int ticket;                 // next task of the work queue
+  int done;                   // workgroups that have left the queue
+  int status;                 // sticky: bit 0 = a bounded wait gave up
+  int pad;
+  int ready[kMaxChunks];      // completed GEMM tiles per chunk
+  int landed[kMaxShards];     // copied segments per gathered slice
+};
+
+enum TaskKind : int { TK_GEMM = 0, TK_REDUCE = 1, TK_COPY = 2 };
+
+// The shard GEMMs of one call.  Tile (shard k, rows, cols) reads A[k] and
+// B[k] and writes dst + k * dst_shard_stride.
+struct GemmOperands {
+  const __bf16* A[kMaxShards];
+  const __bf16* B[kMaxShards];
+  int64_t lda, ldb;
+  void* dst;                  // fp32 partials (reducing ops) or the output (AllGather->MatMul)
+  int64_t dst_shard_stride;   // elements
+  int64_t ldd;
+  int dst_dtype;              // OUT_F32 or OUT_BF16
+  int M, N, K;                // rows, output width, reduction length per shard
+  int nshard;                 // shard GEMMs (p, or 1 for AllGather->MatMul)
+};
+
+struct ChunkGeom {
+  int n;       // number of chunks
+  int base;    // rows of every chunk but the last (floor(M / n))
+  int M;
+  __host__ __device__ int row0(int c) const { return c * base; }
+  __host__ __device__ int row1(int c) const { return c == n - 1 ? M : (c + 1) * base; }
+};
+
+struct FusedArgs {
+  GemmOperands g;
+  ReduceOut ro;
+  const float* P;             // partials (reducing ops)
+  int64_t p_stride;           // elements between shards' partials (M * N)
+  int p;                      // shards summed by the reduction
+  int reduce_rows;            // rows per reduce task
+  // AllGather: slice r (slice_bytes) is copied to gathered + r * slice_bytes
+  const char* src[kMaxShards];
+  char* gathered;
+  int64_t slice_bytes;
+  int64_t copy_seg_bytes;
+  int copy_segs;              // copy tasks per slice
+  int slice_rows;             // M / p
+  int gather;                 // 1 for AllGather->MatMul
+  ChunkGeom ch;
+  int nseg;
+  int seg_start[kMaxSegs + 1];   // first ticket of each segment; seg_start[nseg] = total tasks
+  int seg_info[kMaxSegs];        // kind | (chunk or slice) << 4
+  int gemm_tasks[kMaxChunks];    // GEMM tiles of each chunk (the ready target)
+  Ctrl* ctrl;
+  int64_t spin_limit;
+  int unreachable;               // debug: waits target an unreachable count
+};
+
+// Tile configurations (chosen from the op's shape only, never from the chunk
+// count, so every chunking runs the same per-element arithmetic).
+enum CfgId : int { CFG_LARGE = 0, CFG_SMALL = 1 };
+using CfgLarge = TileCfg<256, 256, 64, 2, 2>;
+using CfgSmall = TileCfg<32, 128, 64, 1, 4>;
+
+int cfg_bm(int cfg);
+int cfg_bn(int cfg);
+
+hipError_t launch_gemm_rows(int cfg, int bl, const GemmOperands& g, int row0, int row1, hipStream_t s);
+hipError_t launch_reduce_rows(const float* P, int64_t stride, int p, int row0, int row1, int N,
+                              const ReduceOut& o, int num_cus, hipStream_t s);
+hipError_t launch_fused(int cfg, int bl, const FusedArgs& a, int grid, hipStream_t s);
+hipError_t launch_copy(const char* src, char* dst, int64_t bytes, int num_cus, hipStream_t s);
+hipError_t launch_clear_status(Ctrl* c, hipStream_t s);
+
+}  // namespace tpf

@@ -1,0 +1,278 @@
+// Kernels of the fused tensor-parallel Linear and their launchers.
+//
+//  gemm_rows_kernel  one workgroup per (shard, row tile, column tile) of a row
+//                    range: the shard GEMMs of one chunk (two-stream
+//                    scheduler) or of all rows (unfused baseline).
+//  reduce_rows_kernel the fixed-order sum over shards of a row range, written
+//                    in AllReduce or ReduceScatter layout.
+//  fused_kernel      the persistent scheduler: every workgroup pulls tickets
+//                    from one queue whose order interleaves the GEMM tiles of
+//                    chunk c+1 with the reduction tasks of chunk c; a reduce
+//                    task waits on chunk c's ready counter, which each GEMM
+//                    tile of chunk c bumps after its partial is visible.  For
+//                    AllGather->MatMul the queue holds gather-copy tasks
+//                    instead, and a GEMM tile waits until the slices under its
+//                    rows have landed.
+//
+// Deadlock freedom of fused_kernel: a task only ever waits for tasks with
+// smaller tickets, and a ticket is handed out only to a workgroup that is
+// already running, so every awaited task is owned by a running workgroup
+// that does not itself wait on anything later.  This holds however many
+// workgroups are resident.
+#include "tpf_internal.hpp"
+
+namespace tpf {
+
+// Kernel arguments are read in place from the kernarg segment.  Indexing a
+// by-value struct argument with a run-time index (a shard's pointer, a
+// segment boundary) would otherwise make the compiler copy the whole struct
+// into per-lane scratch memory.  Each kernel below takes exactly one
+// argument, which therefore sits at offset 0 of the segment.
+template <class T>
+__device__ __forceinline__ const T& kernarg() {
+  return *(const T*)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
+int cfg_bm(int cfg) { return cfg == CFG_SMALL ? CfgSmall::BM : CfgLarge::BM; }
+int cfg_bn(int cfg) { return cfg == CFG_SMALL ? CfgSmall::BN : CfgLarge::BN; }
+
+template <class Cfg>
+__device__ __forceinline__ void store_any(const Frag<Cfg>& f, const TileJob& j, const GemmOperands& g, int shard) {
+  if (g.dst_dtype == OUT_F32) {
+    float* d = reinterpret_cast<float*>(g.dst) + (int64_t)shard * g.dst_shard_stride;
+    store_tile<Cfg, OUT_F32>(f, j, d, g.ldd);
+  } else {
+    uint16_t* d = reinterpret_cast<uint16_t*>(g.dst) + (int64_t)shard * g.dst_shard_stride;
+    store_tile<Cfg, OUT_BF16>(f, j, d, g.ldd);
+  }
+}
+
+template <class Cfg>
+__device__ __forceinline__ TileJob make_job(const GemmOperands& g, int shard, int row0, int row1, int tm, int tn) {
+  TileJob j;
+  j.A = g.A[shard];
+  j.B = g.B[shard];
+  j.lda = g.lda;
+  j.ldb = g.ldb;
+  j.m0 = row0 + tm * Cfg::BM;
+  j.rows = min(Cfg::BM, row1 - j.m0);
+  j.n0 = tn * Cfg::BN;
+  j.N = g.N;
+  j.K = g.K;
+  return j;
+}
+
+struct GemmRowsArgs {
+  GemmOperands g;
+  int row0, row1;
+};
+
+template <class Cfg, int BL>
+__global__ __launch_bounds__(256) void gemm_rows_kernel(GemmRowsArgs args) {
+  (void)args;
+  const GemmRowsArgs& ka = kernarg<GemmRowsArgs>();
+  const GemmOperands& g = ka.g;
+  const int row0 = ka.row0, row1 = ka.row1;
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  const int tiles_n = (g.N + Cfg::BN - 1) / Cfg::BN;
+  const int tiles_m = (row1 - row0 + Cfg::BM - 1) / Cfg::BM;
+  const int per_shard = tiles_m * tiles_n;
+  const int b = blockIdx.x;
+  const int shard = b / per_shard;
+  const int rem = b - shard * per_shard;
+  const int tm = rem / tiles_n, tn = rem - (rem / tiles_n) * tiles_n;
+  const TileJob j = make_job<Cfg>(g, shard, row0, row1, tm, tn);
+  Frag<Cfg> f;
+  gemm_tile<Cfg, BL>(f, j, lds);
+  store_any<Cfg>(f, j, g, shard);
+}
+
+template <int OUT>
+__device__ __forceinline__ void reduce_dispatch_p(const float* P, int64_t stride, int p, int64_t e0, int64_t e1,
+                                                  int N, const ReduceOut& o, int64_t t, int64_t nthr) {
+  switch (p) {
+    case 2: reduce_range<2, OUT>(P, stride, p, e0, e1, N, o, t, nthr); break;
+    case 4: reduce_range<4, OUT>(P, stride, p, e0, e1, N, o, t, nthr); break;
+    case 8: reduce_range<8, OUT>(P, stride, p, e0, e1, N, o, t, nthr); break;
+    default: reduce_range<0, OUT>(P, stride, p, e0, e1, N, o, t, nthr); break;
+  }
+}
+
+__device__ __forceinline__ void reduce_any(const float* P, int64_t stride, int p, int64_t e0, int64_t e1, int N,
+                                           const ReduceOut& o, int64_t t, int64_t nthr) {
+  if (o.dtype == OUT_F32)
+    reduce_dispatch_p<OUT_F32>(P, stride, p, e0, e1, N, o, t, nthr);
+  else
+    reduce_dispatch_p<OUT_BF16>(P, stride, p, e0, e1, N, o, t, nthr);
+}
+
+__global__ __launch_bounds__(256) void reduce_rows_kernel(const float* P, int64_t stride, int p, int64_t e0,
+                                                          int64_t e1, int N, ReduceOut o) {
+  reduce_any(P, stride, p, e0, e1, N, o, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256);
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const char* src, char* dst, int64_t bytes) {
+  copy_range(src, dst, 0, bytes, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256);
+}
+
+__global__ void clear_status_kernel(Ctrl* c) {
+  if (threadIdx.x == 0) atomic_store_relaxed(&c->status, 0);
+}
+
+// Thread 0 polls *ctr until it reaches target or the bound runs out.
+__device__ __forceinline__ void wait_at_least(const int* ctr, int target, const FusedArgs& a) {
+  if (a.unreachable) target = target + 1 + (1 << 30);
+  int64_t polls = 0;
+  while (atomic_load_acquire(ctr) < target) {
+    if (++polls > a.spin_limit) {
+      __hip_atomic_fetch_or(&a.ctrl->status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+template <class Cfg, int BL>
+__global__ __launch_bounds__(256) void fused_kernel(FusedArgs args) {
+  (void)args;
+  const FusedArgs& a = kernarg<FusedArgs>();
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  __shared__ int s_ticket;
+  const int tid = threadIdx.x;
+  Ctrl* ctl = a.ctrl;
+  const int total = a.seg_start[a.nseg];
+  const int tiles_n = (a.g.N + Cfg::BN - 1) / Cfg::BN;
+  int seg = 0;
+  for (;;) {
+    if (tid == 0) s_ticket = __hip_atomic_fetch_add(&ctl->ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int t = s_ticket;
+    __syncthreads();
+    if (t >= total) break;
+    while (a.seg_start[seg + 1] <= t) ++seg;   // this workgroup's tickets only increase
+    const int u = t - a.seg_start[seg];
+    const int kind = a.seg_info[seg] & 0xF;
+    const int idx = a.seg_info[seg] >> 4;
+
+    if (kind == TK_GEMM) {
+      const int c = idx;
+      const int row0 = a.ch.row0(c), row1 = a.ch.row1(c);
+      const int tiles_m = (row1 - row0 + Cfg::BM - 1) / Cfg::BM;
+      const int per_shard = tiles_m * tiles_n;
+      const int shard = u / per_shard;
+      const int rem = u - shard * per_shard;
+      const int tm = rem / tiles_n, tn = rem - (rem / tiles_n) * tiles_n;
+      const TileJob j = make_job<Cfg>(a.g, shard, row0, row1, tm, tn);
+      if (a.gather) {
+        // The rows of this tile must have landed in the gathered buffer.
+        if (tid == 0) {
+          const int s0 = j.m0 / a.slice_rows, s1 = (j.m0 + j.rows - 1) / a.slice_rows;
+          for (int s = s0; s <= s1; ++s) wait_at_least(&ctl->landed[s], a.copy_segs, a);
+        }
+        __syncthreads();
+        fence_acquire_agent();
+      }
+      Frag<Cfg> f;
+      gemm_tile<Cfg, BL>(f, j, lds);
+      store_any<Cfg>(f, j, a.g, shard);
+      if (!a.gather) {
+        fence_release_agent();
+        __syncthreads();
+        if (tid == 0) atomic_add_release(&ctl->ready[c], 1);
+      }
+    } else if (kind == TK_REDUCE) {
+      const int c = idx;
+      if (tid == 0) wait_at_least(&ctl->ready[c], a.gemm_tasks[c], a);
+      __syncthreads();
+      fence_acquire_agent();
+      const int r0 = a.ch.row0(c) + u * a.reduce_rows;
+      const int r1 = min(r0 + a.reduce_rows, a.ch.row1(c));
+      reduce_any(a.P, a.p_stride, a.p, (int64_t)r0 * a.g.N, (int64_t)r1 * a.g.N, a.g.N, a.ro, tid, 256);
+    } else {  // TK_COPY
+      const int r = idx;
+      const int64_t b0 = (int64_t)u * a.copy_seg_bytes;
+      const int64_t b1 = min(b0 + a.copy_seg_bytes, a.slice_bytes);
+      copy_range(a.src[r], a.gathered + (int64_t)r * a.slice_bytes, b0, b1, tid, 256);
+      fence_release_agent();
+      __syncthreads();
+      if (tid == 0) atomic_add_release(&ctl->landed[r], 1);
+    }
+  }
+  // The last workgroup out clears the counters for the next call.
+  if (tid == 0) {
+    const int d = atomic_add_acq_rel(&ctl->done, 1);
+    if (d == (int)gridDim.x - 1) {
+      for (int c = 0; c < a.ch.n; ++c) atomic_store_relaxed(&ctl->ready[c], 0);
+      for (int s = 0; s < kMaxShards; ++s) atomic_store_relaxed(&ctl->landed[s], 0);
+      atomic_store_relaxed(&ctl->ticket, 0);
+      atomic_store_relaxed(&ctl->done, 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+
+template <class Cfg>
+static hipError_t launch_gemm_cfg(int bl, const GemmOperands& g, int row0, int row1, hipStream_t s) {
+  const int tiles_n = (g.N + Cfg::BN - 1) / Cfg::BN;
+  const int tiles_m = (row1 - row0 + Cfg::BM - 1) / Cfg::BM;
+  const int grid = g.nshard * tiles_m * tiles_n;
+  if (grid <= 0) return hipSuccess;
+  GemmRowsArgs args{g, row0, row1};
+  if (bl == B_KN)
+    hipLaunchKernelGGL((gemm_rows_kernel<Cfg, B_KN>), dim3(grid), dim3(256), 0, s, args);
+  else
+    hipLaunchKernelGGL((gemm_rows_kernel<Cfg, B_NK>), dim3(grid), dim3(256), 0, s, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_rows(int cfg, int bl, const GemmOperands& g, int row0, int row1, hipStream_t s) {
+  if (cfg == CFG_SMALL) return launch_gemm_cfg<CfgSmall>(bl, g, row0, row1, s);
+  return launch_gemm_cfg<CfgLarge>(bl, g, row0, row1, s);
+}
+
+hipError_t launch_reduce_rows(const float* P, int64_t stride, int p, int row0, int row1, int N,
+                              const ReduceOut& o, int num_cus, hipStream_t s) {
+  const int64_t e0 = (int64_t)row0 * N, e1 = (int64_t)row1 * N;
+  const int64_t groups = (e1 - e0) / 4;
+  if (groups <= 0) return hipSuccess;
+  int64_t grid = (groups + 256 * 2 - 1) / (256 * 2);
+  const int64_t cap = (int64_t)num_cus * 8;
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, P, stride, p, e0, e1, N, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(const char* src, char* dst, int64_t bytes, int num_cus, hipStream_t s) {
+  const int64_t chunks = bytes / 16;
+  if (chunks <= 0) return hipSuccess;
+  int64_t grid = (chunks + 256 * 4 - 1) / (256 * 4);
+  const int64_t cap = (int64_t)num_cus * 8;
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(256), 0, s, src, dst, bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(int cfg, int bl, const FusedArgs& a, int grid, hipStream_t s) {
+  if (cfg == CFG_SMALL) {
+    if (bl == B_KN)
+      hipLaunchKernelGGL((fused_kernel<CfgSmall, B_KN>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((fused_kernel<CfgSmall, B_NK>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (bl == B_KN)
+      hipLaunchKernelGGL((fused_kernel<CfgLarge, B_KN>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((fused_kernel<CfgLarge, B_NK>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_status(Ctrl* c, hipStream_t s) {
+  hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(64), 0, s, c);
+  return hipGetLastError();
+}
+
+}  // namespace tpf

@@ -1,0 +1,245 @@
+"""Python binding of libtpfuse (ctypes).
+
+Argument marshalling only: every step of the fused path runs in the HIP
+kernels of ``libtpfuse.so``.  PyTorch supplies device memory (tensors) and
+the stream (``torch.cuda.current_stream()``).  If the library is not built
+the import of a call fails loudly; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libtpfuse.so")
+
+# Status codes, dtypes, schedulers, semantics and op ids (include/tpfuse.h).
+OK = 0
+ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGNMENT, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP, ERR_TIMEOUT = range(-1, -8, -1)
+BF16, F32 = 0, 1
+SCHED_AUTO, SCHED_PERSISTENT, SCHED_TWO_STREAM, SCHED_UNFUSED, SCHED_GEMM_ONLY, SCHED_REDUCE_ONLY = range(6)
+ALLREDUCE, REDUCESCATTER = 0, 1
+OP_MATMUL_ALLREDUCE, OP_MATMUL_REDUCESCATTER, OP_ALLGATHER_MATMUL, OP_MATMUL_DX = range(4)
+MAX_SHARDS = 16
+MAX_CHUNKS = 64
+
+SCHEDS = {"auto": SCHED_AUTO, "persistent": SCHED_PERSISTENT, "two_stream": SCHED_TWO_STREAM,
+          "unfused": SCHED_UNFUSED, "gemm_only": SCHED_GEMM_ONLY, "reduce_only": SCHED_REDUCE_ONLY}
+
+_VP = ctypes.c_void_p
+_PP = ctypes.POINTER(ctypes.c_void_p)
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+# name -> (restype, argtypes); the set of exported functions of include/tpfuse.h
+SIGNATURES = {
+    "tpf_create": (_I, [ctypes.POINTER(_VP), _I]),
+    "tpf_destroy": (_I, [_VP]),
+    "tpf_workspace_size": (_SZ, [_I, _I, _I64, _I64, _I64, _I, _I]),
+    "tpf_matmul_allreduce": (_I, [_VP, _I, _I64, _I64, _I64, _PP, _PP, _VP, _I, _I, _I, _VP, _SZ, _VP]),
+    "tpf_matmul_reducescatter": (_I, [_VP, _I, _I64, _I64, _I64, _PP, _PP, _PP, _I, _I, _I, _VP, _SZ, _VP]),
+    "tpf_allgather_matmul": (_I, [_VP, _I, _I64, _I64, _I64, _PP, _VP, _VP, _VP, _I, _I, _I, _VP, _SZ, _VP]),
+    "tpf_matmul_dx": (_I, [_VP, _I, _I, _I64, _I64, _I64, _PP, _PP, _PP, _I, _I, _I, _VP, _SZ, _VP]),
+    "tpf_sync_status": (_I, [_VP, _VP]),
+    "tpf_debug_set_wait": (_I, [_VP, _I64, _I]),
+    "tpf_status_string": (ctypes.c_char_p, [_I]),
+    "tpf_last_error": (ctypes.c_char_p, []),
+    "tpf_version": (_I, []),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class TpfError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libtpfuse error {code}: {msg}")
+        self.code = code
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree libtpfuse.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m tensor_gemm_reduction_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def check(code: int) -> None:
+    if code != OK:
+        msg = load().tpf_last_error().decode(errors="replace")
+        raise TpfError(code, msg)
+
+
+def ptr_array(ptrs: Sequence[int]):
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p
+    return arr
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return BF16
+    if dt == torch.float32:
+        return F32
+    raise ValueError(f"output dtype must be bfloat16 or float32, got {dt}")
+
+
+def _sched(s) -> int:
+    return SCHEDS[s] if isinstance(s, str) else int(s)
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+class Handle:
+    """A libtpfuse handle bound to one device (owns a side stream, events, counters)."""
+
+    def __init__(self, device: int = 0):
+        lib = load()
+        h = ctypes.c_void_p()
+        check(lib.tpf_create(ctypes.byref(h), int(device)))
+        self._h = h
+        self.device = device
+
+    @property
+    def ptr(self):
+        return self._h
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            load().tpf_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def sync_status(self, stream=None) -> int:
+        return load().tpf_sync_status(self._h, _stream_ptr(stream))
+
+    def debug_set_wait(self, spins: int, unreachable: bool) -> None:
+        check(load().tpf_debug_set_wait(self._h, int(spins), 1 if unreachable else 0))
+
+
+_default_handles = {}
+
+
+def default_handle(device: Optional[int] = None) -> Handle:
+    dev = torch.cuda.current_device() if device is None else device
+    h = _default_handles.get(dev)
+    if h is None:
+        h = Handle(dev)
+        _default_handles[dev] = h
+    return h
+
+
+def workspace_size(op: int, p: int, M: int, N: int, K: int, n_chunks: int = 1, sched=SCHED_AUTO) -> int:
+    return int(load().tpf_workspace_size(op, p, M, N, K, n_chunks, _sched(sched)))
+
+
+def _ws(op, p, M, N, K, n_chunks, sched, ws, device):
+    need = workspace_size(op, p, M, N, K, n_chunks, sched)
+    if need == 0:
+        return ws, 0 if ws is None else ws.numel() * ws.element_size()
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def matmul_allreduce(X: List[torch.Tensor], W: List[torch.Tensor], out_dtype=torch.bfloat16, n_chunks: int = 1,
+                     sched="auto", Y: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                     handle: Optional[Handle] = None, stream=None) -> torch.Tensor:
+    """Y = sum_k X[k] @ W[k] (row-parallel Linear, AllReduce layout)."""
+    p = len(X)
+    M, K = X[0].shape
+    N = W[0].shape[1]
+    dev = X[0].device
+    if Y is None:
+        Y = torch.empty((M, N), dtype=out_dtype, device=dev)
+    ws, ws_bytes = _ws(OP_MATMUL_ALLREDUCE, p, M, N, K, n_chunks, sched, ws, dev)
+    h = handle or default_handle(dev.index)
+    check(load().tpf_matmul_allreduce(h.ptr, p, M, N, K, ptr_array([x.data_ptr() for x in X]),
+                                      ptr_array([w.data_ptr() for w in W]), Y.data_ptr(), _dtype_code(Y.dtype),
+                                      n_chunks, _sched(sched), ws.data_ptr() if ws is not None else None, ws_bytes,
+                                      _stream_ptr(stream)))
+    return Y
+
+
+def matmul_reducescatter(X: List[torch.Tensor], W: List[torch.Tensor], out_dtype=torch.bfloat16, n_chunks: int = 1,
+                         sched="auto", Y: Optional[List[torch.Tensor]] = None, ws: Optional[torch.Tensor] = None,
+                         handle: Optional[Handle] = None, stream=None) -> List[torch.Tensor]:
+    """Slice r = rows [r*M/p, (r+1)*M/p) of sum_k X[k] @ W[k] (ReduceScatter layout)."""
+    p = len(X)
+    M, K = X[0].shape
+    N = W[0].shape[1]
+    dev = X[0].device
+    if Y is None:
+        Y = [torch.empty((M // p, N), dtype=out_dtype, device=dev) for _ in range(p)]
+    ws, ws_bytes = _ws(OP_MATMUL_REDUCESCATTER, p, M, N, K, n_chunks, sched, ws, dev)
+    h = handle or default_handle(dev.index)
+    check(load().tpf_matmul_reducescatter(h.ptr, p, M, N, K, ptr_array([x.data_ptr() for x in X]),
+                                          ptr_array([w.data_ptr() for w in W]), ptr_array([y.data_ptr() for y in Y]),
+                                          _dtype_code(Y[0].dtype), n_chunks, _sched(sched),
+                                          ws.data_ptr() if ws is not None else None, ws_bytes, _stream_ptr(stream)))
+    return Y
+
+
+def allgather_matmul(X_slices: List[torch.Tensor], W: torch.Tensor, out_dtype=torch.bfloat16, n_chunks: int = 1,
+                     sched="auto", X_gathered: Optional[torch.Tensor] = None, Y: Optional[torch.Tensor] = None,
+                     handle: Optional[Handle] = None, stream=None):
+    """(X_gathered, Y): slices concatenated in rank order, then Y = X_gathered @ W."""
+    p = len(X_slices)
+    Ms, K = X_slices[0].shape
+    M = Ms * p
+    N = W.shape[1]
+    dev = W.device
+    if X_gathered is None:
+        X_gathered = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=out_dtype, device=dev)
+    h = handle or default_handle(dev.index)
+    check(load().tpf_allgather_matmul(h.ptr, p, M, N, K, ptr_array([x.data_ptr() for x in X_slices]), W.data_ptr(),
+                                      X_gathered.data_ptr(), Y.data_ptr(), _dtype_code(Y.dtype), n_chunks,
+                                      _sched(sched), None, 0, _stream_ptr(stream)))
+    return X_gathered, Y
+
+
+def matmul_dx(dY: List[torch.Tensor], W: List[torch.Tensor], semantic: int = ALLREDUCE, out_dtype=torch.bfloat16,
+              n_chunks: int = 1, sched="auto", dX=None, ws: Optional[torch.Tensor] = None,
+              handle: Optional[Handle] = None, stream=None):
+    """dX = sum_k dY[k] @ W[k]^T; one tensor (ALLREDUCE) or p row slices (REDUCESCATTER)."""
+    p = len(dY)
+    M, Ns = dY[0].shape
+    Kin = W[0].shape[0]
+    dev = dY[0].device
+    if dX is None:
+        if semantic == ALLREDUCE:
+            dX = torch.empty((M, Kin), dtype=out_dtype, device=dev)
+        else:
+            dX = [torch.empty((M // p, Kin), dtype=out_dtype, device=dev) for _ in range(p)]
+    outs = [dX] if semantic == ALLREDUCE else list(dX)
+    ws, ws_bytes = _ws(OP_MATMUL_DX, p, M, Kin, Ns, n_chunks, sched, ws, dev)
+    h = handle or default_handle(dev.index)
+    check(load().tpf_matmul_dx(h.ptr, semantic, p, M, Kin, Ns, ptr_array([d.data_ptr() for d in dY]),
+                               ptr_array([w.data_ptr() for w in W]), ptr_array([o.data_ptr() for o in outs]),
+                               _dtype_code(outs[0].dtype), n_chunks, _sched(sched),
+                               ws.data_ptr() if ws is not None else None, ws_bytes, _stream_ptr(stream)))
+    return dX

@@ -1,0 +1,248 @@
+"""GPU parity of the HIP path against the CPU oracle, at sizes the oracle
+finishes in seconds that still span several tiles and ragged edges (rows,
+columns and K not multiples of the tile), plus the invariants the design
+promises: identical bits for every chunk count and every scheduler,
+ReduceScatter slices equal to AllReduce rows, bf16 output equal to the RNE
+rounding of the fp32 output, and exact results for integer inputs.
+
+All calls go through the C ABI (tensor_gemm_reduction_amd.tpfuse)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import tpf_oracle as O
+from tensor_gemm_reduction_amd import inputs, tpfuse as tp
+from tests.parity import (assert_bf16, assert_bf16_is_rne_of_f32, assert_bitwise, assert_f32)
+
+pytestmark = pytest.mark.gpu
+
+SCHEDS = ["persistent", "two_stream", "unfused"]
+DEV = "cuda"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def shards(shapes, dist, seed, mode="random"):
+    return [inputs.draw(s, dist, seed * 1000 + i, mode) for i, s in enumerate(shapes)]
+
+
+def bits(ts):
+    return [inputs.bf16_to_bits(t) for t in ts]
+
+
+def gpu(ts):
+    return [t.to(DEV) for t in ts]
+
+
+# ---------------------------------------------------------------------------
+# MatMul -> AllReduce
+# ---------------------------------------------------------------------------
+
+AR_CASES = [
+    # p, M, N, K  (ragged against the 256x256 tile in every dimension)
+    (3, 300, 328, 200),
+    (2, 128, 2048, 1024),       # the worked example's shapes
+    (1, 520, 264, 72),
+    (4, 64, 392, 136),          # small-M tile configuration
+    (8, 16, 1024, 256),
+]
+
+
+@pytest.mark.parametrize("p,M,N,K", AR_CASES)
+def test_allreduce_parity(p, M, N, K):
+    say(f"allreduce p={p} M={M} N={N} K={K}")
+    Xh = shards([(M, K)] * p, ("normal", 1.0), 11)
+    Wh = shards([(K, N)] * p, ("normal", 0.05), 12)
+    ref = O.matmul_allreduce(bits(Xh), bits(Wh))
+    X, W = gpu(Xh), gpu(Wh)
+    outs = {}
+    for sched in SCHEDS:
+        for n in sorted({1, 3, min(M, 7), min(M, 64)}):
+            y32 = tp.matmul_allreduce(X, W, torch.float32, n_chunks=n, sched=sched)
+            y16 = tp.matmul_allreduce(X, W, torch.bfloat16, n_chunks=n, sched=sched)
+            torch.cuda.synchronize()
+            what = f"AR p={p} M={M} N={N} K={K} {sched} n={n}"
+            assert_f32(y32, ref, what)
+            assert_bf16(y16, ref, what)
+            assert_bf16_is_rne_of_f32(y16, y32, what)
+            outs[(sched, n)] = (y32, y16)
+    base32, base16 = outs[("unfused", 1)]
+    for key, (y32, y16) in outs.items():
+        assert_bitwise(y32, base32, f"fp32 {key} vs unfused n=1")
+        assert_bitwise(y16, base16, f"bf16 {key} vs unfused n=1")
+
+
+def test_allreduce_integer_exact():
+    p, M, N, K = 4, 272, 264, 520
+    say(f"allreduce integer-exact p={p} M={M} N={N} K={K}")
+    Xh = shards([(M, K)] * p, None, 21, mode="int")
+    Wh = shards([(K, N)] * p, None, 22, mode="int")
+    ref = O.matmul_allreduce(bits(Xh), bits(Wh))
+    assert np.all(ref == np.round(ref))
+    for sched in SCHEDS:
+        y = tp.matmul_allreduce(gpu(Xh), gpu(Wh), torch.float32, n_chunks=5, sched=sched)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().double().numpy(), ref), sched
+
+
+def test_worked_example_full():
+    """The worked example exactly as configured: p=2, four 32-row chunks, fp32 and bf16."""
+    wl = inputs.WORKLOADS["worked"]
+    say("worked example p=2 [128,1024]x[1024,2048] n=4")
+    inp = inputs.make_inputs(wl, seed=0)
+    ref = O.matmul_allreduce(bits(inp.X), bits(inp.W))
+    X, W = gpu(inp.X), gpu(inp.W)
+    y32 = tp.matmul_allreduce(X, W, torch.float32, n_chunks=4, sched="persistent")
+    y16 = tp.matmul_allreduce(X, W, torch.bfloat16, n_chunks=4, sched="persistent")
+    torch.cuda.synchronize()
+    assert_f32(y32, ref, "worked fp32")
+    assert_bf16(y16, ref, "worked bf16")
+    assert_bf16_is_rne_of_f32(y16, y32, "worked")
+    # the chunked message of the pages: 32 rows x 2048 columns x 2 bytes = 128 KiB
+    assert O.message_bytes(32, 2048, y16.element_size()) == 128 * 1024
+
+
+def test_gemm_only_then_reduce_only_equals_unfused():
+    p, M, N, K = 3, 300, 328, 200
+    say(f"phases p={p} M={M} N={N} K={K}")
+    X = gpu(shards([(M, K)] * p, ("normal", 1.0), 31))
+    W = gpu(shards([(K, N)] * p, ("normal", 0.05), 32))
+    ws = torch.empty(tp.workspace_size(tp.OP_MATMUL_ALLREDUCE, p, M, N, K), dtype=torch.uint8, device=DEV)
+    Y1 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    tp.matmul_allreduce(X, W, sched="gemm_only", Y=Y1, ws=ws)
+    tp.matmul_allreduce(X, W, sched="reduce_only", Y=Y1, ws=ws)
+    Y2 = tp.matmul_allreduce(X, W, torch.bfloat16, sched="unfused")
+    torch.cuda.synchronize()
+    assert_bitwise(Y1, Y2, "gemm_only + reduce_only vs unfused")
+    # the workspace holds each shard's fp32 local output X_k W_k
+    P = ws.view(torch.float32).view(p, M, N)
+    Xh = [x.cpu() for x in X]
+    Wh = [w.cpu() for w in W]
+    parts = O.shard_products(bits(Xh), bits(Wh))
+    for k in range(p):
+        assert_f32(P[k], parts[k], f"partial {k}")
+
+
+def test_repeated_persistent_calls_are_deterministic():
+    p, M, N, K = 2, 520, 264, 136
+    say(f"repeat p={p} M={M} N={N} K={K}")
+    X = gpu(shards([(M, K)] * p, ("normal", 1.0), 41))
+    W = gpu(shards([(K, N)] * p, ("normal", 0.05), 42))
+    first = tp.matmul_allreduce(X, W, torch.float32, n_chunks=4, sched="persistent")
+    for _ in range(5):
+        again = tp.matmul_allreduce(X, W, torch.float32, n_chunks=4, sched="persistent")
+        torch.cuda.synchronize()
+        assert_bitwise(again, first, "repeat")
+    assert tp.default_handle().sync_status() == tp.OK
+
+
+# ---------------------------------------------------------------------------
+# MatMul -> ReduceScatter
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("p,M,N,K", [(4, 512, 264, 136), (8, 1024, 328, 72), (2, 64, 136, 264)])
+def test_reducescatter_parity(p, M, N, K):
+    say(f"reducescatter p={p} M={M} N={N} K={K}")
+    Xh = shards([(M, K)] * p, ("normal", 1.0), 51)
+    Wh = shards([(K, N)] * p, ("normal", 0.05), 52)
+    ref_slices = O.matmul_reducescatter(bits(Xh), bits(Wh))
+    X, W = gpu(Xh), gpu(Wh)
+    ar = tp.matmul_allreduce(X, W, torch.bfloat16, n_chunks=1, sched="unfused")
+    for sched in SCHEDS:
+        for n in (1, p, min(M, 2 * p + 1)):
+            s32 = tp.matmul_reducescatter(X, W, torch.float32, n_chunks=n, sched=sched)
+            s16 = tp.matmul_reducescatter(X, W, torch.bfloat16, n_chunks=n, sched=sched)
+            torch.cuda.synchronize()
+            for r in range(p):
+                what = f"RS p={p} {sched} n={n} slice {r}"
+                assert_f32(s32[r], ref_slices[r], what)
+                assert_bf16(s16[r], ref_slices[r], what)
+                assert_bf16_is_rne_of_f32(s16[r], s32[r], what)
+                assert_bitwise(s16[r], ar[r * (M // p):(r + 1) * (M // p)], what + " vs AllReduce rows")
+
+
+# ---------------------------------------------------------------------------
+# AllGather -> MatMul
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("p,Ms,N,K", [(4, 96, 264, 200), (8, 32, 520, 136), (2, 256, 264, 72)])
+def test_allgather_parity(p, Ms, N, K):
+    M = p * Ms
+    say(f"allgather p={p} slices [{Ms},{K}] W [{K},{N}]")
+    Sh = shards([(Ms, K)] * p, ("normal", 1.0), 61)
+    Wh = shards([(K, N)], ("normal", 0.05), 62)[0]
+    xg_ref, y_ref = O.allgather_matmul(bits(Sh), inputs.bf16_to_bits(Wh))
+    S, W = gpu(Sh), Wh.to(DEV)
+    outs = {}
+    for sched in SCHEDS:
+        for n in sorted({1, p, min(M, 3), min(M, 2 * p + 3)}):
+            xg, y32 = tp.allgather_matmul(S, W, torch.float32, n_chunks=n, sched=sched)
+            _, y16 = tp.allgather_matmul(S, W, torch.bfloat16, n_chunks=n, sched=sched)
+            torch.cuda.synchronize()
+            what = f"AG p={p} {sched} n={n}"
+            assert np.array_equal(xg.cpu().double().numpy(), xg_ref), what + " gathered input"
+            assert_f32(y32, y_ref, what)
+            assert_bf16(y16, y_ref, what)
+            assert_bf16_is_rne_of_f32(y16, y32, what)
+            outs[(sched, n)] = y32
+    base = outs[("unfused", 1)]
+    for key, y in outs.items():
+        assert_bitwise(y, base, f"AG {key}")
+
+
+# ---------------------------------------------------------------------------
+# Column-parallel backward dX
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("p,M,Kin,Ns", [(3, 160, 200, 136), (8, 256, 264, 72), (2, 64, 520, 264)])
+def test_dx_parity(p, M, Kin, Ns):
+    say(f"dx p={p} M={M} K_in={Kin} N_shard={Ns}")
+    dYh = shards([(M, Ns)] * p, ("normal", 1.0), 71)
+    Wh = shards([(Kin, Ns)] * p, ("normal", 0.05), 72)
+    ref = O.matmul_dx(bits(dYh), bits(Wh))
+    dY, W = gpu(dYh), gpu(Wh)
+    base = None
+    for sched in SCHEDS:
+        for n in (1, 4):
+            d32 = tp.matmul_dx(dY, W, tp.ALLREDUCE, torch.float32, n_chunks=n, sched=sched)
+            d16 = tp.matmul_dx(dY, W, tp.ALLREDUCE, torch.bfloat16, n_chunks=n, sched=sched)
+            torch.cuda.synchronize()
+            what = f"dX p={p} {sched} n={n}"
+            assert_f32(d32, ref, what)
+            assert_bf16(d16, ref, what)
+            assert_bf16_is_rne_of_f32(d16, d32, what)
+            if base is None:
+                base = d32
+            assert_bitwise(d32, base, what)
+            if M % p == 0:
+                sl = tp.matmul_dx(dY, W, tp.REDUCESCATTER, torch.bfloat16, n_chunks=n, sched=sched)
+                torch.cuda.synchronize()
+                for r in range(p):
+                    assert_bitwise(sl[r], d16[r * (M // p):(r + 1) * (M // p)], what + f" RS slice {r}")
+
+
+# ---------------------------------------------------------------------------
+# Failure handling: the persistent kernel's bounded waits
+# ---------------------------------------------------------------------------
+
+def test_bounded_wait_reports_timeout_and_recovers():
+    """Force every wait to target an unreachable count with a tiny bound: each
+    wait gives up after a few polls, the kernel still finishes, and the
+    handle reports TPF_ERR_TIMEOUT once; normal calls work afterwards."""
+    p, M, N, K = 2, 64, 264, 72
+    say("bounded-wait timeout path")
+    h = tp.Handle(0)
+    X = gpu(shards([(M, K)] * p, ("normal", 1.0), 81))
+    W = gpu(shards([(K, N)] * p, ("normal", 0.05), 82))
+    h.debug_set_wait(spins=16, unreachable=True)
+    tp.matmul_allreduce(X, W, torch.float32, n_chunks=2, sched="persistent", handle=h)
+    assert h.sync_status() == tp.ERR_TIMEOUT
+    assert h.sync_status() == tp.OK          # the flag is cleared by the query
+    h.debug_set_wait(spins=0, unreachable=False)
+    y = tp.matmul_allreduce(X, W, torch.float32, n_chunks=2, sched="persistent", handle=h)
+    ref = tp.matmul_allreduce(X, W, torch.float32, n_chunks=1, sched="unfused", handle=h)
+    assert h.sync_status() == tp.OK
+    assert_bitwise(y, ref, "after timeout")
+    h.close()
