@@ -147,7 +147,7 @@ def main():
 
     # --- the other modes (measurement context) ---
     modes = {}
-    for m in [x for x in args.modes.split(",") if x]:
+    for m in [x for x in args.modes.split(",") if x and x != "none"]:
         modes[m] = time_mode(m, max(5, args.steps // 2), 2)
     extra = {}
     if "gemm_only" in modes and args.sched in modes:

@@ -72,6 +72,10 @@ int check_common(int p, int64_t M, int64_t N, int64_t K, int n_chunks, int dtype
   if (M * N > ((int64_t)1 << 40) || M * K > ((int64_t)1 << 40) || N * K > ((int64_t)1 << 40))
     return fail(TPF_ERR_SHAPE, "operand too large");
   if (need_div && M % p != 0) return fail(TPF_ERR_SHAPE, "M must be divisible by p for this layout");
+  // Operands are addressed with 32-bit buffer offsets.
+  const int64_t lim = ((int64_t)1 << 31) - 1;
+  if (M * K * 2 > lim || N * K * 2 > lim || M * N * 4 > lim)
+    return fail(TPF_ERR_UNSUPPORTED, "each operand and each shard's fp32 partial must be smaller than 2 GiB");
   if (n_chunks < 1 || n_chunks > kMaxChunks || n_chunks > M)
     return fail(TPF_ERR_SHAPE, "n_chunks must be in [1, min(M, " + std::to_string(kMaxChunks) + ")]");
   if (N % 8 != 0 || K % 8 != 0) return fail(TPF_ERR_ALIGNMENT, "N and K must be multiples of 8");
@@ -148,6 +152,7 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
   g.M = rc.M;
   g.N = rc.N;
   g.K = rc.K;
+  g.b_rows = rc.bl == B_KN ? rc.K : rc.N;
   g.nshard = rc.p;
   ChunkGeom ch{rc.n_chunks, rc.M / rc.n_chunks, rc.M};
   const int64_t stride = (int64_t)rc.M * rc.N;
@@ -183,8 +188,9 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
       a.P = rc.P;
       a.p_stride = stride;
       a.p = rc.p;
-      // Reduce tasks of about 64 Ki elements per shard (256 KiB of fp32 partials each).
-      a.reduce_rows = std::max(1, (int)(65536 / rc.N));
+      // Reduce tasks of 8 Ki output elements (32 KiB of fp32 partials per shard):
+      // many small tasks spread a chunk's reduction over many CUs.
+      a.reduce_elems = 8192;
       a.gather = 0;
       a.ch = ch;
       a.ctrl = h->ctrl;
@@ -201,7 +207,10 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
         ++nseg;
       };
       auto gemm_count = [&](int c) { return rc.p * ((ch.row1(c) - ch.row0(c) + bm - 1) / bm) * tiles_n; };
-      auto red_count = [&](int c) { return (ch.row1(c) - ch.row0(c) + a.reduce_rows - 1) / a.reduce_rows; };
+      auto red_count = [&](int c) {
+        const int64_t e = (int64_t)(ch.row1(c) - ch.row0(c)) * rc.N;
+        return (int)((e + a.reduce_elems - 1) / a.reduce_elems);
+      };
       for (int c = 0; c < ch.n; ++c) a.gemm_tasks[c] = gemm_count(c);
       add_seg(TK_GEMM, 0, gemm_count(0));
       for (int c = 1; c < ch.n; ++c) {
@@ -211,7 +220,7 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
       add_seg(TK_REDUCE, ch.n - 1, red_count(ch.n - 1));
       a.nseg = nseg;
       a.seg_start[nseg] = t;
-      const int grid = std::min(t, h->num_cus);
+      const int grid = std::min(t, h->num_cus * fused_occupancy(cfg, rc.bl));
       TPF_HIP(launch_fused(cfg, rc.bl, a, grid, stream));
       return TPF_OK;
     }
@@ -427,6 +436,7 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
   g.M = Mi;
   g.N = Ni;
   g.K = Ki;
+  g.b_rows = Ki;
   g.nshard = 1;
   const int slice_rows = Mi / p;
   const int64_t slice_bytes = (int64_t)slice_rows * Ki * 2;
@@ -514,7 +524,7 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
       copy_upto(p - 1);
       a.nseg = nseg;
       a.seg_start[nseg] = t;
-      const int grid = std::min(t, h->num_cus);
+      const int grid = std::min(t, h->num_cus * fused_occupancy(cfg, B_KN));
       TPF_HIP(launch_fused(cfg, B_KN, a, grid, stream_));
       return TPF_OK;
     }

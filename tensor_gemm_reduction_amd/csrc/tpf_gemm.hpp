@@ -1,0 +1,565 @@
+// bf16 matrix-core GEMM tile for gfx950.
+//
+// A workgroup of NW wave64s (arranged WAVES_M x WAVES_N) computes a BM x BN
+// block of C = A B in fp32, with A row-major [M][K] and B either row-major
+// [K][N] ("KN": a forward weight W_k) or row-major [N][K] ("NK": a weight
+// used transposed, as in dX = dY W^T).
+//
+// Data path:
+//  * global -> LDS without registers: buffer_load_dwordx4 ... lds.  One such
+//    instruction moves 64 lanes x 16 bytes into 1 KiB of contiguous LDS, lane
+//    l landing at byte 16*l.  Loads are addressed through buffer resources
+//    whose size is the whole operand, so rows past the end of an operand and
+//    K (or N) tails read as zeros.
+//  * K advances in steps of BK (32 or 64) through STAGES LDS buffers: the loads of step
+//    kt+STAGES-1 are issued right after the barrier of step kt, so they
+//    overlap STAGES-1 steps of MFMAs.  One barrier per step.
+//  * A tiles are stored [m][BK k]; each lane of
+//    v_mfma_f32_32x32x16_bf16 reads its eight consecutive k with one
+//    ds_read_b128.  16-byte chunks are XOR-swizzled by row so that the 16
+//    lanes of one LDS pass (same k, consecutive rows) hit all 64 banks once.
+//  * KN B tiles stay row-major [BK k][BN n] as they come from memory.  The
+//    gfx950 transpose read ds_read_b64_tr_b16 hands lane i of each 16-lane
+//    group element i of the four 16-element rows supplied by lanes 4r..4r+3,
+//    so lanes 4r+q pointing at B[k0+r][n0+4q] deliver to lane i the four
+//    values B[k0..k0+3][n0+i]: two such reads give the eight consecutive k of
+//    one column that the MFMA B operand needs.  32-byte blocks are
+//    XOR-swizzled by k so that the four rows of a read land in distinct banks.
+//  * NK B tiles are stored like A.
+//
+// Every output element is accumulated by the same sequence of MFMAs in
+// increasing k whatever the tile shape, origin or number of valid rows, so the
+// result does not depend on how the rows are chunked or which tile
+// configuration computed it.
+#pragma once
+
+#include "tpf_device.hpp"
+
+namespace tpf {
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset that is always out of range (operands < 2 GiB)
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int BK_ = 64, int L2PF_ = 1, int PP_ = 0,
+          int PPMODE_ = 0, int SWB_ = 2>
+struct TileCfg {
+  // PP: ping-pong schedule (two wave groups one barrier phase apart; only
+  // group 0 issues global loads).  PPMODE selects how waves form the groups:
+  // 0: group = wave / (NW/2), 1: group = wave % 2.
+  static constexpr int PP = PP_;
+  static constexpr int PPMODE = PPMODE_;
+  // L2PF > 0: every K step also touches each 128-byte line of step
+  // (issued step + L2PF), so that step's LDS loads later hit in L2.
+  static constexpr int L2PF = L2PF_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
+  static constexpr int KCH = BK / 8;              // 16-byte chunks per A row
+  static constexpr int RB = BK * 2;               // bytes per A row
+  static constexpr int ROWS_PER_PERIOD = 256 / RB;  // A rows per 256-byte span of the 64 LDS banks
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int NW = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int STAGES = STAGES_;
+  static constexpr int SWB = SWB_;    // KN-B 32-byte block swizzle: block ^ (SWB * (k & 3))
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static_assert(TM >= 1 && TN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile of 32x32 MFMA blocks");
+  static constexpr int LDS_A = BM * BK * 2;
+  static constexpr int LDS_B = BN * BK * 2;
+  static constexpr int LDS_STAGE = LDS_A + LDS_B;
+  static constexpr int LDS_BYTES = STAGES * LDS_STAGE;
+  static constexpr int A_INSTR = LDS_A / 1024;   // 1 KiB load instructions per A tile
+  static constexpr int B_INSTR = LDS_B / 1024;
+  static constexpr int NLW = PP ? NW / 2 : NW;      // waves that issue global loads
+  static_assert(A_INSTR % NLW == 0 && B_INSTR % NLW == 0, "loads must split evenly over waves");
+  static constexpr int A_PER_WAVE = A_INSTR / NLW;
+  static constexpr int B_PER_WAVE = B_INSTR / NLW;
+  static constexpr int TOUCH_LINES = (BM * BK * 2 + BN * BK * 2) / 128;
+  static constexpr int TOUCH_PER_WAVE = L2PF > 0 ? (TOUCH_LINES + THREADS - 1) / THREADS : 0;
+  static constexpr int LOADS_PER_WAVE = A_PER_WAVE + B_PER_WAVE + TOUCH_PER_WAVE;
+  static_assert(BN >= 128 && 1024 % (BN * 2 > 1024 ? 1024 : BN * 2) == 0 && (BN * 2) % 256 == 0,
+                "KN rows hold >= 8 swizzled 32-byte blocks and tile 1 KiB");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert((STAGES - 2) * LOADS_PER_WAVE + TOUCH_PER_WAVE <= 63, "vmcnt range");
+  static_assert(L2PF == 0 || (BK == 64 && BM % 64 == 0 && !PP), "line touches: 128-byte A rows, A/B split on a wave");
+};
+
+// Operand description of one tile job.
+struct TileJob {
+  const __bf16* A;   // operand base (row 0)
+  const __bf16* B;
+  int64_t lda, ldb;  // elements
+  int a_rows;        // rows of the A operand (its size bound)
+  int b_rows;        // rows of the B operand (K for KN, N for NK)
+  int m0;            // first row of the tile (absolute)
+  int rows;          // valid rows from m0 (<= BM)
+  int n0;            // first column
+  int N, K;          // output width and reduction length
+};
+
+template <class Cfg>
+struct Frag {
+  f32x16_t acc[Cfg::TM][Cfg::TN];
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// A (and NK-B) rows: 16 consecutive rows read the same logical chunk in one
+// pass of 16 lanes x 16 bytes = 256 bytes = all 64 banks.  Rows in the same
+// 256-byte span already use different banks; rows ROWS_PER_PERIOD apart would
+// collide, so the chunk is XORed with (row / ROWS_PER_PERIOD) mod KCH.
+template <class Cfg>
+__device__ __forceinline__ int swz_row(int row) { return (row / Cfg::ROWS_PER_PERIOD) & (Cfg::KCH - 1); }
+
+// s_waitcnt vmcnt(n) for a small compile-time bound on outstanding loads.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4] in [15:14]
+#define TPF_VM(N) __builtin_amdgcn_s_waitcnt((((N) & 15) | 0x70 | 0xF00 | (((N) >> 4) << 14)))
+  switch (n) {
+    case 0: TPF_VM(0); break;
+    case 1: TPF_VM(1); break;
+    case 2: TPF_VM(2); break;
+    case 3: TPF_VM(3); break;
+    case 4: TPF_VM(4); break;
+    case 5: TPF_VM(5); break;
+    case 6: TPF_VM(6); break;
+    case 7: TPF_VM(7); break;
+    case 8: TPF_VM(8); break;
+    case 10: TPF_VM(10); break;
+    case 12: TPF_VM(12); break;
+    case 14: TPF_VM(14); break;
+    case 16: TPF_VM(16); break;
+    case 20: TPF_VM(20); break;
+    case 24: TPF_VM(24); break;
+    case 28: TPF_VM(28); break;
+    case 32: TPF_VM(32); break;
+    case 40: TPF_VM(40); break;
+    case 48: TPF_VM(48); break;
+    default: TPF_VM(0); break;
+  }
+#undef TPF_VM
+}
+
+template <class Cfg, int BL>
+struct TileLoader {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t a_off[Cfg::A_PER_WAVE];   // byte offsets at k0 = 0 (kOOB when out of range)
+  uint32_t b_off[Cfg::B_PER_WAVE];
+  int a_kc[Cfg::A_PER_WAVE];         // logical k chunk of this lane's A (and NK B) loads
+  int b_kc[Cfg::B_PER_WAVE];         // NK: logical k chunk; KN: k row within the step
+  int K;
+  uint32_t ldb_bytes;
+  uint32_t lda_bytes;
+  // L2 touch: this lane's line (A row, or B row segment) at k0 = 0.
+  uint32_t t_off[Cfg::TOUCH_PER_WAVE > 0 ? Cfg::TOUCH_PER_WAVE : 1];
+  int t_isb[Cfg::TOUCH_PER_WAVE > 0 ? Cfg::TOUCH_PER_WAVE : 1];
+
+  __device__ __forceinline__ void init(const TileJob& j) {
+    const int wave = loader_wave(), lane = threadIdx.x & 63;
+    K = j.K;
+    ldb_bytes = (uint32_t)(j.ldb * 2);
+    lda_bytes = (uint32_t)(j.lda * 2);
+    ra = make_rsrc(j.A, (int64_t)j.a_rows * j.lda * 2);
+    rb = make_rsrc(j.B, (int64_t)j.b_rows * j.ldb * 2);
+#pragma unroll
+    for (int i = 0; i < Cfg::A_PER_WAVE; ++i) {
+      const int row = (wave * Cfg::A_PER_WAVE + i) * (1024 / Cfg::RB) + lane / Cfg::KCH;
+      const int kc = (lane % Cfg::KCH) ^ swz_row<Cfg>(row);
+      const int gm = j.m0 + row;
+      a_kc[i] = kc;
+      a_off[i] = gm < j.a_rows ? (uint32_t)(((int64_t)gm * j.lda + kc * 8) * 2) : kOOB;
+    }
+    if constexpr (BL == B_NK) {
+#pragma unroll
+      for (int i = 0; i < Cfg::B_PER_WAVE; ++i) {
+        const int row = (wave * Cfg::B_PER_WAVE + i) * (1024 / Cfg::RB) + lane / Cfg::KCH;
+        const int kc = (lane % Cfg::KCH) ^ swz_row<Cfg>(row);
+        const int gn = j.n0 + row;
+        b_kc[i] = kc;
+        b_off[i] = gn < j.b_rows ? (uint32_t)(((int64_t)gn * j.ldb + kc * 8) * 2) : kOOB;
+      }
+    } else {
+      constexpr int ROW_BYTES = Cfg::BN * 2;
+#pragma unroll
+      for (int i = 0; i < Cfg::B_PER_WAVE; ++i) {
+        const int byte = (wave * Cfg::B_PER_WAVE + i) * 1024 + lane * 16;
+        const int k = byte / ROW_BYTES;                  // row of the 64 x BN tile
+        const int pchunk = (byte % ROW_BYTES) / 16;
+        const int cblk = (pchunk >> 1) ^ (Cfg::SWB * (k & 3));
+        const int c = cblk * 2 + (pchunk & 1);           // logical 16-byte chunk: n = 8c
+        const int gn = j.n0 + c * 8;
+        b_kc[i] = k;
+        b_off[i] = gn < j.N ? (uint32_t)(((int64_t)k * j.ldb + gn) * 2) : kOOB;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::TOUCH_PER_WAVE; ++i) {
+      const int line = threadIdx.x + i * Cfg::THREADS;
+      uint32_t off = kOOB;
+      int isb = 0;
+      if (line < Cfg::BM) {                       // A row `line`, 64 k = 128 bytes
+        const int gm = j.m0 + line;
+        if (gm < j.a_rows) off = (uint32_t)((int64_t)gm * j.lda * 2);
+      } else if (line < Cfg::TOUCH_LINES) {
+        const int bl = line - Cfg::BM;
+        isb = 1;
+        if constexpr (BL == B_NK) {               // B row n, 64 k = 128 bytes
+          const int gn = j.n0 + bl;
+          if (gn < j.b_rows) off = (uint32_t)((int64_t)gn * j.ldb * 2);
+        } else {                                  // B row k, segment of 64 n
+          constexpr int SEGS = Cfg::BN / 64;
+          const int k = bl / SEGS, gn = j.n0 + (bl % SEGS) * 64;
+          if (gn < j.N) off = (uint32_t)(((int64_t)k * j.ldb + gn) * 2);
+        }
+      }
+      t_off[i] = off;
+      t_isb[i] = isb;
+    }
+  }
+
+  // Touch every line of the K step starting at k0 (4 bytes per lane into an
+  // LDS scratch that is never read) so that the step's later loads hit L2.
+  __device__ __forceinline__ void touch(char* scratch, int k0) const {
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < Cfg::TOUCH_PER_WAVE; ++i) {
+      uint32_t off = t_off[i];
+      if (off != kOOB) {
+        if (t_isb[i] && BL == B_KN)
+          off += (uint32_t)k0 * ldb_bytes;
+        else
+          off += (uint32_t)k0 * 2;
+      }
+      // A and B lines are split on a wave boundary (BM is a multiple of 64),
+      // so the operand choice is wave-uniform: select the resource in SGPRs.
+      if (__builtin_amdgcn_readfirstlane(t_isb[i]))
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(scratch + (i * Cfg::NW + wave) * 256), 4, off, 0, 0,
+                                                 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(scratch + (i * Cfg::NW + wave) * 256), 4, off, 0, 0,
+                                                 0);
+    }
+  }
+
+  // Issue the loads of K step starting at k0 into `stage`.
+  // Index of this wave among the waves that issue global loads.
+  __device__ __forceinline__ static int loader_wave() {
+    const int w = threadIdx.x >> 6;
+    if constexpr (!Cfg::PP) return w;
+    else if constexpr (Cfg::PPMODE == 0) return w;   // group 0 = waves 0 .. NW/2-1
+    else return w >> 1;                             // group 0 = even waves
+  }
+
+  __device__ __forceinline__ void issue(char* stage, int k0) const {
+    const int wave = loader_wave();
+    char* la = stage;
+    char* lb = stage + Cfg::LDS_A;
+#pragma unroll
+    for (int i = 0; i < Cfg::A_PER_WAVE; ++i) {
+      const uint32_t off = (a_off[i] != kOOB && k0 + a_kc[i] * 8 < K) ? a_off[i] + (uint32_t)k0 * 2 : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(la + (wave * Cfg::A_PER_WAVE + i) * 1024), 16,
+                                               off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::B_PER_WAVE; ++i) {
+      uint32_t off;
+      if constexpr (BL == B_NK)
+        off = (b_off[i] != kOOB && k0 + b_kc[i] * 8 < K) ? b_off[i] + (uint32_t)k0 * 2 : kOOB;
+      else  // KN: the tile's row k is operand row k0 + k
+        off = (b_off[i] != kOOB && k0 + b_kc[i] < K) ? b_off[i] + (uint32_t)k0 * ldb_bytes : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(lb + (wave * Cfg::B_PER_WAVE + i) * 1024), 16,
+                                               off, 0, 0, 0);
+    }
+  }
+};
+
+// MFMA operand fragments of one 16-wide k step.
+template <class Cfg>
+struct Operands {
+  bf16x8_t a[Cfg::TM];
+  bf16x8_t b[Cfg::TN];
+};
+
+template <class Cfg, int BL>
+__device__ __forceinline__ void read_operands(Operands<Cfg>& o, const char* stage, int s, int wm, int wn, int lane) {
+  const char* la = stage;
+  const char* lb = stage + Cfg::LDS_A;
+  const int r32 = lane & 31, half = lane >> 5;
+  const int kc = s * 2 + half;
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i) {
+    const int m = wm * Cfg::WM + i * 32 + r32;
+    o.a[i] = *reinterpret_cast<const bf16x8_t*>(la + m * Cfg::RB + ((kc ^ swz_row<Cfg>(m)) * 16));
+  }
+  if constexpr (BL == B_NK) {
+#pragma unroll
+    for (int jn = 0; jn < Cfg::TN; ++jn) {
+      const int n = wn * Cfg::WN + jn * 32 + r32;
+      o.b[jn] = *reinterpret_cast<const bf16x8_t*>(lb + n * Cfg::RB + ((kc ^ swz_row<Cfg>(n)) * 16));
+    }
+  } else {
+    constexpr int ROW_BYTES = Cfg::BN * 2;
+    const int g = lane >> 4, jl = lane & 15;
+    const int r = jl >> 2, q = jl & 3;
+    const int k = s * 16 + (g >> 1) * 8 + r;          // this lane's row for the first read; +4 for the second
+#pragma unroll
+    for (int jn = 0; jn < Cfg::TN; ++jn) {
+      const int n = wn * Cfg::WN + jn * 32 + (g & 1) * 16 + q * 4;
+      const int c = n >> 3;
+      const int pblk = (c >> 1) ^ (Cfg::SWB * (k & 3));   // (k + 4) & 3 == k & 3
+      const int off = (pblk * 2 + (c & 1)) * 16 + (q & 1) * 8;
+      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(
+          (lds_void_t*)(lb + k * ROW_BYTES + off)));
+      const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(
+          (lds_void_t*)(lb + (k + 4) * ROW_BYTES + off)));
+      o.b[jn] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+}
+
+template <class Cfg>
+__device__ __forceinline__ void mfma_step(Frag<Cfg>& f, const Operands<Cfg>& o) {
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < Cfg::TN; ++jn)
+      f.acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[i], o.b[jn], f.acc[i][jn], 0, 0, 0);
+}
+
+// Each LDS stage is its own __shared__ object.  The loads of a later step are
+// LDS writes in flight (buffer_load ... lds) while the current stage is read;
+// with one object per stage, and every access naming its stage at compile
+// time, the compiler can see that they do not overlap and does not wait for
+// the in-flight loads before reading the current stage.
+template <class Cfg, int S>
+__device__ __forceinline__ char* stage_ptr() {
+  __shared__ __attribute__((aligned(1024))) char buf[Cfg::LDS_STAGE];
+  return buf;
+}
+
+template <class Cfg>
+__device__ __forceinline__ char* touch_scratch() {
+  __shared__ __attribute__((aligned(256))) char buf[Cfg::TOUCH_PER_WAVE > 0 ? Cfg::TOUCH_PER_WAVE * Cfg::THREADS * 4 : 4];
+  return buf;
+}
+
+// Loads of K step `step` into stage S, plus (L2PF > 0) the L2 touch of step
+// step + L2PF.  Every wave issues exactly LOADS_PER_WAVE vector-memory
+// instructions per call, so vmcnt arithmetic stays per-step.
+template <class Cfg, int BL, int S>
+__device__ __forceinline__ void issue_stage(const TileLoader<Cfg, BL>& ld, int step, int nk) {
+  ld.issue(stage_ptr<Cfg, S>(), step * Cfg::BK);
+  if constexpr (Cfg::L2PF > 0) {
+    const int ts = step + Cfg::L2PF;
+    ld.touch(touch_scratch<Cfg>(), (ts < nk ? ts : nk - 1) * Cfg::BK);
+  }
+}
+
+template <class Cfg, int BL, int S>
+__device__ __forceinline__ void prefetch(const TileLoader<Cfg, BL>& ld, int nk) {
+  if constexpr (S < Cfg::STAGES - 1) {
+    if (S < nk) issue_stage<Cfg, BL, S>(ld, S, nk);
+    prefetch<Cfg, BL, S + 1>(ld, nk);
+  }
+}
+
+// Wait until this wave's loads of step `t` have landed, given that every
+// step up to min(t + STAGES - 2, nk - 1) has been issued.
+template <class Cfg>
+__device__ __forceinline__ void wait_step(int t, int nk) {
+  wait_vmcnt(min(Cfg::STAGES - 2, nk - 1 - t) * Cfg::LOADS_PER_WAVE + Cfg::TOUCH_PER_WAVE);
+}
+
+// One K step on stage S, software-pipelined across steps.  On entry the
+// fragments of this step's first 16-wide k slice are in o[0].  Each slice's
+// MFMAs run while the next slice's fragments are read.  Before the last
+// slice's MFMAs, the workgroup waits for the next step's data and passes the
+// barrier (every wave has finished reading stage S by then), refills stage S
+// with the loads of step kt + STAGES, and starts reading the next step's
+// first slice; the last slice's MFMAs then cover that latency.
+template <class Cfg, int BL, int S>
+__device__ __forceinline__ void kstep(Frag<Cfg>& f, const TileLoader<Cfg, BL>& ld, Operands<Cfg> (&o)[2], int kt,
+                                      int nk, int wm, int wn, int lane) {
+  constexpr int SUB = Cfg::BK / 16;
+  static_assert(SUB % 2 == 0, "even number of k slices per step");
+  const char* cur = stage_ptr<Cfg, S>();
+#pragma unroll
+  for (int s = 0; s < SUB - 1; ++s) {
+    read_operands<Cfg, BL>(o[(s + 1) & 1], cur, s + 1, wm, wn, lane);
+    mfma_step<Cfg>(f, o[s & 1]);
+#ifdef TPF_IGLP
+    __builtin_amdgcn_iglp_opt(TPF_IGLP);
+#endif
+  }
+  if (kt + 1 < nk) {
+    wait_step<Cfg>(kt + 1, nk);
+    __syncthreads();
+    if (kt + Cfg::STAGES < nk) issue_stage<Cfg, BL, S>(ld, kt + Cfg::STAGES, nk);
+    read_operands<Cfg, BL>(o[0], stage_ptr<Cfg, (S + 1) % Cfg::STAGES>(), 0, wm, wn, lane);
+  }
+  mfma_step<Cfg>(f, o[1]);
+}
+
+template <class Cfg, int BL, int S>
+__device__ __forceinline__ void ksteps(Frag<Cfg>& f, const TileLoader<Cfg, BL>& ld, Operands<Cfg> (&o)[2], int kt,
+                                       int nk, int wm, int wn, int lane) {
+  if constexpr (S < Cfg::STAGES) {
+    if (kt + S < nk) {
+      kstep<Cfg, BL, S>(f, ld, o, kt + S, nk, wm, wn, lane);
+      ksteps<Cfg, BL, S + 1>(f, ld, o, kt, nk, wm, wn, lane);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong schedule.  The waves form two groups, paired so that each SIMD
+// runs one wave of each.  Group 1 starts one barrier phase behind group 0,
+// and every wave alternates
+//   M(t): read all fragments of step t from LDS  (group 0 also issues the
+//         global loads of step t + STAGES - 1)
+//   C(t): the MFMAs of step t from registers     (group 0 then waits for its
+//         loads of step t + 1)
+// with a workgroup barrier after each phase.  While one wave of a SIMD is in
+// C, the other is in M, so the matrix core is fed back to back.  Stage t is
+// read by group 0 in phase 2t and by group 1 in phase 2t+1, so its refill
+// (step t + STAGES) is issued in group 0's M(t+1), phase 2t+2.
+// ---------------------------------------------------------------------------
+template <class Cfg>
+__device__ __forceinline__ int pp_group(int wave) {
+  if constexpr (Cfg::PPMODE == 0) return wave >= Cfg::NW / 2 ? 1 : 0;
+  else return wave & 1;
+}
+
+template <class Cfg, int BL, int S>
+__device__ __forceinline__ void pp_step(Frag<Cfg>& f, const TileLoader<Cfg, BL>& ld, int grp, int t, int nk, int wm,
+                                        int wn, int lane) {
+  constexpr int SUB = Cfg::BK / 16;
+  Operands<Cfg> o[SUB];
+  // ---- M(t)
+  if (grp == 0) {
+    constexpr int SL = (S + Cfg::STAGES - 1) % Cfg::STAGES;   // stage of step t-1 (== step t+STAGES-1)
+    if (t + Cfg::STAGES - 1 < nk) ld.issue(stage_ptr<Cfg, SL>(), (t + Cfg::STAGES - 1) * Cfg::BK);
+  }
+  const char* cur = stage_ptr<Cfg, S>();
+#pragma unroll
+  for (int s = 0; s < SUB; ++s) read_operands<Cfg, BL>(o[s], cur, s, wm, wn, lane);
+  __syncthreads();
+  // ---- C(t)
+#pragma unroll
+  for (int s = 0; s < SUB; ++s) mfma_step<Cfg>(f, o[s]);
+  if (grp == 0 && t + 1 < nk) {
+    // loads issued after step t+1's: steps t+2 .. min(t+STAGES-1, nk-1)
+    wait_vmcnt(min(Cfg::STAGES - 2, nk - 2 - t) * Cfg::LOADS_PER_WAVE);
+  }
+  __syncthreads();
+}
+
+template <class Cfg, int BL, int S>
+__device__ __forceinline__ void pp_steps(Frag<Cfg>& f, const TileLoader<Cfg, BL>& ld, int grp, int t, int nk, int wm,
+                                         int wn, int lane) {
+  if constexpr (S < Cfg::STAGES) {
+    if (t + S < nk) {
+      pp_step<Cfg, BL, S>(f, ld, grp, t + S, nk, wm, wn, lane);
+      pp_steps<Cfg, BL, S + 1>(f, ld, grp, t, nk, wm, wn, lane);
+    }
+  }
+}
+
+template <class Cfg, int BL, int S>
+__device__ __forceinline__ void pp_prefetch(const TileLoader<Cfg, BL>& ld, int nk) {
+  if constexpr (S < Cfg::STAGES - 1) {
+    if (S < nk) ld.issue(stage_ptr<Cfg, S>(), S * Cfg::BK);
+    pp_prefetch<Cfg, BL, S + 1>(ld, nk);
+  }
+}
+
+template <class Cfg, int BL>
+__device__ __forceinline__ void gemm_tile_pp(Frag<Cfg>& f, const TileJob& j) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+  const int grp = pp_group<Cfg>(wave);
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < Cfg::TN; ++jn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) f.acc[i][jn][v] = 0.0f;
+  const int nk = (j.K + Cfg::BK - 1) / Cfg::BK;
+  TileLoader<Cfg, BL> ld;
+  if (grp == 0) {
+    ld.init(j);
+    pp_prefetch<Cfg, BL, 0>(ld, nk);
+    wait_vmcnt(min(Cfg::STAGES - 2, nk - 1) * Cfg::LOADS_PER_WAVE);
+  }
+  __syncthreads();                 // step 0 has landed
+  if (grp == 1) __syncthreads();   // group 1 starts one phase behind
+  for (int t = 0; t < nk; t += Cfg::STAGES) pp_steps<Cfg, BL, 0>(f, ld, grp, t, nk, wm, wn, lane);
+  if (grp == 0) __syncthreads();   // match group 1's phase count
+}
+
+// Full K loop of one tile into registers.  Ends with a barrier, so the
+// caller may reuse the stages (e.g. stage 0's first word) immediately.
+template <class Cfg, int BL>
+__device__ __forceinline__ void gemm_tile(Frag<Cfg>& f, const TileJob& j) {
+  if constexpr (Cfg::PP) {
+    gemm_tile_pp<Cfg, BL>(f, j);
+    return;
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < Cfg::TN; ++jn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) f.acc[i][jn][v] = 0.0f;
+
+  TileLoader<Cfg, BL> ld;
+  ld.init(j);
+  const int nk = (j.K + Cfg::BK - 1) / Cfg::BK;
+  // Steps 0 .. STAGES-2 are loaded up front; step STAGES-1 is issued into
+  // the last stage right away (nothing has used it yet).
+  prefetch<Cfg, BL, 0>(ld, nk);
+  wait_step<Cfg>(0, nk);
+  __syncthreads();
+  if (Cfg::STAGES - 1 < nk) issue_stage<Cfg, BL, Cfg::STAGES - 1>(ld, Cfg::STAGES - 1, nk);
+  Operands<Cfg> o[2];
+  read_operands<Cfg, BL>(o[0], stage_ptr<Cfg, 0>(), 0, wm, wn, lane);
+  for (int kt = 0; kt < nk; kt += Cfg::STAGES) ksteps<Cfg, BL, 0>(f, ld, o, kt, nk, wm, wn, lane);
+  __syncthreads();
+}
+
+// Write the accumulators of one tile.  Element (row, col) of the 32x32 MFMA
+// block held in register v of lane l: col = l % 32,
+// row = 8 * (v / 4) + 4 * (l / 32) + v % 4.
+template <class Cfg, int OUT>
+__device__ __forceinline__ void store_tile(const Frag<Cfg>& f, const TileJob& j, void* out, int64_t ldo) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+  const int r32 = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i) {
+#pragma unroll
+    for (int jn = 0; jn < Cfg::TN; ++jn) {
+      const int col = j.n0 + wn * Cfg::WN + jn * 32 + r32;
+      if (col >= j.N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * Cfg::WM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (row < j.rows) {
+          const int64_t off = (int64_t)(j.m0 + row) * ldo + col;
+          if constexpr (OUT == OUT_F32)
+            reinterpret_cast<float*>(out)[off] = f.acc[i][jn][v];
+          else
+            reinterpret_cast<uint16_t*>(out)[off] = (uint16_t)f32_to_bf16_bits(f.acc[i][jn][v]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace tpf

@@ -5,11 +5,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "tpf_device.hpp"
+#include "tpf_gemm.hpp"
 
 namespace tpf {
 
 constexpr int kMaxShards = 16;
+constexpr int kXcds = 8;      // accelerator dies (XCDs) of an MI355X, each with its own L2
 constexpr int kMaxChunks = 64;
 // GEMM and reduce segments per chunk, plus one copy segment per slice.
 constexpr int kMaxSegs = 2 * kMaxChunks + kMaxShards + 2;
@@ -23,6 +24,7 @@ struct Ctrl {
   int pad;
   int ready[kMaxChunks];      // completed GEMM tiles per chunk
   int landed[kMaxShards];     // copied segments per gathered slice
+  int sub[kMaxChunks][kXcds]; // claimed tiles of each XCD's share of a chunk
 };
 
 enum TaskKind : int { TK_GEMM = 0, TK_REDUCE = 1, TK_COPY = 2 };
@@ -38,6 +40,7 @@ struct GemmOperands {
   int64_t ldd;
   int dst_dtype;              // OUT_F32 or OUT_BF16
   int M, N, K;                // rows, output width, reduction length per shard
+  int b_rows;                 // rows of each B operand (K for KN weights, N for NK)
   int nshard;                 // shard GEMMs (p, or 1 for AllGather->MatMul)
 };
 
@@ -55,7 +58,7 @@ struct FusedArgs {
   const float* P;             // partials (reducing ops)
   int64_t p_stride;           // elements between shards' partials (M * N)
   int p;                      // shards summed by the reduction
-  int reduce_rows;            // rows per reduce task
+  int64_t reduce_elems;      // output elements per reduce task (multiple of 4)
   // AllGather: slice r (slice_bytes) is copied to gathered + r * slice_bytes
   const char* src[kMaxShards];
   char* gathered;
@@ -77,8 +80,24 @@ struct FusedArgs {
 // Tile configurations (chosen from the op's shape only, never from the chunk
 // count, so every chunking runs the same per-element arithmetic).
 enum CfgId : int { CFG_LARGE = 0, CFG_SMALL = 1 };
-using CfgLarge = TileCfg<256, 256, 64, 2, 2>;
-using CfgSmall = TileCfg<32, 128, 64, 1, 4>;
+#ifndef TPF_LARGE_STAGES
+#define TPF_LARGE_STAGES 2
+#endif
+#ifndef TPF_LARGE_BK
+#define TPF_LARGE_BK 64
+#endif
+#ifndef TPF_LARGE_L2PF
+#define TPF_LARGE_L2PF 1
+#endif
+#ifndef TPF_LARGE_PP
+#define TPF_LARGE_PP 0
+#endif
+#ifndef TPF_LARGE_PPMODE
+#define TPF_LARGE_PPMODE 0
+#endif
+using CfgLarge = TileCfg<256, 256, 2, 4, TPF_LARGE_STAGES, TPF_LARGE_BK, TPF_LARGE_L2PF, TPF_LARGE_PP,
+                         TPF_LARGE_PPMODE>;   // 8 waves
+using CfgSmall = TileCfg<32, 128, 1, 4, 4, 64, 0>;    // decode-shaped rows, 4 stages of 20 KiB
 
 int cfg_bm(int cfg);
 int cfg_bn(int cfg);
@@ -87,6 +106,7 @@ hipError_t launch_gemm_rows(int cfg, int bl, const GemmOperands& g, int row0, in
 hipError_t launch_reduce_rows(const float* P, int64_t stride, int p, int row0, int row1, int N,
                               const ReduceOut& o, int num_cus, hipStream_t s);
 hipError_t launch_fused(int cfg, int bl, const FusedArgs& a, int grid, hipStream_t s);
+int fused_occupancy(int cfg, int bl);   // resident fused workgroups per CU
 hipError_t launch_copy(const char* src, char* dst, int64_t bytes, int num_cus, hipStream_t s);
 hipError_t launch_clear_status(Ctrl* c, hipStream_t s);
 

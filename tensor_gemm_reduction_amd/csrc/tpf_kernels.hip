@@ -54,6 +54,8 @@ __device__ __forceinline__ TileJob make_job(const GemmOperands& g, int shard, in
   j.B = g.B[shard];
   j.lda = g.lda;
   j.ldb = g.ldb;
+  j.a_rows = g.M;
+  j.b_rows = g.b_rows;
   j.m0 = row0 + tm * Cfg::BM;
   j.rows = min(Cfg::BM, row1 - j.m0);
   j.n0 = tn * Cfg::BN;
@@ -67,23 +69,44 @@ struct GemmRowsArgs {
   int row0, row1;
 };
 
+// Tile u of a row range (shard-major) -> (shard, tm, tn).  Within a shard the
+// tiles go in groups of kGroupM tile-rows, column by column, so that tiles
+// running at the same time share A and B panels.
+constexpr int kGroupM = 4;
+
+__device__ __forceinline__ void tile_coords(int u, int tiles_m, int tiles_n, int& shard, int& tm, int& tn) {
+  const int per_shard = tiles_m * tiles_n;
+  shard = u / per_shard;
+  const int t = u - shard * per_shard;
+  const int group = t / (kGroupM * tiles_n);
+  const int first = group * kGroupM;
+  const int gsize = min(kGroupM, tiles_m - first);
+  const int w = t - first * tiles_n;
+  tm = first + w % gsize;
+  tn = w / gsize;
+}
+
+// Block b runs on XCD b % 8 (round-robin dispatch).  Give each XCD a
+// contiguous run of tiles so its L2 sees neighbouring tiles.
+__device__ __forceinline__ int xcd_tile(int b, int total) {
+  const int x = b & 7, i = b >> 3;
+  const int q = total >> 3, r = total & 7;
+  return x * q + min(x, r) + i;
+}
+
 template <class Cfg, int BL>
-__global__ __launch_bounds__(256) void gemm_rows_kernel(GemmRowsArgs args) {
+__global__ __launch_bounds__(Cfg::THREADS) void gemm_rows_kernel(GemmRowsArgs args) {
   (void)args;
   const GemmRowsArgs& ka = kernarg<GemmRowsArgs>();
   const GemmOperands& g = ka.g;
   const int row0 = ka.row0, row1 = ka.row1;
-  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
   const int tiles_n = (g.N + Cfg::BN - 1) / Cfg::BN;
   const int tiles_m = (row1 - row0 + Cfg::BM - 1) / Cfg::BM;
-  const int per_shard = tiles_m * tiles_n;
-  const int b = blockIdx.x;
-  const int shard = b / per_shard;
-  const int rem = b - shard * per_shard;
-  const int tm = rem / tiles_n, tn = rem - (rem / tiles_n) * tiles_n;
+  int shard, tm, tn;
+  tile_coords(xcd_tile(blockIdx.x, (int)gridDim.x), tiles_m, tiles_n, shard, tm, tn);
   const TileJob j = make_job<Cfg>(g, shard, row0, row1, tm, tn);
   Frag<Cfg> f;
-  gemm_tile<Cfg, BL>(f, j, lds);
+  gemm_tile<Cfg, BL>(f, j);
   store_any<Cfg>(f, j, g, shard);
 }
 
@@ -119,32 +142,85 @@ __global__ void clear_status_kernel(Ctrl* c) {
   if (threadIdx.x == 0) atomic_store_relaxed(&c->status, 0);
 }
 
-// Thread 0 polls *ctr until it reaches target or the bound runs out.
+// The XCD (accelerator die) this wave runs on, from the hardware register
+// XCC_ID.  Used only as a locality hint.
+__device__ __forceinline__ int xcd_id() {
+  return (int)(__builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & (kXcds - 1));
+}
+
+// Claim one of the G GEMM tiles of chunk c for a workgroup on XCD x.  The
+// tiles of a chunk are split into kXcds contiguous shares; a workgroup takes
+// the next tile of its own XCD's share, or, once that share is used up, of
+// the next XCD's.  The global ticket already guarantees that exactly G
+// claims are made for chunk c, so every claim finds a free tile.
+__device__ __forceinline__ int claim_tile(Ctrl* ctl, int c, int G, int x) {
+  const int q = G / kXcds, r = G % kXcds;
+  for (int d = 0; d < kXcds; ++d) {
+    const int y = (x + d) & (kXcds - 1);
+    const int size = q + (y < r ? 1 : 0);
+    if (size == 0) continue;
+    const int s = __hip_atomic_fetch_add(&ctl->sub[c][y], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (s < size) return y * q + min(y, r) + s;
+  }
+  return -1;   // unreachable: G claims are made for G tiles
+}
+
+// Thread 0 polls *ctr with relaxed loads (no cache maintenance per poll)
+// until it reaches target or the bound runs out, then performs one
+// agent-scope acquire.  The caller's following barrier orders the other
+// threads' loads after that acquire.
 __device__ __forceinline__ void wait_at_least(const int* ctr, int target, const FusedArgs& a) {
   if (a.unreachable) target = target + 1 + (1 << 30);
   int64_t polls = 0;
-  while (atomic_load_acquire(ctr) < target) {
+  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
     if (++polls > a.spin_limit) {
       __hip_atomic_fetch_or(&a.ctrl->status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
     __builtin_amdgcn_s_sleep(2);
   }
+  fence_acquire_agent();
+}
+
+// Publish this workgroup's global writes: every thread's writes are ordered
+// before the barrier (workgroup-scope release), and thread 0's agent-scope
+// release increment makes them visible to any workgroup on any XCD that
+// acquires the counter.
+__device__ __forceinline__ void publish(int* ctr) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (threadIdx.x == 0) atomic_add_release(ctr, 1);
 }
 
 template <class Cfg, int BL>
-__global__ __launch_bounds__(256) void fused_kernel(FusedArgs args) {
+__global__ __launch_bounds__(Cfg::THREADS) void fused_kernel(FusedArgs args) {
   (void)args;
   const FusedArgs& a = kernarg<FusedArgs>();
-  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
-  __shared__ int s_ticket;
+  // The ticket is broadcast through the first word of LDS stage 0, which is
+  // idle between tasks (gemm_tile ends with every load consumed and a
+  // barrier) and keeps the LDS footprint at exactly STAGES stages.
+  int& s_ticket = *reinterpret_cast<int*>(stage_ptr<Cfg, 0>());
   const int tid = threadIdx.x;
   Ctrl* ctl = a.ctrl;
   const int total = a.seg_start[a.nseg];
   const int tiles_n = (a.g.N + Cfg::BN - 1) / Cfg::BN;
   int seg = 0;
+  const int xcd = xcd_id();
   for (;;) {
-    if (tid == 0) s_ticket = __hip_atomic_fetch_add(&ctl->ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      const int tk = __hip_atomic_fetch_add(&ctl->ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int val = tk;
+      if (tk < total) {
+        int sg = seg;
+        while (a.seg_start[sg + 1] <= tk) ++sg;
+        // A GEMM ticket names the chunk; the tile comes from this XCD's share.
+        if ((a.seg_info[sg] & 0xF) == TK_GEMM) {
+          const int c = a.seg_info[sg] >> 4;
+          val = a.seg_start[sg] + claim_tile(ctl, c, a.seg_start[sg + 1] - a.seg_start[sg], xcd);
+        }
+      }
+      s_ticket = val;
+    }
     __syncthreads();
     const int t = s_ticket;
     __syncthreads();
@@ -158,10 +234,8 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs args) {
       const int c = idx;
       const int row0 = a.ch.row0(c), row1 = a.ch.row1(c);
       const int tiles_m = (row1 - row0 + Cfg::BM - 1) / Cfg::BM;
-      const int per_shard = tiles_m * tiles_n;
-      const int shard = u / per_shard;
-      const int rem = u - shard * per_shard;
-      const int tm = rem / tiles_n, tn = rem - (rem / tiles_n) * tiles_n;
+      int shard, tm, tn;
+      tile_coords(u, tiles_m, tiles_n, shard, tm, tn);
       const TileJob j = make_job<Cfg>(a.g, shard, row0, row1, tm, tn);
       if (a.gather) {
         // The rows of this tile must have landed in the gathered buffer.
@@ -170,39 +244,34 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs args) {
           for (int s = s0; s <= s1; ++s) wait_at_least(&ctl->landed[s], a.copy_segs, a);
         }
         __syncthreads();
-        fence_acquire_agent();
       }
       Frag<Cfg> f;
-      gemm_tile<Cfg, BL>(f, j, lds);
+      gemm_tile<Cfg, BL>(f, j);
       store_any<Cfg>(f, j, a.g, shard);
-      if (!a.gather) {
-        fence_release_agent();
-        __syncthreads();
-        if (tid == 0) atomic_add_release(&ctl->ready[c], 1);
-      }
+      if (!a.gather) publish(&ctl->ready[c]);
     } else if (kind == TK_REDUCE) {
       const int c = idx;
       if (tid == 0) wait_at_least(&ctl->ready[c], a.gemm_tasks[c], a);
       __syncthreads();
-      fence_acquire_agent();
-      const int r0 = a.ch.row0(c) + u * a.reduce_rows;
-      const int r1 = min(r0 + a.reduce_rows, a.ch.row1(c));
-      reduce_any(a.P, a.p_stride, a.p, (int64_t)r0 * a.g.N, (int64_t)r1 * a.g.N, a.g.N, a.ro, tid, 256);
+      const int64_t e0 = (int64_t)a.ch.row0(c) * a.g.N + (int64_t)u * a.reduce_elems;
+      const int64_t e1 = min(e0 + a.reduce_elems, (int64_t)a.ch.row1(c) * a.g.N);
+      reduce_any(a.P, a.p_stride, a.p, e0, e1, a.g.N, a.ro, tid, Cfg::THREADS);
     } else {  // TK_COPY
       const int r = idx;
       const int64_t b0 = (int64_t)u * a.copy_seg_bytes;
       const int64_t b1 = min(b0 + a.copy_seg_bytes, a.slice_bytes);
-      copy_range(a.src[r], a.gathered + (int64_t)r * a.slice_bytes, b0, b1, tid, 256);
-      fence_release_agent();
-      __syncthreads();
-      if (tid == 0) atomic_add_release(&ctl->landed[r], 1);
+      copy_range(a.src[r], a.gathered + (int64_t)r * a.slice_bytes, b0, b1, tid, Cfg::THREADS);
+      publish(&ctl->landed[r]);
     }
   }
   // The last workgroup out clears the counters for the next call.
   if (tid == 0) {
     const int d = atomic_add_acq_rel(&ctl->done, 1);
     if (d == (int)gridDim.x - 1) {
-      for (int c = 0; c < a.ch.n; ++c) atomic_store_relaxed(&ctl->ready[c], 0);
+      for (int c = 0; c < a.ch.n; ++c) {
+        atomic_store_relaxed(&ctl->ready[c], 0);
+        for (int x = 0; x < kXcds; ++x) atomic_store_relaxed(&ctl->sub[c][x], 0);
+      }
       for (int s = 0; s < kMaxShards; ++s) atomic_store_relaxed(&ctl->landed[s], 0);
       atomic_store_relaxed(&ctl->ticket, 0);
       atomic_store_relaxed(&ctl->done, 0);
@@ -222,9 +291,9 @@ static hipError_t launch_gemm_cfg(int bl, const GemmOperands& g, int row0, int r
   if (grid <= 0) return hipSuccess;
   GemmRowsArgs args{g, row0, row1};
   if (bl == B_KN)
-    hipLaunchKernelGGL((gemm_rows_kernel<Cfg, B_KN>), dim3(grid), dim3(256), 0, s, args);
+    hipLaunchKernelGGL((gemm_rows_kernel<Cfg, B_KN>), dim3(grid), dim3(Cfg::THREADS), 0, s, args);
   else
-    hipLaunchKernelGGL((gemm_rows_kernel<Cfg, B_NK>), dim3(grid), dim3(256), 0, s, args);
+    hipLaunchKernelGGL((gemm_rows_kernel<Cfg, B_NK>), dim3(grid), dim3(Cfg::THREADS), 0, s, args);
   return hipGetLastError();
 }
 
@@ -255,17 +324,35 @@ hipError_t launch_copy(const char* src, char* dst, int64_t bytes, int num_cus, h
   return hipGetLastError();
 }
 
+template <class Cfg, int BL>
+static int fused_blocks_per_cu() {
+  static int cached = 0;
+  if (!cached) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fused_kernel<Cfg, BL>, Cfg::THREADS, 0) != hipSuccess ||
+        n < 1)
+      n = 1;
+    cached = n;
+  }
+  return cached;
+}
+
+int fused_occupancy(int cfg, int bl) {
+  if (cfg == CFG_SMALL) return bl == B_KN ? fused_blocks_per_cu<CfgSmall, B_KN>() : fused_blocks_per_cu<CfgSmall, B_NK>();
+  return bl == B_KN ? fused_blocks_per_cu<CfgLarge, B_KN>() : fused_blocks_per_cu<CfgLarge, B_NK>();
+}
+
 hipError_t launch_fused(int cfg, int bl, const FusedArgs& a, int grid, hipStream_t s) {
   if (cfg == CFG_SMALL) {
     if (bl == B_KN)
-      hipLaunchKernelGGL((fused_kernel<CfgSmall, B_KN>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((fused_kernel<CfgSmall, B_KN>), dim3(grid), dim3(CfgSmall::THREADS), 0, s, a);
     else
-      hipLaunchKernelGGL((fused_kernel<CfgSmall, B_NK>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((fused_kernel<CfgSmall, B_NK>), dim3(grid), dim3(CfgSmall::THREADS), 0, s, a);
   } else {
     if (bl == B_KN)
-      hipLaunchKernelGGL((fused_kernel<CfgLarge, B_KN>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((fused_kernel<CfgLarge, B_KN>), dim3(grid), dim3(CfgLarge::THREADS), 0, s, a);
     else
-      hipLaunchKernelGGL((fused_kernel<CfgLarge, B_NK>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((fused_kernel<CfgLarge, B_NK>), dim3(grid), dim3(CfgLarge::THREADS), 0, s, a);
   }
   return hipGetLastError();
 }
