@@ -37,11 +37,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mlp_down")
     ap.add_argument("--chunks", type=int, default=0, help="0 = the workload's default")
-    ap.add_argument("--sched", default="persistent")
+    ap.add_argument("--sched", default="auto", help="auto: persistent kernel for >= 2 chunks, else unfused")
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated to defeat the 256 MB last-level cache")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--modes", default="gemm_only,reduce_only,unfused,two_stream,persistent")
+    ap.add_argument("--modes", default="gemm_only,reduce_only,unfused,two_stream,persistent,auto")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -57,6 +59,18 @@ def main():
 
     import torch
     from tensor_gemm_reduction_amd import inputs, tpfuse as tp
+
+    if args.copy_calibration:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters
+        # give the scale between those counters and real HBM bytes.
+        n = args.copy_calibration * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "note": "plain device copy for counter calibration"}), flush=True)
+        return
 
     tp.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -188,13 +202,20 @@ def main():
                    "workspace_bytes": ws_bytes, "note": wl.note},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "fused_kernel" if args.sched == "persistent" else args.sched,
+                     "kernel": kernel_name(args.sched, n),
                      "avg_kernel_ms": round(avg_kernel_ms, 4)},
         "cpu_baseline": cpu,
         "modes": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in modes.items()},
         **{k: round(v, 4) for k, v in extra.items()},
     }
     print(json.dumps(out), flush=True)
+
+
+def kernel_name(sched, n):
+    """The kernel that dominates one step of `sched` (what `roofline` prices)."""
+    if sched == "persistent" or (sched == "auto" and n >= 2):
+        return "fused_kernel (persistent: shard GEMM tiles + chunk reductions)"
+    return "gemm_rows_kernel (shard GEMM tiles)"
 
 
 def cpu_baseline(wl, inp, seconds):

@@ -75,7 +75,7 @@ extern "C" {
 #define TPF_F32 1
 
 /* Schedulers.  Every scheduler computes the same bits. */
-#define TPF_SCHED_AUTO 0         /* library's choice (currently PERSISTENT) */
+#define TPF_SCHED_AUTO 0         /* library's choice: PERSISTENT for n_chunks >= 2, else UNFUSED */
 #define TPF_SCHED_PERSISTENT 1   /* one persistent kernel: work queue + per-chunk ready counters */
 #define TPF_SCHED_TWO_STREAM 2   /* per-chunk GEMM launches, reductions on a side stream after per-chunk events */
 #define TPF_SCHED_UNFUSED 3      /* whole GEMM, then the whole reduction (the serial baseline) */
@@ -167,6 +167,19 @@ int tpf_sync_status(tpf_handle h, void* stream);
  * never reached, so each wait ends by its bound: used to test the timeout
  * path without any kernel hanging. */
 int tpf_debug_set_wait(tpf_handle h, int64_t spins, int unreachable);
+
+/* Debug: record the persistent kernel's task timeline.  `events` is a
+ * caller-owned device buffer of `max_events` 32-byte records
+ *   { uint32 ticket; uint16 kind (0 GEMM tile, 1 reduce, 2 copy);
+ *     uint16 chunk (or slice); uint16 workgroup; uint16 xcd;
+ *     uint32 mid (for a GEMM tile that also reduced a slice of the previous
+ *                 chunk: clock ticks from t_start to the end of its GEMM part);
+ *     uint64 t_start; uint64 t_end }   (little-endian)
+ * indexed by ticket, stamped with the GPU's constant 100 MHz clock.  Every
+ * later persistent call on this handle writes the events of its first
+ * max_events tickets; pass NULL / 0 to stop.  The buffer must stay valid
+ * while such calls run. */
+int tpf_debug_set_timeline(tpf_handle h, void* events, int max_events);
 
 /* Static text for a status code. */
 const char* tpf_status_string(int code);

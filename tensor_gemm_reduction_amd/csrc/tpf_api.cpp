@@ -31,11 +31,15 @@ struct tpf_context {
   Ctrl* ctrl = nullptr;
   int64_t spin_limit = 0;
   int unreachable = 0;
+  TimelineEvent* timeline = nullptr;   // caller-owned device buffer (debug)
+  int timeline_cap = 0;
 };
 
 namespace {
 
-constexpr int64_t kDefaultSpinLimit = (int64_t)1 << 26;   // polls; each poll sleeps ~100 cycles
+// Polls before a bounded wait gives up (polls back off to ~4K clocks each,
+// so this is a few seconds: far beyond any legitimate wait).
+constexpr int64_t kDefaultSpinLimit = (int64_t)1 << 21;
 
 thread_local std::string g_last_error;
 
@@ -116,7 +120,15 @@ int check_handle(tpf_handle h) {
   return TPF_OK;
 }
 
-int resolve_sched(int sched) { return sched == TPF_SCHED_AUTO ? TPF_SCHED_PERSISTENT : sched; }
+// AUTO: with one chunk there is no later GEMM for the reduction to overlap,
+// and a kernel boundary is the cheapest device-wide barrier, so the GEMM
+// kernel is followed by the reduction kernel; with two or more chunks the
+// persistent kernel overlaps each chunk's reduction with the next chunk's
+// GEMM.
+int resolve_sched(int sched, int n_chunks) {
+  if (sched != TPF_SCHED_AUTO) return sched;
+  return n_chunks >= 2 ? TPF_SCHED_PERSISTENT : TPF_SCHED_UNFUSED;
+}
 
 // A reducing op (row-parallel AR/RS, or dX with either semantic).
 struct ReduceCall {
@@ -188,17 +200,29 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
       a.P = rc.P;
       a.p_stride = stride;
       a.p = rc.p;
-      // Reduce tasks of 8 Ki output elements (32 KiB of fp32 partials per shard):
-      // many small tasks spread a chunk's reduction over many CUs.
-      a.reduce_elems = 8192;
+      // Reduce tasks small enough that one chunk's reduction spreads over
+      // every resident workgroup (between 1 Ki and 8 Ki output elements, i.e.
+      // 4 to 32 KiB of fp32 partials per shard).
+      const int occ = fused_occupancy(cfg, rc.bl);
+      const int64_t chunk_elems = (int64_t)(ch.row1(0) - ch.row0(0)) * rc.N;
+      int64_t re = chunk_elems / ((int64_t)h->num_cus * occ);
+      re = std::max<int64_t>(1024, std::min<int64_t>(8192, re));
+      a.reduce_elems = (re + 255) / 256 * 256;
       a.gather = 0;
       a.ch = ch;
       a.ctrl = h->ctrl;
       a.spin_limit = h->spin_limit > 0 ? h->spin_limit : kDefaultSpinLimit;
       a.unreachable = h->unreachable;
+      a.timeline = h->timeline;
+      a.timeline_cap = h->timeline_cap;
       const int bm = cfg_bm(cfg), bn = cfg_bn(cfg);
       const int tiles_n = (rc.N + bn - 1) / bn;
-      // Queue order: G0, G1, R0, G2, R1, ..., G(n-1), R(n-2), R(n-1).
+      // Queue order: G0, G1, ..., G(n-1), R(n-1).  Each GEMM tile of chunk
+      // c > 0 also reduces one slice of chunk c-1 once it is ready (all of
+      // chunk c-1's tiles hold smaller tickets), so the reduction of chunk
+      // c-1 runs spread over chunk c's GEMM; only the last chunk's
+      // reduction has tasks of its own.
+      a.piggyback = 1;
       int nseg = 0, t = 0;
       auto add_seg = [&](int kind, int idx, int count) {
         a.seg_start[nseg] = t;
@@ -212,11 +236,7 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
         return (int)((e + a.reduce_elems - 1) / a.reduce_elems);
       };
       for (int c = 0; c < ch.n; ++c) a.gemm_tasks[c] = gemm_count(c);
-      add_seg(TK_GEMM, 0, gemm_count(0));
-      for (int c = 1; c < ch.n; ++c) {
-        add_seg(TK_GEMM, c, gemm_count(c));
-        add_seg(TK_REDUCE, c - 1, red_count(c - 1));
-      }
+      for (int c = 0; c < ch.n; ++c) add_seg(TK_GEMM, c, gemm_count(c));
       add_seg(TK_REDUCE, ch.n - 1, red_count(ch.n - 1));
       a.nseg = nseg;
       a.seg_start[nseg] = t;
@@ -345,7 +365,7 @@ int tpf_matmul_allreduce(tpf_handle h, int p, int64_t M, int64_t N, int64_t K_sh
   rc.ro.rows_per_slice = (int)M;
   rc.ro.dtype = out_kind(y_dtype);
   rc.n_chunks = n_chunks;
-  rc.sched = resolve_sched(sched);
+  rc.sched = resolve_sched(sched, n_chunks);
   rc.P = reinterpret_cast<float*>(ws);
   return run_reduce_call(h, rc, reinterpret_cast<hipStream_t>(stream));
 }
@@ -373,7 +393,7 @@ int tpf_matmul_reducescatter(tpf_handle h, int p, int64_t M, int64_t N, int64_t 
   rc.ro.rows_per_slice = (int)(M / p);
   rc.ro.dtype = out_kind(y_dtype);
   rc.n_chunks = n_chunks;
-  rc.sched = resolve_sched(sched);
+  rc.sched = resolve_sched(sched, n_chunks);
   rc.P = reinterpret_cast<float*>(ws);
   return run_reduce_call(h, rc, reinterpret_cast<hipStream_t>(stream));
 }
@@ -403,7 +423,7 @@ int tpf_matmul_dx(tpf_handle h, int sem, int p, int64_t M, int64_t K_in, int64_t
   rc.ro.rows_per_slice = rs ? (int)(M / p) : (int)M;
   rc.ro.dtype = out_kind(dx_dtype);
   rc.n_chunks = n_chunks;
-  rc.sched = resolve_sched(sched);
+  rc.sched = resolve_sched(sched, n_chunks);
   rc.P = reinterpret_cast<float*>(ws);
   return run_reduce_call(h, rc, reinterpret_cast<hipStream_t>(stream));
 }
@@ -442,7 +462,7 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
   const int64_t slice_bytes = (int64_t)slice_rows * Ki * 2;
   char* xg = reinterpret_cast<char*>(X_gathered);
   ChunkGeom ch{n_chunks, Mi / n_chunks, Mi};
-  const int s = resolve_sched(sched);
+  const int s = resolve_sched(sched, n_chunks);
   switch (s) {
     case TPF_SCHED_GEMM_ONLY:
       TPF_HIP(launch_gemm_rows(cfg, B_KN, g, 0, Mi, stream_));
@@ -496,6 +516,8 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
       a.ctrl = h->ctrl;
       a.spin_limit = h->spin_limit > 0 ? h->spin_limit : kDefaultSpinLimit;
       a.unreachable = h->unreachable;
+      a.timeline = h->timeline;
+      a.timeline_cap = h->timeline_cap;
       const int bm = cfg_bm(cfg), bn = cfg_bn(cfg);
       const int tiles_n = (Ni + bn - 1) / bn;
       int nseg = 0, t = 0;
@@ -545,6 +567,16 @@ int tpf_sync_status(tpf_handle h, void* stream) {
     TPF_HIP(hipStreamSynchronize(s));
     return fail(TPF_ERR_TIMEOUT, "a bounded wait in the persistent kernel gave up");
   }
+  return TPF_OK;
+}
+
+int tpf_debug_set_timeline(tpf_handle h, void* events, int max_events) {
+  int st = check_handle(h);
+  if (st) return st;
+  if (max_events < 0 || (max_events > 0 && !events)) return fail(TPF_ERR_INVALID_ARG, "bad timeline buffer");
+  if (events && !aligned16(events)) return fail(TPF_ERR_ALIGNMENT, "timeline buffer is not 16-byte aligned");
+  h->timeline = max_events > 0 ? reinterpret_cast<TimelineEvent*>(events) : nullptr;
+  h->timeline_cap = max_events;
   return TPF_OK;
 }
 

@@ -104,8 +104,17 @@ struct Frag {
   f32x16_t acc[Cfg::TM][Cfg::TN];
 };
 
+// A buffer resource lives in scalar registers.  Its base and size are the
+// same for every lane of the workgroup; readfirstlane states that, so the
+// compiler never falls back to per-lane "waterfall" loops around the loads
+// when it cannot prove the uniformity itself (e.g. when the operand was
+// chosen from a ticket read back from LDS).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
 }
 
 // A (and NK-B) rows: 16 consecutive rows read the same logical chunk in one

@@ -58,7 +58,8 @@ struct FusedArgs {
   const float* P;             // partials (reducing ops)
   int64_t p_stride;           // elements between shards' partials (M * N)
   int p;                      // shards summed by the reduction
-  int64_t reduce_elems;      // output elements per reduce task (multiple of 4)
+  int64_t reduce_elems;      // output elements per separate reduce task (multiple of 4)
+  int piggyback;             // 1: each GEMM tile of chunk c > 0 also reduces one slice of chunk c-1
   // AllGather: slice r (slice_bytes) is copied to gathered + r * slice_bytes
   const char* src[kMaxShards];
   char* gathered;
@@ -75,7 +76,24 @@ struct FusedArgs {
   Ctrl* ctrl;
   int64_t spin_limit;
   int unreachable;               // debug: waits target an unreachable count
+  // Optional task timeline: one TimelineEvent per ticket (NULL = off).
+  struct TimelineEvent* timeline;
+  int timeline_cap;
 };
+
+// One persistent-kernel task, stamped with the GPU's constant 100 MHz clock
+// (s_memrealtime), so events of different workgroups share one time base.
+struct TimelineEvent {
+  uint32_t ticket;     // global ticket (queue position)
+  uint16_t kind;       // TK_GEMM / TK_REDUCE / TK_COPY
+  uint16_t chunk;      // chunk (GEMM, reduce) or slice (copy)
+  uint16_t block;      // workgroup id
+  uint16_t xcd;        // XCD the workgroup ran on
+  uint32_t mid;        // GEMM tasks with a reduce slice: clock ticks from t_start to the end of the GEMM part
+  uint64_t t_start;    // after the task was claimed
+  uint64_t t_end;      // after the task's results were published
+};
+static_assert(sizeof(TimelineEvent) == 32, "timeline event layout");
 
 // Tile configurations (chosen from the op's shape only, never from the chunk
 // count, so every chunking runs the same per-element arithmetic).
@@ -95,8 +113,11 @@ enum CfgId : int { CFG_LARGE = 0, CFG_SMALL = 1 };
 #ifndef TPF_LARGE_PPMODE
 #define TPF_LARGE_PPMODE 0
 #endif
-using CfgLarge = TileCfg<256, 256, 2, 4, TPF_LARGE_STAGES, TPF_LARGE_BK, TPF_LARGE_L2PF, TPF_LARGE_PP,
-                         TPF_LARGE_PPMODE>;   // 8 waves
+#ifndef TPF_LARGE_WN
+#define TPF_LARGE_WN 4
+#endif
+using CfgLarge = TileCfg<256, 256, 2, TPF_LARGE_WN, TPF_LARGE_STAGES, TPF_LARGE_BK, TPF_LARGE_L2PF, TPF_LARGE_PP,
+                         TPF_LARGE_PPMODE>;   // 2 x WN waves
 using CfgSmall = TileCfg<32, 128, 1, 4, 4, 64, 0>;    // decode-shaped rows, 4 stages of 20 KiB
 
 int cfg_bm(int cfg);

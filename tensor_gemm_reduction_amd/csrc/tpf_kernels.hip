@@ -165,19 +165,22 @@ __device__ __forceinline__ int claim_tile(Ctrl* ctl, int c, int G, int x) {
   return -1;   // unreachable: G claims are made for G tiles
 }
 
-// Thread 0 polls *ctr with relaxed loads (no cache maintenance per poll)
-// until it reaches target or the bound runs out, then performs one
+// Thread 0 polls *ctr with relaxed loads (no cache maintenance per poll),
+// backing off exponentially so that many waiting workgroups do not hammer one
+// memory channel, until it reaches target or the bound runs out; then one
 // agent-scope acquire.  The caller's following barrier orders the other
 // threads' loads after that acquire.
 __device__ __forceinline__ void wait_at_least(const int* ctr, int target, const FusedArgs& a) {
   if (a.unreachable) target = target + 1 + (1 << 30);
   int64_t polls = 0;
+  int nap = 1;
   while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
     if (++polls > a.spin_limit) {
       __hip_atomic_fetch_or(&a.ctrl->status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
-    __builtin_amdgcn_s_sleep(2);
+    for (int i = 0; i < nap; ++i) __builtin_amdgcn_s_sleep(8);   // ~512 clocks each
+    nap = nap < 8 ? nap * 2 : 8;
   }
   fence_acquire_agent();
 }
@@ -222,9 +225,14 @@ __global__ __launch_bounds__(Cfg::THREADS) void fused_kernel(FusedArgs args) {
       s_ticket = val;
     }
     __syncthreads();
-    const int t = s_ticket;
+    // The ticket is the same for the whole workgroup; saying so keeps every
+    // value derived from it (shard, operand pointers, buffer resources) in
+    // scalar registers instead of per-lane "waterfall" loops.
+    const int t = __builtin_amdgcn_readfirstlane(s_ticket);
     __syncthreads();
     if (t >= total) break;
+    const uint64_t t_start = a.timeline ? __builtin_amdgcn_s_memrealtime() : 0;
+    uint64_t t_mid = 0;
     while (a.seg_start[seg + 1] <= t) ++seg;   // this workgroup's tickets only increase
     const int u = t - a.seg_start[seg];
     const int kind = a.seg_info[seg] & 0xF;
@@ -248,7 +256,23 @@ __global__ __launch_bounds__(Cfg::THREADS) void fused_kernel(FusedArgs args) {
       Frag<Cfg> f;
       gemm_tile<Cfg, BL>(f, j);
       store_any<Cfg>(f, j, a.g, shard);
-      if (!a.gather) publish(&ctl->ready[c]);
+      if (!a.gather) {
+        publish(&ctl->ready[c]);
+        if (a.piggyback && c > 0) {
+          // Slice u of chunk c-1's reduction.  Every tile of chunk c-1 holds a
+          // smaller ticket than this one, so the wait ends; usually at once.
+          t_mid = a.timeline ? __builtin_amdgcn_s_memrealtime() : 0;
+          const int G = a.gemm_tasks[c];
+          const int64_t cb = (int64_t)a.ch.row0(c - 1) * a.g.N, ce = (int64_t)a.ch.row1(c - 1) * a.g.N;
+          const int64_t per = ((ce - cb + G - 1) / G + 3) / 4 * 4;
+          const int64_t e0 = cb + (int64_t)u * per, e1 = min(e0 + per, ce);
+          if (e0 < e1) {
+            if (tid == 0) wait_at_least(&ctl->ready[c - 1], a.gemm_tasks[c - 1], a);
+            __syncthreads();
+            reduce_any(a.P, a.p_stride, a.p, e0, e1, a.g.N, a.ro, tid, Cfg::THREADS);
+          }
+        }
+      }
     } else if (kind == TK_REDUCE) {
       const int c = idx;
       if (tid == 0) wait_at_least(&ctl->ready[c], a.gemm_tasks[c], a);
@@ -262,6 +286,18 @@ __global__ __launch_bounds__(Cfg::THREADS) void fused_kernel(FusedArgs args) {
       const int64_t b1 = min(b0 + a.copy_seg_bytes, a.slice_bytes);
       copy_range(a.src[r], a.gathered + (int64_t)r * a.slice_bytes, b0, b1, tid, Cfg::THREADS);
       publish(&ctl->landed[r]);
+    }
+    if (a.timeline && tid == 0 && t < a.timeline_cap) {
+      TimelineEvent ev;
+      ev.ticket = (uint32_t)t;
+      ev.kind = (uint16_t)kind;
+      ev.chunk = (uint16_t)idx;
+      ev.block = (uint16_t)blockIdx.x;
+      ev.xcd = (uint16_t)xcd;
+      ev.mid = t_mid ? (uint32_t)(t_mid - t_start) : 0u;
+      ev.t_start = t_start;
+      ev.t_end = __builtin_amdgcn_s_memrealtime();
+      a.timeline[t] = ev;
     }
   }
   // The last workgroup out clears the counters for the next call.

@@ -46,6 +46,7 @@ SIGNATURES = {
     "tpf_matmul_dx": (_I, [_VP, _I, _I, _I64, _I64, _I64, _PP, _PP, _PP, _I, _I, _I, _VP, _SZ, _VP]),
     "tpf_sync_status": (_I, [_VP, _VP]),
     "tpf_debug_set_wait": (_I, [_VP, _I64, _I]),
+    "tpf_debug_set_timeline": (_I, [_VP, _VP, _I]),
     "tpf_status_string": (ctypes.c_char_p, [_I]),
     "tpf_last_error": (ctypes.c_char_p, []),
     "tpf_version": (_I, []),
@@ -137,6 +138,24 @@ class Handle:
 
     def debug_set_wait(self, spins: int, unreachable: bool) -> None:
         check(load().tpf_debug_set_wait(self._h, int(spins), 1 if unreachable else 0))
+
+    def set_timeline(self, events: Optional[torch.Tensor]) -> None:
+        """Record persistent-kernel task events into `events` (uint8 device tensor, 32 B per event)."""
+        if events is None:
+            check(load().tpf_debug_set_timeline(self._h, None, 0))
+        else:
+            check(load().tpf_debug_set_timeline(self._h, events.data_ptr(), events.numel() // 32))
+
+
+TIMELINE_DTYPE = [("ticket", "<u4"), ("kind", "<u2"), ("chunk", "<u2"), ("block", "<u2"), ("xcd", "<u2"),
+                  ("mid", "<u4"), ("t_start", "<u8"), ("t_end", "<u8")]
+
+
+def timeline_events(events: torch.Tensor, count: int):
+    """Decode the first `count` timeline records into a numpy structured array."""
+    import numpy as np
+    raw = events[: count * 32].cpu().numpy()
+    return raw.view(np.dtype(TIMELINE_DTYPE))
 
 
 _default_handles = {}
