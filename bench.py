@@ -179,6 +179,11 @@ def main():
         extra["model_pipeline_ms"] = t_c + (n - 1) * max(t_c, t_m) + t_m
         extra["model_serial_ms"] = n * (t_c + t_m)
 
+    # --- HBM bytes per launch from the committed counter summary (if current) ---
+    from tensor_gemm_reduction_amd import profiling
+    rec = profiling.load_traffic(wl.name, os.path.join(ROOT, "profiles"))
+    traffic = round(rec["hbm_bytes"]) if rec and rec.get("sched", args.sched) == args.sched else None
+
     # --- CPU oracle baseline on a bounded sample of rows ---
     cpu = None
     if not args.no_cpu:
@@ -201,7 +206,7 @@ def main():
                    "n_chunks": n, "sched": args.sched, "out": "bf16", "input_sets": args.sets,
                    "workspace_bytes": ws_bytes, "note": wl.note},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": kernel_name(args.sched, n),
                      "avg_kernel_ms": round(avg_kernel_ms, 4)},
         "cpu_baseline": cpu,

@@ -1,0 +1,116 @@
+"""Turn rocprofv3 CSV output into the small summaries kept under profiles/.
+
+  python -m tensor_gemm_reduction_amd.profiling stats  <kernel_stats.csv> <out.txt> <command...>
+      Kernel durations (calls, average, min, max) of the library's kernels.
+
+  python -m tensor_gemm_reduction_amd.profiling traffic <workload> <kernel-substring>
+          <fetch.csv> <write.csv> <copy_fetch.csv> <copy_write.csv> <copy_bytes> <out.json>
+      HBM bytes per dispatch of one kernel from the FETCH_SIZE and WRITE_SIZE
+      counters (KiB per dispatch), each scaled by the ratio between the true
+      bytes of a plain device copy of known size and what the same counter
+      reports for it.  The record carries a hash of the kernel sources; the
+      benchmark only reports it while the sources still match.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+
+
+def source_hash() -> str:
+    """sha256 over the device/host sources of libtpfuse (what the counters describe)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _rows(path_or_dir: str, suffix: str):
+    paths = [path_or_dir] if os.path.isfile(path_or_dir) else \
+        glob.glob(os.path.join(path_or_dir, "**", "*" + suffix), recursive=True)
+    for p in paths:
+        with open(p) as f:
+            yield from csv.DictReader(f)
+
+
+def counter_per_dispatch(path: str, counter: str, kernel_sub: str) -> float:
+    vals = [float(r["Counter_Value"]) for r in _rows(path, "counter_collection.csv")
+            if r.get("Counter_Name") == counter and kernel_sub in r.get("Kernel_Name", "")]
+    if not vals:
+        raise SystemExit(f"no {counter} samples for kernels matching {kernel_sub!r} in {path}")
+    return sum(vals) / len(vals)
+
+
+def stats(csv_path: str, out_path: str, command: str) -> None:
+    lines = [f"# rocprofv3 kernel statistics (durations in microseconds)", f"# command: {command}", ""]
+    lines.append(f"{'kernel':90s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+    for r in _rows(csv_path, "kernel_stats.csv"):
+        name = r["Name"]
+        if "tpf::" not in name and "copyBuffer" not in name:
+            continue
+        lines.append(f"{name[:90]:90s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def traffic(workload, kernel_sub, fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, out_path, command=""):
+    copy_bytes = int(copy_bytes)
+    cf = counter_per_dispatch(cfetch_csv, "FETCH_SIZE", "copyBuffer")
+    cw = counter_per_dispatch(cwrite_csv, "WRITE_SIZE", "copyBuffer")
+    fetch_scale = copy_bytes / (cf * 1024.0)
+    write_scale = copy_bytes / (cw * 1024.0)
+    f = counter_per_dispatch(fetch_csv, "FETCH_SIZE", kernel_sub)
+    w = counter_per_dispatch(write_csv, "WRITE_SIZE", kernel_sub)
+    rec = {
+        "workload": workload,
+        "kernel": kernel_sub,
+        "source_hash": source_hash(),
+        "fetch_kib_per_dispatch": f,
+        "write_kib_per_dispatch": w,
+        "copy_bytes": copy_bytes,
+        "copy_fetch_kib": cf,
+        "copy_write_kib": cw,
+        "fetch_scale": fetch_scale,
+        "write_scale": write_scale,
+        "hbm_read_bytes": f * 1024.0 * fetch_scale,
+        "hbm_write_bytes": w * 1024.0 * write_scale,
+        "hbm_bytes": f * 1024.0 * fetch_scale + w * 1024.0 * write_scale,
+        "command": command,
+    }
+    with open(out_path, "w") as fo:
+        json.dump(rec, fo, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def load_traffic(workload: str, profiles_dir: str):
+    """HBM bytes per dispatch recorded for `workload`, or None if absent or stale."""
+    path = os.path.join(profiles_dir, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec
+
+
+if __name__ == "__main__":
+    cmd = sys.argv[1]
+    if cmd == "stats":
+        stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+    elif cmd == "traffic":
+        traffic(*sys.argv[2:10], command=" ".join(sys.argv[10:]))
+    else:
+        raise SystemExit(__doc__)
