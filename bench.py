@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated to defeat the 256 MB last-level cache")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--modes", default="gemm_only,reduce_only,unfused,two_stream,persistent,auto")
+    ap.add_argument("--modes", default="gemm_only,reduce_only,unfused,two_stream,persistent,tile,auto")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
     return ap.parse_args()

@@ -83,6 +83,14 @@ extern "C" {
                                     AllGather->MatMul: only the GEMM over an already gathered X) */
 #define TPF_SCHED_REDUCE_ONLY 5  /* measurement: only the reduction of partials already in the workspace
                                     (for AllGather->MatMul: only the gather copy) */
+#define TPF_SCHED_TILE 6         /* readiness per output tile: one persistent kernel runs the shard GEMM
+                                    tiles of the whole output in an L2-friendly order, and the workgroup
+                                    that finishes the last shard of an output tile sums that tile at once
+                                    (the M027 page's per-chunk readiness at the finest chunking, every
+                                    output tile its own chunk; n_chunks is checked but does not change
+                                    the schedule).  At most 131072 output tiles (TPF_ERR_UNSUPPORTED
+                                    beyond).  For AllGather->MatMul, which has no reduction, it runs as
+                                    TPF_SCHED_PERSISTENT. */
 
 /* Output semantics of the column-parallel backward. */
 #define TPF_ALLREDUCE 0          /* one full [M, K_in] result */

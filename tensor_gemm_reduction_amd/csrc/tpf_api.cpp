@@ -29,6 +29,7 @@ struct tpf_context {
   hipEvent_t ev_chunk[kMaxChunks] = {};
   hipEvent_t ev_slice[kMaxShards] = {};
   Ctrl* ctrl = nullptr;
+  int* tile_cnt = nullptr;             // kTileCounters per-output-tile counters (tile scheduler)
   int64_t spin_limit = 0;
   int unreachable = 0;
   TimelineEvent* timeline = nullptr;   // caller-owned device buffer (debug)
@@ -60,7 +61,7 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool valid_sched(int s) { return s >= TPF_SCHED_AUTO && s <= TPF_SCHED_REDUCE_ONLY; }
+bool valid_sched(int s) { return s >= TPF_SCHED_AUTO && s <= TPF_SCHED_TILE; }
 bool valid_dtype(int d) { return d == TPF_BF16 || d == TPF_F32; }
 
 int out_kind(int dtype) { return dtype == TPF_F32 ? OUT_F32 : OUT_BF16; }
@@ -193,6 +194,27 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
       TPF_HIP(hipStreamWaitEvent(stream, h->ev_join, 0));
       return TPF_OK;
     }
+    case TPF_SCHED_TILE: {
+      TileArgs a{};
+      a.g = g;
+      a.ro = rc.ro;
+      a.P = rc.P;
+      a.p_stride = stride;
+      a.p = rc.p;
+      a.row0 = 0;
+      a.row1 = rc.M;
+      a.tiles_m = (rc.M + cfg_bm(cfg) - 1) / cfg_bm(cfg);
+      a.tiles_n = (rc.N + cfg_bn(cfg) - 1) / cfg_bn(cfg);
+      if ((int64_t)a.tiles_m * a.tiles_n > kTileCounters)
+        return fail(TPF_ERR_UNSUPPORTED, "the tile scheduler handles at most " + std::to_string(kTileCounters) +
+                                             " output tiles");
+      a.tasks = rc.p * a.tiles_m * a.tiles_n;
+      a.cnt = h->tile_cnt;
+      a.timeline = h->timeline;
+      a.timeline_cap = h->timeline_cap;
+      TPF_HIP(launch_tiles(cfg, rc.bl, 1, a, stream));
+      return TPF_OK;
+    }
     case TPF_SCHED_PERSISTENT: {
       FusedArgs a{};
       a.g = g;
@@ -298,7 +320,10 @@ int tpf_create(tpf_handle* out, int device) {
   if (e != hipSuccess) return cleanup(hip_fail(e, "hipEventCreateWithFlags"));
   e = hipMalloc(reinterpret_cast<void**>(&h->ctrl), sizeof(Ctrl));
   if (e != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(control block)"));
+  e = hipMalloc(reinterpret_cast<void**>(&h->tile_cnt), sizeof(int) * kTileCounters);
+  if (e != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(tile counters)"));
   e = hipMemset(h->ctrl, 0, sizeof(Ctrl));
+  if (e == hipSuccess) e = hipMemset(h->tile_cnt, 0, sizeof(int) * kTileCounters);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) return cleanup(hip_fail(e, "hipMemset(control block)"));
   *out = h;
@@ -309,10 +334,9 @@ int tpf_destroy(tpf_handle h) {
   if (!h) return TPF_OK;
   (void)hipSetDevice(h->device);
   if (h->side) (void)hipStreamSynchronize(h->side);
-  if (h->ctrl) {
-    (void)hipDeviceSynchronize();
-    (void)hipFree(h->ctrl);
-  }
+  if (h->ctrl || h->tile_cnt) (void)hipDeviceSynchronize();
+  if (h->ctrl) (void)hipFree(h->ctrl);
+  if (h->tile_cnt) (void)hipFree(h->tile_cnt);
   for (auto& ev : h->ev_chunk)
     if (ev) (void)hipEventDestroy(ev);
   for (auto& ev : h->ev_slice)
@@ -462,7 +486,8 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
   const int64_t slice_bytes = (int64_t)slice_rows * Ki * 2;
   char* xg = reinterpret_cast<char*>(X_gathered);
   ChunkGeom ch{n_chunks, Mi / n_chunks, Mi};
-  const int s = resolve_sched(sched, n_chunks);
+  int s = resolve_sched(sched, n_chunks);
+  if (s == TPF_SCHED_TILE) s = TPF_SCHED_PERSISTENT;   // no reduction to fold into the tiles
   switch (s) {
     case TPF_SCHED_GEMM_ONLY:
       TPF_HIP(launch_gemm_rows(cfg, B_KN, g, 0, Mi, stream_));

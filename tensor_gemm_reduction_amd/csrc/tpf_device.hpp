@@ -112,6 +112,54 @@ __device__ __forceinline__ void reduce_range(const float* __restrict__ P, int64_
   }
 }
 
+// The same fixed-order sum over one rectangular output tile: rows
+// [m0, m0 + rows) and columns [n0, n0 + ncols) (ncols a multiple of 4) of the
+// [M][N] result, with `nthr` threads numbered `t`.  Per element it performs
+// exactly the additions of reduce_range, so both give identical bits.
+template <int PP, int OUT>
+__device__ __forceinline__ void reduce_tile(const float* __restrict__ P, int64_t shard_stride, int p, int m0,
+                                            int rows, int n0, int ncols, int N, const ReduceOut& o, int t, int nthr) {
+  constexpr int U = PP >= 8 ? 2 : (PP >= 4 ? 4 : (PP >= 2 ? 8 : 4));
+  const int np = PP > 0 ? PP : p;
+  const int gpr = ncols / 4;               // 4-element groups per tile row
+  const int total = rows * gpr;
+  for (int g = t; g < total; g += nthr * U) {
+    f32x4_t s[U];
+    int64_t e[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = g + u * nthr;
+      const int r = i / gpr;
+      e[u] = (int64_t)(m0 + r) * N + n0 + 4 * (i - r * gpr);
+      if (i < total) s[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(P + e[u]));
+    }
+    if constexpr (PP > 0) {
+      f32x4_t v[PP > 1 ? PP - 1 : 1][U];
+#pragma unroll
+      for (int k = 1; k < PP; ++k)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (g + u * nthr < total)
+            v[k - 1][u] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4_t*>(P + (int64_t)k * shard_stride + e[u]));
+#pragma unroll
+      for (int k = 1; k < PP; ++k)
+#pragma unroll
+        for (int u = 0; u < U; ++u) s[u] = s[u] + v[k - 1][u];
+    } else {
+      for (int k = 1; k < np; ++k)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (g + u * nthr < total)
+            s[u] = s[u] + __builtin_nontemporal_load(
+                              reinterpret_cast<const f32x4_t*>(P + (int64_t)k * shard_stride + e[u]));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (g + u * nthr < total) reduce_store4<OUT>(o, e[u], N, s[u]);
+  }
+}
+
 // Copy bytes [b0, b1) (multiples of 16) from src to dst with nthr threads.
 __device__ __forceinline__ void copy_range(const char* __restrict__ src, char* __restrict__ dst,
                                            int64_t b0, int64_t b1, int64_t t, int64_t nthr) {

@@ -158,8 +158,6 @@ struct TileLoader {
   __amdgpu_buffer_rsrc_t ra, rb;
   uint32_t a_off[Cfg::A_PER_WAVE];   // byte offsets at k0 = 0 (kOOB when out of range)
   uint32_t b_off[Cfg::B_PER_WAVE];
-  int a_kc[Cfg::A_PER_WAVE];         // logical k chunk of this lane's A (and NK B) loads
-  int b_kc[Cfg::B_PER_WAVE];         // NK: logical k chunk; KN: k row within the step
   int K;
   uint32_t ldb_bytes;
   uint32_t lda_bytes;
@@ -179,7 +177,6 @@ struct TileLoader {
       const int row = (wave * Cfg::A_PER_WAVE + i) * (1024 / Cfg::RB) + lane / Cfg::KCH;
       const int kc = (lane % Cfg::KCH) ^ swz_row<Cfg>(row);
       const int gm = j.m0 + row;
-      a_kc[i] = kc;
       a_off[i] = gm < j.a_rows ? (uint32_t)(((int64_t)gm * j.lda + kc * 8) * 2) : kOOB;
     }
     if constexpr (BL == B_NK) {
@@ -188,7 +185,6 @@ struct TileLoader {
         const int row = (wave * Cfg::B_PER_WAVE + i) * (1024 / Cfg::RB) + lane / Cfg::KCH;
         const int kc = (lane % Cfg::KCH) ^ swz_row<Cfg>(row);
         const int gn = j.n0 + row;
-        b_kc[i] = kc;
         b_off[i] = gn < j.b_rows ? (uint32_t)(((int64_t)gn * j.ldb + kc * 8) * 2) : kOOB;
       }
     } else {
@@ -201,7 +197,6 @@ struct TileLoader {
         const int cblk = (pchunk >> 1) ^ (Cfg::SWB * (k & 3));
         const int c = cblk * 2 + (pchunk & 1);           // logical 16-byte chunk: n = 8c
         const int gn = j.n0 + c * 8;
-        b_kc[i] = k;
         b_off[i] = gn < j.N ? (uint32_t)(((int64_t)k * j.ldb + gn) * 2) : kOOB;
       }
     }
@@ -263,23 +258,45 @@ struct TileLoader {
     else return w >> 1;                             // group 0 = even waves
   }
 
+  // Logical k chunk (A, NK B) of this lane's i-th A or B load, or (KN B) its
+  // k row within the step.  Only the K tail step needs them, so they are
+  // recomputed there instead of being kept in registers.
+  __device__ __forceinline__ static int a_kchunk(int wave, int lane, int i) {
+    const int row = (wave * Cfg::A_PER_WAVE + i) * (1024 / Cfg::RB) + lane / Cfg::KCH;
+    return (lane % Cfg::KCH) ^ swz_row<Cfg>(row);
+  }
+  __device__ __forceinline__ static int b_kpos(int wave, int lane, int i) {
+    if constexpr (BL == B_NK) {
+      const int row = (wave * Cfg::B_PER_WAVE + i) * (1024 / Cfg::RB) + lane / Cfg::KCH;
+      return ((lane % Cfg::KCH) ^ swz_row<Cfg>(row)) * 8;
+    } else {
+      return ((wave * Cfg::B_PER_WAVE + i) * 1024 + lane * 16) / (Cfg::BN * 2);
+    }
+  }
+
   __device__ __forceinline__ void issue(char* stage, int k0) const {
-    const int wave = loader_wave();
+    const int wave = loader_wave(), lane = threadIdx.x & 63;
     char* la = stage;
     char* lb = stage + Cfg::LDS_A;
+    const bool tail = k0 + Cfg::BK > K;   // the same for the whole workgroup
+    // In the tail step the lane index is passed through an empty asm
+    // statement, which the compiler cannot move: the tail-only index
+    // arithmetic then stays inside the branch instead of being hoisted out of
+    // the K loop into registers that every step would keep live.
+    int tl = lane;
+    if (tail) asm volatile("" : "+v"(tl));
 #pragma unroll
     for (int i = 0; i < Cfg::A_PER_WAVE; ++i) {
-      const uint32_t off = (a_off[i] != kOOB && k0 + a_kc[i] * 8 < K) ? a_off[i] + (uint32_t)k0 * 2 : kOOB;
+      uint32_t off = a_off[i] != kOOB ? a_off[i] + (uint32_t)k0 * 2 : kOOB;
+      if (tail && k0 + a_kchunk(wave, tl, i) * 8 >= K) off = kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(la + (wave * Cfg::A_PER_WAVE + i) * 1024), 16,
                                                off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < Cfg::B_PER_WAVE; ++i) {
-      uint32_t off;
-      if constexpr (BL == B_NK)
-        off = (b_off[i] != kOOB && k0 + b_kc[i] * 8 < K) ? b_off[i] + (uint32_t)k0 * 2 : kOOB;
-      else  // KN: the tile's row k is operand row k0 + k
-        off = (b_off[i] != kOOB && k0 + b_kc[i] < K) ? b_off[i] + (uint32_t)k0 * ldb_bytes : kOOB;
+      // NK: k runs along the row; KN: the tile's row k is operand row k0 + k
+      uint32_t off = b_off[i] != kOOB ? b_off[i] + (uint32_t)k0 * (BL == B_NK ? 2u : ldb_bytes) : kOOB;
+      if (tail && k0 + b_kpos(wave, tl, i) >= K) off = kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(lb + (wave * Cfg::B_PER_WAVE + i) * 1024), 16,
                                                off, 0, 0, 0);
     }

@@ -27,6 +27,10 @@ struct Ctrl {
   int sub[kMaxChunks][kXcds]; // claimed tiles of each XCD's share of a chunk
 };
 
+// Per-output-tile counters of the tile scheduler (shards finished).  A handle
+// owns this many; every count is back at zero when a call ends.
+constexpr int kTileCounters = 1 << 17;
+
 enum TaskKind : int { TK_GEMM = 0, TK_REDUCE = 1, TK_COPY = 2 };
 
 // The shard GEMMs of one call.  Tile (shard k, rows, cols) reads A[k] and
@@ -81,6 +85,25 @@ struct FusedArgs {
   int timeline_cap;
 };
 
+// The nshard * tiles_m * tiles_n GEMM tiles of a row range, one workgroup
+// each.  Plain shard GEMMs use only g, the rows and the tile grid.  The tile
+// scheduler adds the reduction: each output tile has its own counter, and
+// the workgroup that completes the last shard of an output tile sums that
+// tile.  Nothing waits.
+struct TileArgs {
+  GemmOperands g;
+  int row0, row1;             // output rows covered (the tile grid starts at row0)
+  ReduceOut ro;
+  const float* P;             // fp32 partials, shard k at P + k * p_stride
+  int64_t p_stride;
+  int p;
+  int tiles_m, tiles_n;       // output tile grid
+  int tasks;                  // p * tiles_m * tiles_n
+  int* cnt;                   // kTileCounters per-output-tile counters
+  struct TimelineEvent* timeline;
+  int timeline_cap;
+};
+
 // One persistent-kernel task, stamped with the GPU's constant 100 MHz clock
 // (s_memrealtime), so events of different workgroups share one time base.
 struct TimelineEvent {
@@ -123,11 +146,15 @@ using CfgSmall = TileCfg<32, 128, 1, 4, 4, 64, 0>;    // decode-shaped rows, 4 s
 int cfg_bm(int cfg);
 int cfg_bn(int cfg);
 
+// Shard GEMM tiles of rows [row0, row1) into g.dst (no reduction).
 hipError_t launch_gemm_rows(int cfg, int bl, const GemmOperands& g, int row0, int row1, hipStream_t s);
 hipError_t launch_reduce_rows(const float* P, int64_t stride, int p, int row0, int row1, int N,
                               const ReduceOut& o, int num_cus, hipStream_t s);
 hipError_t launch_fused(int cfg, int bl, const FusedArgs& a, int grid, hipStream_t s);
 int fused_occupancy(int cfg, int bl);   // resident fused workgroups per CU
+// One workgroup per tile; red = 1 for the tile scheduler (fp32 partials,
+// per-output-tile counters, last arriver sums).
+hipError_t launch_tiles(int cfg, int bl, int red, const TileArgs& a, hipStream_t s);
 hipError_t launch_copy(const char* src, char* dst, int64_t bytes, int num_cus, hipStream_t s);
 hipError_t launch_clear_status(Ctrl* c, hipStream_t s);
 

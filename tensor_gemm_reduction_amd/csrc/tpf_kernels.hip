@@ -1,8 +1,10 @@
 // Kernels of the fused tensor-parallel Linear and their launchers.
 //
-//  gemm_rows_kernel  one workgroup per (shard, row tile, column tile) of a row
-//                    range: the shard GEMMs of one chunk (two-stream
-//                    scheduler) or of all rows (unfused baseline).
+//  tile_kernel       one workgroup per shard GEMM tile of a row range: the
+//                    shard GEMMs of one chunk (two-stream scheduler) or of all
+//                    rows (unfused baseline); with RED = 1 also the tile
+//                    scheduler, whose last workgroup to finish an output tile
+//                    sums it over the shards.
 //  reduce_rows_kernel the fixed-order sum over shards of a row range, written
 //                    in AllReduce or ReduceScatter layout.
 //  fused_kernel      the persistent scheduler: every workgroup pulls tickets
@@ -19,6 +21,8 @@
 // already running, so every awaited task is owned by a running workgroup
 // that does not itself wait on anything later.  This holds however many
 // workgroups are resident.
+#include <algorithm>
+
 #include "tpf_internal.hpp"
 
 namespace tpf {
@@ -64,11 +68,6 @@ __device__ __forceinline__ TileJob make_job(const GemmOperands& g, int shard, in
   return j;
 }
 
-struct GemmRowsArgs {
-  GemmOperands g;
-  int row0, row1;
-};
-
 // Tile u of a row range (shard-major) -> (shard, tm, tn).  Within a shard the
 // tiles go in groups of kGroupM tile-rows, column by column, so that tiles
 // running at the same time share A and B panels.
@@ -84,30 +83,6 @@ __device__ __forceinline__ void tile_coords(int u, int tiles_m, int tiles_n, int
   const int w = t - first * tiles_n;
   tm = first + w % gsize;
   tn = w / gsize;
-}
-
-// Block b runs on XCD b % 8 (round-robin dispatch).  Give each XCD a
-// contiguous run of tiles so its L2 sees neighbouring tiles.
-__device__ __forceinline__ int xcd_tile(int b, int total) {
-  const int x = b & 7, i = b >> 3;
-  const int q = total >> 3, r = total & 7;
-  return x * q + min(x, r) + i;
-}
-
-template <class Cfg, int BL>
-__global__ __launch_bounds__(Cfg::THREADS) void gemm_rows_kernel(GemmRowsArgs args) {
-  (void)args;
-  const GemmRowsArgs& ka = kernarg<GemmRowsArgs>();
-  const GemmOperands& g = ka.g;
-  const int row0 = ka.row0, row1 = ka.row1;
-  const int tiles_n = (g.N + Cfg::BN - 1) / Cfg::BN;
-  const int tiles_m = (row1 - row0 + Cfg::BM - 1) / Cfg::BM;
-  int shard, tm, tn;
-  tile_coords(xcd_tile(blockIdx.x, (int)gridDim.x), tiles_m, tiles_n, shard, tm, tn);
-  const TileJob j = make_job<Cfg>(g, shard, row0, row1, tm, tn);
-  Frag<Cfg> f;
-  gemm_tile<Cfg, BL>(f, j);
-  store_any<Cfg>(f, j, g, shard);
 }
 
 template <int OUT>
@@ -315,28 +290,101 @@ __global__ __launch_bounds__(Cfg::THREADS) void fused_kernel(FusedArgs args) {
   }
 }
 
+// Block b of a grid of `total` blocks -> task index.  Blocks are dealt to the
+// XCDs round-robin (block b runs on XCD b % 8), so the tasks are split into
+// kXcds contiguous shares and block b takes task b / 8 of share b % 8: each
+// XCD's L2 then sees a contiguous run of tiles.
+__device__ __forceinline__ int xcd_task(int b, int total) {
+  const int x = b & (kXcds - 1), i = b / kXcds;
+  return x * (total / kXcds) + min(x, total % kXcds) + i;
+}
+
+// Sum output tile (m0, rows, n0, ncols) over the p shards' partials.
+__device__ __forceinline__ void reduce_tile_any(const TileArgs& a, int m0, int rows, int n0, int ncols, int tid,
+                                                int nthr) {
+  const int N = a.g.N;
+  if (a.ro.dtype == OUT_F32) {
+    switch (a.p) {
+      case 2: reduce_tile<2, OUT_F32>(a.P, a.p_stride, 2, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+      case 4: reduce_tile<4, OUT_F32>(a.P, a.p_stride, 4, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+      case 8: reduce_tile<8, OUT_F32>(a.P, a.p_stride, 8, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+      default: reduce_tile<0, OUT_F32>(a.P, a.p_stride, a.p, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+    }
+  } else {
+    switch (a.p) {
+      case 2: reduce_tile<2, OUT_BF16>(a.P, a.p_stride, 2, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+      case 4: reduce_tile<4, OUT_BF16>(a.P, a.p_stride, 4, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+      case 8: reduce_tile<8, OUT_BF16>(a.P, a.p_stride, 8, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+      default: reduce_tile<0, OUT_BF16>(a.P, a.p_stride, a.p, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+    }
+  }
+}
+
+// One workgroup per GEMM tile, used both for plain shard GEMMs (RED = 0) and
+// for the tile scheduler (RED = 1).  The nshard * tiles_m * tiles_n tiles of
+// rows [row0, row1) are taken in the order of tile_coords (shard-major,
+// grouped tile rows) through xcd_task, so each XCD works through the operand
+// panels of one shard, and the XCDs of different shards advance through the
+// same output tiles at the same time.
+//
+// RED = 1: after storing its fp32 partial, a workgroup bumps the output
+// tile's counter (release); the one that brings it to p acquires and sums
+// the tile in shard order.  No workgroup ever waits for another.
+template <class Cfg, int BL, int RED>
+__global__ __launch_bounds__(Cfg::THREADS) void tile_kernel(TileArgs args) {
+  (void)args;
+  const TileArgs& a = kernarg<TileArgs>();
+  const int tid = threadIdx.x;
+  const int u = xcd_task(blockIdx.x, a.tasks);
+  int shard, tm, tn;
+  tile_coords(u, a.tiles_m, a.tiles_n, shard, tm, tn);
+  const TileJob j = make_job<Cfg>(a.g, shard, a.row0, a.row1, tm, tn);
+  Frag<Cfg> f;
+  if constexpr (RED == 0) {
+    gemm_tile<Cfg, BL>(f, j);
+    store_any<Cfg>(f, j, a.g, shard);
+  } else {
+    int& s_word = *reinterpret_cast<int*>(stage_ptr<Cfg, 0>());   // idle once gemm_tile returns
+    const uint64_t t_start = a.timeline ? __builtin_amdgcn_s_memrealtime() : 0;
+    uint64_t t_mid = 0;
+    gemm_tile<Cfg, BL>(f, j);
+    store_tile<Cfg, OUT_F32>(f, j, reinterpret_cast<float*>(a.g.dst) + (int64_t)shard * a.g.dst_shard_stride,
+                             a.g.ldd);
+    const int T = tm * a.tiles_n + tn;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (tid == 0) {
+      const int prev = atomic_add_release(&a.cnt[T], 1);
+      const int last = prev == a.p - 1;
+      if (last) {
+        fence_acquire_agent();
+        atomic_store_relaxed(&a.cnt[T], 0);   // every shard of tile T is counted: ready for the next call
+      }
+      s_word = last;
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(s_word)) {
+      t_mid = a.timeline ? __builtin_amdgcn_s_memrealtime() : 0;
+      reduce_tile_any(a, j.m0, j.rows, j.n0, min(Cfg::BN, j.N - j.n0), tid, Cfg::THREADS);
+    }
+    if (a.timeline && tid == 0 && u < a.timeline_cap) {
+      TimelineEvent ev;
+      ev.ticket = (uint32_t)u;
+      ev.kind = (uint16_t)TK_GEMM;
+      ev.chunk = (uint16_t)T;
+      ev.block = (uint16_t)blockIdx.x;
+      ev.xcd = (uint16_t)xcd_id();
+      ev.mid = t_mid ? (uint32_t)(t_mid - t_start) : 0u;
+      ev.t_start = t_start;
+      ev.t_end = __builtin_amdgcn_s_memrealtime();
+      a.timeline[u] = ev;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-
-template <class Cfg>
-static hipError_t launch_gemm_cfg(int bl, const GemmOperands& g, int row0, int row1, hipStream_t s) {
-  const int tiles_n = (g.N + Cfg::BN - 1) / Cfg::BN;
-  const int tiles_m = (row1 - row0 + Cfg::BM - 1) / Cfg::BM;
-  const int grid = g.nshard * tiles_m * tiles_n;
-  if (grid <= 0) return hipSuccess;
-  GemmRowsArgs args{g, row0, row1};
-  if (bl == B_KN)
-    hipLaunchKernelGGL((gemm_rows_kernel<Cfg, B_KN>), dim3(grid), dim3(Cfg::THREADS), 0, s, args);
-  else
-    hipLaunchKernelGGL((gemm_rows_kernel<Cfg, B_NK>), dim3(grid), dim3(Cfg::THREADS), 0, s, args);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_rows(int cfg, int bl, const GemmOperands& g, int row0, int row1, hipStream_t s) {
-  if (cfg == CFG_SMALL) return launch_gemm_cfg<CfgSmall>(bl, g, row0, row1, s);
-  return launch_gemm_cfg<CfgLarge>(bl, g, row0, row1, s);
-}
 
 hipError_t launch_reduce_rows(const float* P, int64_t stride, int p, int row0, int row1, int N,
                               const ReduceOut& o, int num_cus, hipStream_t s) {
@@ -391,6 +439,38 @@ hipError_t launch_fused(int cfg, int bl, const FusedArgs& a, int grid, hipStream
       hipLaunchKernelGGL((fused_kernel<CfgLarge, B_NK>), dim3(grid), dim3(CfgLarge::THREADS), 0, s, a);
   }
   return hipGetLastError();
+}
+
+template <class Cfg, int RED>
+static void launch_tile_cfg(int bl, const TileArgs& a, int grid, hipStream_t s) {
+  if (bl == B_KN)
+    hipLaunchKernelGGL((tile_kernel<Cfg, B_KN, RED>), dim3(grid), dim3(Cfg::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((tile_kernel<Cfg, B_NK, RED>), dim3(grid), dim3(Cfg::THREADS), 0, s, a);
+}
+
+hipError_t launch_tiles(int cfg, int bl, int red, const TileArgs& a, hipStream_t s) {
+  if (a.tasks <= 0) return hipSuccess;
+  const int grid = a.tasks;
+  if (cfg == CFG_SMALL) {
+    if (red) launch_tile_cfg<CfgSmall, 1>(bl, a, grid, s);
+    else launch_tile_cfg<CfgSmall, 0>(bl, a, grid, s);
+  } else {
+    if (red) launch_tile_cfg<CfgLarge, 1>(bl, a, grid, s);
+    else launch_tile_cfg<CfgLarge, 0>(bl, a, grid, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_rows(int cfg, int bl, const GemmOperands& g, int row0, int row1, hipStream_t s) {
+  TileArgs a{};
+  a.g = g;
+  a.row0 = row0;
+  a.row1 = row1;
+  a.tiles_m = (row1 - row0 + cfg_bm(cfg) - 1) / cfg_bm(cfg);
+  a.tiles_n = (g.N + cfg_bn(cfg) - 1) / cfg_bn(cfg);
+  a.tasks = g.nshard * a.tiles_m * a.tiles_n;
+  return launch_tiles(cfg, bl, 0, a, s);
 }
 
 hipError_t launch_clear_status(Ctrl* c, hipStream_t s) {

@@ -41,6 +41,7 @@ def test_constants_match_header():
     assert int(defs["TPF_ERR_HIP"]) == tp.ERR_HIP
     assert int(defs["TPF_F32"]) == tp.F32 and int(defs["TPF_BF16"]) == tp.BF16
     assert int(defs["TPF_SCHED_REDUCE_ONLY"]) == tp.SCHED_REDUCE_ONLY
+    assert int(defs["TPF_SCHED_TILE"]) == tp.SCHED_TILE
     assert int(defs["TPF_REDUCESCATTER"]) == tp.REDUCESCATTER
     assert int(defs["TPF_OP_MATMUL_DX"]) == tp.OP_MATMUL_DX
     assert int(defs["TPF_MAX_SHARDS"]) == tp.MAX_SHARDS and int(defs["TPF_MAX_CHUNKS"]) == tp.MAX_CHUNKS

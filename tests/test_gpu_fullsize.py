@@ -71,7 +71,7 @@ def test_fullsize_parity(name):
     assert_bf16_is_rne_of_f32(y16, y32, what)
     # every other chunk count and scheduler gives the same bits
     for m in wl.chunks:
-        for sched in ("persistent", "two_stream", "unfused"):
+        for sched in ("persistent", "two_stream", "unfused", "tile"):
             if m == n and sched == "persistent" and n == 1:
                 continue
             y = run(wl, inp, torch.bfloat16, m, sched)
@@ -110,6 +110,37 @@ def test_fullsize_allgather_copy_exact():
     xg, _ = tp.allgather_matmul(inp.X, inp.W[0], torch.bfloat16, n_chunks=wl.default_chunks)
     torch.cuda.synchronize()
     assert torch.equal(xg, torch.cat(inp.X, 0))
+
+
+def test_tile_timeline_reduces_each_tile_once_and_overlaps():
+    """Tile scheduler: every output tile is summed exactly once, by the
+    workgroup that finished its last shard, and those sums run while GEMM
+    tiles of other output tiles are still being computed."""
+    wl = inputs.WORKLOADS["mlp_down"]
+    say("mlp_down: tile-scheduler timeline")
+    inp = inputs.make_inputs(wl, seed=0, device="cuda")
+    h = tp.Handle(0)
+    tiles = (wl.M // 256) * (wl.N // 256)
+    ev = torch.zeros(32 * wl.p * tiles, dtype=torch.uint8, device="cuda")
+    h.set_timeline(ev)
+    y = tp.matmul_allreduce(inp.X, inp.W, n_chunks=wl.default_chunks, sched="tile", handle=h)
+    torch.cuda.synchronize()
+    h.set_timeline(None)
+    assert h.sync_status() == tp.OK
+    e = tp.timeline_events(ev, wl.p * tiles)
+    assert (e["t_end"] > 0).all()
+    red = e[e["mid"] > 0]
+    assert sorted(red["chunk"].tolist()) == list(range(tiles))    # each output tile summed once
+    r0 = red["t_start"] + red["mid"]
+    r1 = red["t_end"]
+    g_end = np.where(e["mid"] > 0, e["t_start"] + e["mid"], e["t_end"])
+    hit = (r0[:, None] < g_end[None, :]) & (e["t_start"][None, :] < r1[:, None])
+    overlapped = hit.any(axis=1).mean()
+    assert overlapped > 0.5, f"only {overlapped:.2f} of the tile sums overlap a GEMM tile"
+    ref = tp.matmul_allreduce(inp.X, inp.W, n_chunks=1, sched="unfused")
+    torch.cuda.synchronize()
+    assert_bitwise(y, ref, "tile vs unfused")
+    h.close()
 
 
 def test_timeline_shows_chunk_overlap():

@@ -16,7 +16,7 @@ from tests.parity import (assert_bf16, assert_bf16_is_rne_of_f32, assert_bitwise
 
 pytestmark = pytest.mark.gpu
 
-SCHEDS = ["persistent", "two_stream", "unfused"]
+SCHEDS = ["persistent", "two_stream", "unfused", "tile"]
 DEV = "cuda"
 
 
@@ -135,6 +135,26 @@ def test_repeated_persistent_calls_are_deterministic():
         again = tp.matmul_allreduce(X, W, torch.float32, n_chunks=4, sched="persistent")
         torch.cuda.synchronize()
         assert_bitwise(again, first, "repeat")
+    assert tp.default_handle().sync_status() == tp.OK
+
+
+def test_tile_counters_reset_between_calls():
+    """The tile scheduler's per-output-tile counters and queue shares return to
+    zero at the end of every call: calls of different tile grids in a row
+    (more tiles, then fewer, then more again) all give the unfused bits."""
+    cases = [(4, 600, 1032, 136), (2, 40, 264, 72), (3, 300, 520, 200), (8, 16, 1024, 256)]
+    data = []
+    for i, (p, M, N, K) in enumerate(cases):
+        X = gpu(shards([(M, K)] * p, ("normal", 1.0), 51 + i))
+        W = gpu(shards([(K, N)] * p, ("normal", 0.05), 61 + i))
+        ref = tp.matmul_allreduce(X, W, torch.float32, n_chunks=1, sched="unfused")
+        data.append((X, W, ref, (p, M, N, K)))
+    for _ in range(3):
+        for X, W, ref, shape in data:
+            say(f"tile scheduler p,M,N,K={shape}")
+            y = tp.matmul_allreduce(X, W, torch.float32, n_chunks=1, sched="tile")
+            torch.cuda.synchronize()
+            assert_bitwise(y, ref, f"tile {shape}")
     assert tp.default_handle().sync_status() == tp.OK
 
 
