@@ -7,13 +7,16 @@ HBM-resident inputs.  Default workload: the Llama-style MLP down projection
 (row-parallel, p=4 shards X_k [4096,4096] . W_k [4096,4096], 8 M-chunks,
 AllReduce layout, bf16 out).
 
-Prints ONE JSON line.  `value` is fused TFLOP/s (algorithmic 2*M*N*K_total);
-`roofline` prices the dominant kernel (the persistent fused kernel) against
-the bf16 dense MFMA peak with its average duration measured by HIP events on
-the stream it is launched on; `modes` gives the GEMM-only, reduce-only,
-unfused, two-stream and persistent times and the exposed reduction time
-(fused minus GEMM-only); `cpu_baseline` times the CPU oracle on a bounded
-sample of rows of the same workload.
+Prints ONE JSON line.  `value` is whole-step TFLOP/s of the library call
+(algorithmic 2*M*N*K_total over the wall time per step; the default
+scheduler is AUTO, which on one GPU runs the shard-GEMM kernel followed by
+the reduction kernel); `roofline` prices the step's dominant kernel against
+the bf16 dense MFMA peak, its average duration measured by HIP events that
+the library records around that launch on the stream it is launched on;
+`modes` gives the GEMM-only, reduce-only, unfused, two-stream, persistent
+and tile-scheduler times and the exposed reduction time (step minus
+GEMM-only); `cpu_baseline` times the CPU oracle on a bounded sample of rows
+of the same workload.
 """
 from __future__ import annotations
 
@@ -37,7 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mlp_down")
     ap.add_argument("--chunks", type=int, default=0, help="0 = the workload's default")
-    ap.add_argument("--sched", default="auto", help="auto: persistent kernel for >= 2 chunks, else unfused")
+    ap.add_argument("--sched", default="auto",
+                    help="auto (= unfused on one GPU), unfused, persistent, two_stream, tile, gemm_only")
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated to defeat the 256 MB last-level cache")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -87,6 +91,7 @@ def main():
         sets.append(inp)
     M, N, K, p = wl.M, wl.N, wl.K, wl.p
     flops = wl.flops()
+    kbytes = kernel_bytes(wl)
 
     if wl.op in ("allreduce", "reducescatter"):
         op_id = tp.OP_MATMUL_ALLREDUCE if wl.op == "allreduce" else tp.OP_MATMUL_REDUCESCATTER
@@ -142,6 +147,7 @@ def main():
     for i in range(args.warmup):
         call(i, args.sched)
     torch.cuda.synchronize()
+    handle.set_kernel_timing(True)   # events around each step's dominant kernel launch
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -153,11 +159,20 @@ def main():
     st = handle.sync_status()
     if st != tp.OK:
         raise RuntimeError(f"fused path reported status {st}")
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    launch_ms = handle.kernel_times(args.steps)
+    handle.set_kernel_timing(False)
+    step_ms = [a.elapsed_time(b) for a, b in evs]
     ms_per_step = 1e3 * wall / args.steps
+    kern_ms = launch_ms if launch_ms else step_ms    # two_stream records no single dominant launch
     avg_kernel_ms = sum(kern_ms) / len(kern_ms)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (avg_kernel_ms * 1e-3) / 1e12
+    # The dominant kernel is priced against MFMA or HBM, whichever bounds it:
+    # its algorithmic flops per byte against the ridge point peak_flops / peak_bw.
+    hbm_bound = flops / kbytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if hbm_bound:
+        achieved, peak, unit = kbytes / (avg_kernel_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = flops / (avg_kernel_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
 
     # --- the other modes (measurement context) ---
     modes = {}
@@ -182,7 +197,7 @@ def main():
     # --- HBM bytes per launch from the committed counter summary (if current) ---
     from tensor_gemm_reduction_amd import profiling
     rec = profiling.load_traffic(wl.name, os.path.join(ROOT, "profiles"))
-    traffic = round(rec["hbm_bytes"]) if rec and rec.get("sched", args.sched) == args.sched else None
+    traffic = round(rec["hbm_bytes"]) if rec and rec.get("sched") == args.sched else None
 
     # --- CPU oracle baseline on a bounded sample of rows ---
     cpu = None
@@ -205,10 +220,13 @@ def main():
         "config": {"workload": wl.name, "op": wl.op, "p": p, "M": M, "N": N, "K_shard": K,
                    "n_chunks": n, "sched": args.sched, "out": "bf16", "input_sets": args.sets,
                    "workspace_bytes": ws_bytes, "note": wl.note},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": kernel_name(args.sched, n),
-                     "avg_kernel_ms": round(avg_kernel_ms, 4)},
+        "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "algorithmic_bytes": kbytes, "algorithmic_flops": flops,
+                     "kernel": kernel_name(args.sched),
+                     "avg_kernel_ms": round(avg_kernel_ms, 4),
+                     "timed_launches": len(kern_ms),
+                     "avg_step_event_ms": round(sum(step_ms) / len(step_ms), 4)},
         "cpu_baseline": cpu,
         "modes": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in modes.items()},
         **{k: round(v, 4) for k, v in extra.items()},
@@ -216,11 +234,27 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def kernel_name(sched, n):
+def kernel_bytes(wl):
+    """Algorithmic HBM bytes of one launch of the shard-GEMM kernel: every
+    operand read once and every output written once (the fp32 partials of
+    the reducing ops, the bf16 output and gathered input of AllGather)."""
+    p, M, N, K = wl.p, wl.M, wl.N, wl.K
+    if wl.op == "allgather":
+        return 2.0 * M * K + 2.0 * K * N + 2.0 * M * N
+    if wl.op == "dx":      # dY_k [M, N], W_k [K, N], partials [M, K]
+        return p * (2.0 * M * N + 2.0 * K * N + 4.0 * M * K)
+    return p * (2.0 * M * K + 2.0 * K * N + 4.0 * M * N)
+
+
+def kernel_name(sched):
     """The kernel that dominates one step of `sched` (what `roofline` prices)."""
-    if sched == "persistent" or (sched == "auto" and n >= 2):
+    if sched == "persistent":
         return "fused_kernel (persistent: shard GEMM tiles + chunk reductions)"
-    return "gemm_rows_kernel (shard GEMM tiles)"
+    if sched == "tile":
+        return "tile_kernel RED=1 (shard GEMM tiles + last-arriver tile sums)"
+    if sched == "two_stream":
+        return "whole step (per-chunk GEMM and reduction kernels on three streams)"
+    return "tile_kernel RED=0 (shard GEMM tiles)"
 
 
 def cpu_baseline(wl, inp, seconds):

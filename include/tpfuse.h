@@ -36,7 +36,7 @@
  *    or each other.
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default
  *    stream) after any work already on it; the call returns without waiting.
- *    Internal forks onto the handle's side stream join back into `stream`
+ *    Internal forks onto the handle's side streams join back into `stream`
  *    before the call returns, so callers see single-stream semantics.
  *  - A handle runs at most one call at a time; use one handle per concurrent
  *    stream.
@@ -75,9 +75,13 @@ extern "C" {
 #define TPF_F32 1
 
 /* Schedulers.  Every scheduler computes the same bits. */
-#define TPF_SCHED_AUTO 0         /* library's choice: PERSISTENT for n_chunks >= 2, else UNFUSED */
+#define TPF_SCHED_AUTO 0         /* library's choice.  With every shard on one GPU the reduction shares HBM
+                                    and L2 with the GEMM, and overlapping it costs more than it hides, so
+                                    AUTO runs UNFUSED; the chunked schedulers are chosen explicitly. */
 #define TPF_SCHED_PERSISTENT 1   /* one persistent kernel: work queue + per-chunk ready counters */
-#define TPF_SCHED_TWO_STREAM 2   /* per-chunk GEMM launches, reductions on a side stream after per-chunk events */
+#define TPF_SCHED_TWO_STREAM 2   /* per-chunk GEMM launches (alternating between the caller's stream and a
+                                    second handle stream), reductions on a side stream after per-chunk
+                                    events */
 #define TPF_SCHED_UNFUSED 3      /* whole GEMM, then the whole reduction (the serial baseline) */
 #define TPF_SCHED_GEMM_ONLY 4    /* measurement: only the shard GEMMs (partials into the workspace; for
                                     AllGather->MatMul: only the GEMM over an already gathered X) */
@@ -104,14 +108,15 @@ extern "C" {
 
 typedef struct tpf_context* tpf_handle;
 
-/* Create a handle bound to HIP device `device`.  The handle owns a side
- * stream (default priority), a pool of events and a small device control
- * block (counters, status word); these are allocated here and released by
- * tpf_destroy.  Returns TPF_ERR_HIP if the device cannot be used. */
+/* Create a handle bound to HIP device `device`.  The handle owns two side
+ * streams (default priority), a pool of events, a small device control block
+ * (counters, status word) and 512 KiB of per-output-tile counters; these are
+ * allocated here and released by tpf_destroy.  Returns TPF_ERR_HIP if the
+ * device cannot be used. */
 int tpf_create(tpf_handle* h, int device);
 
 /* Release a handle after all work enqueued with it has finished (the call
- * synchronises the handle's side stream).  NULL is accepted. */
+ * synchronises the handle's side streams).  NULL is accepted. */
 int tpf_destroy(tpf_handle h);
 
 /* Bytes of workspace a call needs (0 if none), a pure function of its
@@ -188,6 +193,21 @@ int tpf_debug_set_wait(tpf_handle h, int64_t spins, int unreachable);
  * max_events tickets; pass NULL / 0 to stop.  The buffer must stay valid
  * while such calls run. */
 int tpf_debug_set_timeline(tpf_handle h, void* events, int max_events);
+
+/* Debug: time each call's dominant kernel launch.  With enable != 0, every
+ * later call on this handle records a pair of timing events around that
+ * launch, on the stream it is launched on: the shard-GEMM kernel for
+ * TPF_SCHED_UNFUSED and TPF_SCHED_GEMM_ONLY (and AUTO, which runs UNFUSED),
+ * the reduction kernel for TPF_SCHED_REDUCE_ONLY, the single kernel of
+ * TPF_SCHED_PERSISTENT and TPF_SCHED_TILE; TPF_SCHED_TWO_STREAM calls record
+ * nothing.  The last 256 records are kept.  Enabling creates the handle's
+ * events on first use; both enabling and disabling clear the records. */
+int tpf_debug_set_kernel_timing(tpf_handle h, int enable);
+
+/* Debug: wait for the recorded launches and write up to `max` of their
+ * durations in milliseconds into `ms` (host array), oldest first.  Returns
+ * the number written (>= 0) or a negative status; clears the records. */
+int tpf_debug_kernel_times(tpf_handle h, float* ms, int max);
 
 /* Static text for a status code. */
 const char* tpf_status_string(int code);

@@ -21,11 +21,14 @@ using namespace tpf;
 static_assert(TPF_MAX_SHARDS == kMaxShards, "shard limit mismatch");
 static_assert(TPF_MAX_CHUNKS == kMaxChunks, "chunk limit mismatch");
 
+constexpr int kKernelTimes = 256;   // debug kernel-timing records held per handle
+
 struct tpf_context {
   int device = 0;
   int num_cus = 0;
-  hipStream_t side = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  hipStream_t side = nullptr;           // reductions (reducing ops) or gather copies (AllGather)
+  hipStream_t gemm2 = nullptr;          // every other chunk's GEMM (two-stream scheduler)
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_join2 = nullptr;
   hipEvent_t ev_chunk[kMaxChunks] = {};
   hipEvent_t ev_slice[kMaxShards] = {};
   Ctrl* ctrl = nullptr;
@@ -34,6 +37,12 @@ struct tpf_context {
   int unreachable = 0;
   TimelineEvent* timeline = nullptr;   // caller-owned device buffer (debug)
   int timeline_cap = 0;
+  // Debug kernel timing: a ring of timing-event pairs around each call's
+  // dominant launch.
+  bool ktime = false;
+  hipEvent_t kt0[kKernelTimes] = {}, kt1[kKernelTimes] = {};
+  int kt_next = 0;      // ring slot of the next record
+  int kt_count = 0;     // records held (<= kKernelTimes)
 };
 
 namespace {
@@ -121,14 +130,20 @@ int check_handle(tpf_handle h) {
   return TPF_OK;
 }
 
-// AUTO: with one chunk there is no later GEMM for the reduction to overlap,
-// and a kernel boundary is the cheapest device-wide barrier, so the GEMM
-// kernel is followed by the reduction kernel; with two or more chunks the
-// persistent kernel overlaps each chunk's reduction with the next chunk's
-// GEMM.
+// AUTO.  The M027 page makes fusion conditional: measure the whole GEMM and
+// the whole collective separately first (§04), and expect chunking to slow
+// the GEMM and decode shapes to lack chunkable work (§03, §05).  Here every
+// shard lives on one GPU, so the "messages" travel through the same HBM and
+// L2 as the GEMM's operands: overlapping the reduction costs per-chunk
+// cross-XCD release/acquire, smaller GEMM launches or weights re-read once
+// per chunk, and on MI355X each of those costs more than the reduction it
+// hides (5-10 % of the GEMM at these shapes).  AUTO therefore runs the GEMM
+// kernel followed by the reduction kernel, a kernel boundary being the
+// cheapest device-wide barrier; the chunked schedulers are selected
+// explicitly.
 int resolve_sched(int sched, int n_chunks) {
-  if (sched != TPF_SCHED_AUTO) return sched;
-  return n_chunks >= 2 ? TPF_SCHED_PERSISTENT : TPF_SCHED_UNFUSED;
+  (void)n_chunks;
+  return sched == TPF_SCHED_AUTO ? TPF_SCHED_UNFUSED : sched;
 }
 
 // A reducing op (row-parallel AR/RS, or dX with either semantic).
@@ -146,6 +161,29 @@ int set_device(tpf_handle h) {
   TPF_HIP(hipSetDevice(h->device));
   return TPF_OK;
 }
+
+// Debug kernel timing: record the start / stop event of the current call's
+// dominant launch on the stream it is launched on.
+int ktime_start(tpf_handle h, hipStream_t s) {
+  if (h->ktime) TPF_HIP(hipEventRecord(h->kt0[h->kt_next], s));
+  return TPF_OK;
+}
+int ktime_stop(tpf_handle h, hipStream_t s) {
+  if (!h->ktime) return TPF_OK;
+  TPF_HIP(hipEventRecord(h->kt1[h->kt_next], s));
+  h->kt_next = (h->kt_next + 1) % kKernelTimes;
+  h->kt_count = std::min(h->kt_count + 1, kKernelTimes);
+  return TPF_OK;
+}
+
+#define TPF_TIMED(h, s, launch)      \
+  do {                               \
+    int st_ = ktime_start((h), (s)); \
+    if (st_) return st_;             \
+    TPF_HIP(launch);                 \
+    st_ = ktime_stop((h), (s));      \
+    if (st_) return st_;             \
+  } while (0)
 
 int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
   int st = set_device(h);
@@ -172,26 +210,35 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
 
   switch (rc.sched) {
     case TPF_SCHED_GEMM_ONLY:
-      TPF_HIP(launch_gemm_rows(cfg, rc.bl, g, 0, rc.M, stream));
+      TPF_TIMED(h, stream, launch_gemm_rows(cfg, rc.bl, g, 0, rc.M, stream));
       return TPF_OK;
     case TPF_SCHED_REDUCE_ONLY:
-      TPF_HIP(launch_reduce_rows(rc.P, stride, rc.p, 0, rc.M, rc.N, rc.ro, h->num_cus, stream));
+      TPF_TIMED(h, stream, launch_reduce_rows(rc.P, stride, rc.p, 0, rc.M, rc.N, rc.ro, h->num_cus, stream));
       return TPF_OK;
     case TPF_SCHED_UNFUSED:
-      TPF_HIP(launch_gemm_rows(cfg, rc.bl, g, 0, rc.M, stream));
+      TPF_TIMED(h, stream, launch_gemm_rows(cfg, rc.bl, g, 0, rc.M, stream));
       TPF_HIP(launch_reduce_rows(rc.P, stride, rc.p, 0, rc.M, rc.N, rc.ro, h->num_cus, stream));
       return TPF_OK;
     case TPF_SCHED_TWO_STREAM: {
+      // Chunk c's GEMM goes to the caller's stream (even c) or the handle's
+      // second GEMM stream (odd c), so the next chunk's tiles fill CUs while
+      // the current chunk's last tiles finish; chunk c's reduction runs on
+      // the side stream after chunk c's event, concurrently with the GEMMs of
+      // later chunks.
       TPF_HIP(hipEventRecord(h->ev_fork, stream));
       TPF_HIP(hipStreamWaitEvent(h->side, h->ev_fork, 0));
+      TPF_HIP(hipStreamWaitEvent(h->gemm2, h->ev_fork, 0));
       for (int c = 0; c < ch.n; ++c) {
-        TPF_HIP(launch_gemm_rows(cfg, rc.bl, g, ch.row0(c), ch.row1(c), stream));
-        TPF_HIP(hipEventRecord(h->ev_chunk[c], stream));
+        hipStream_t gs = (c & 1) ? h->gemm2 : stream;
+        TPF_HIP(launch_gemm_rows(cfg, rc.bl, g, ch.row0(c), ch.row1(c), gs));
+        TPF_HIP(hipEventRecord(h->ev_chunk[c], gs));
         TPF_HIP(hipStreamWaitEvent(h->side, h->ev_chunk[c], 0));
         TPF_HIP(launch_reduce_rows(rc.P, stride, rc.p, ch.row0(c), ch.row1(c), rc.N, rc.ro, h->num_cus, h->side));
       }
       TPF_HIP(hipEventRecord(h->ev_join, h->side));
+      TPF_HIP(hipEventRecord(h->ev_join2, h->gemm2));
       TPF_HIP(hipStreamWaitEvent(stream, h->ev_join, 0));
+      TPF_HIP(hipStreamWaitEvent(stream, h->ev_join2, 0));
       return TPF_OK;
     }
     case TPF_SCHED_TILE: {
@@ -212,7 +259,7 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
       a.cnt = h->tile_cnt;
       a.timeline = h->timeline;
       a.timeline_cap = h->timeline_cap;
-      TPF_HIP(launch_tiles(cfg, rc.bl, 1, a, stream));
+      TPF_TIMED(h, stream, launch_tiles(cfg, rc.bl, 1, a, stream));
       return TPF_OK;
     }
     case TPF_SCHED_PERSISTENT: {
@@ -263,7 +310,7 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
       a.nseg = nseg;
       a.seg_start[nseg] = t;
       const int grid = std::min(t, h->num_cus * fused_occupancy(cfg, rc.bl));
-      TPF_HIP(launch_fused(cfg, rc.bl, a, grid, stream));
+      TPF_TIMED(h, stream, launch_fused(cfg, rc.bl, a, grid, stream));
       return TPF_OK;
     }
   }
@@ -312,9 +359,11 @@ int tpf_create(tpf_handle* out, int device) {
   if (e != hipSuccess) return cleanup(hip_fail(e, "hipGetDeviceProperties"));
   h->num_cus = prop.multiProcessorCount;
   e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->gemm2, hipStreamNonBlocking);
   if (e != hipSuccess) return cleanup(hip_fail(e, "hipStreamCreateWithFlags"));
   e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_join2, hipEventDisableTiming);
   for (int c = 0; c < kMaxChunks && e == hipSuccess; ++c) e = hipEventCreateWithFlags(&h->ev_chunk[c], hipEventDisableTiming);
   for (int s = 0; s < kMaxShards && e == hipSuccess; ++s) e = hipEventCreateWithFlags(&h->ev_slice[s], hipEventDisableTiming);
   if (e != hipSuccess) return cleanup(hip_fail(e, "hipEventCreateWithFlags"));
@@ -334,6 +383,7 @@ int tpf_destroy(tpf_handle h) {
   if (!h) return TPF_OK;
   (void)hipSetDevice(h->device);
   if (h->side) (void)hipStreamSynchronize(h->side);
+  if (h->gemm2) (void)hipStreamSynchronize(h->gemm2);
   if (h->ctrl || h->tile_cnt) (void)hipDeviceSynchronize();
   if (h->ctrl) (void)hipFree(h->ctrl);
   if (h->tile_cnt) (void)hipFree(h->tile_cnt);
@@ -341,9 +391,15 @@ int tpf_destroy(tpf_handle h) {
     if (ev) (void)hipEventDestroy(ev);
   for (auto& ev : h->ev_slice)
     if (ev) (void)hipEventDestroy(ev);
+  for (int i = 0; i < kKernelTimes; ++i) {
+    if (h->kt0[i]) (void)hipEventDestroy(h->kt0[i]);
+    if (h->kt1[i]) (void)hipEventDestroy(h->kt1[i]);
+  }
   if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
   if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+  if (h->ev_join2) (void)hipEventDestroy(h->ev_join2);
   if (h->side) (void)hipStreamDestroy(h->side);
+  if (h->gemm2) (void)hipStreamDestroy(h->gemm2);
   delete h;
   return TPF_OK;
 }
@@ -490,7 +546,7 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
   if (s == TPF_SCHED_TILE) s = TPF_SCHED_PERSISTENT;   // no reduction to fold into the tiles
   switch (s) {
     case TPF_SCHED_GEMM_ONLY:
-      TPF_HIP(launch_gemm_rows(cfg, B_KN, g, 0, Mi, stream_));
+      TPF_TIMED(h, stream_, launch_gemm_rows(cfg, B_KN, g, 0, Mi, stream_));
       return TPF_OK;
     case TPF_SCHED_REDUCE_ONLY:
       for (int r = 0; r < p; ++r)
@@ -501,27 +557,29 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
       for (int r = 0; r < p; ++r)
         TPF_HIP(launch_copy(reinterpret_cast<const char*>(X_slices[r]), xg + r * slice_bytes, slice_bytes, h->num_cus,
                             stream_));
-      TPF_HIP(launch_gemm_rows(cfg, B_KN, g, 0, Mi, stream_));
+      TPF_TIMED(h, stream_, launch_gemm_rows(cfg, B_KN, g, 0, Mi, stream_));
       return TPF_OK;
     case TPF_SCHED_TWO_STREAM: {
       // Slices are copied on the side stream in rank order; chunk c's GEMM
-      // waits for the last slice under its rows.
+      // waits for the last slice under its rows, alternating between the
+      // caller's stream and the handle's second GEMM stream as above.
       TPF_HIP(hipEventRecord(h->ev_fork, stream_));
       TPF_HIP(hipStreamWaitEvent(h->side, h->ev_fork, 0));
+      TPF_HIP(hipStreamWaitEvent(h->gemm2, h->ev_fork, 0));
       for (int r = 0; r < p; ++r) {
         TPF_HIP(launch_copy(reinterpret_cast<const char*>(X_slices[r]), xg + r * slice_bytes, slice_bytes, h->num_cus,
                             h->side));
         TPF_HIP(hipEventRecord(h->ev_slice[r], h->side));
       }
-      int waited = -1;
       for (int c = 0; c < ch.n; ++c) {
-        const int last = (ch.row1(c) - 1) / slice_rows;
-        if (last > waited) {
-          TPF_HIP(hipStreamWaitEvent(stream_, h->ev_slice[last], 0));
-          waited = last;
-        }
-        TPF_HIP(launch_gemm_rows(cfg, B_KN, g, ch.row0(c), ch.row1(c), stream_));
+        hipStream_t gs = (c & 1) ? h->gemm2 : stream_;
+        TPF_HIP(hipStreamWaitEvent(gs, h->ev_slice[(ch.row1(c) - 1) / slice_rows], 0));
+        TPF_HIP(launch_gemm_rows(cfg, B_KN, g, ch.row0(c), ch.row1(c), gs));
       }
+      TPF_HIP(hipEventRecord(h->ev_join, h->side));
+      TPF_HIP(hipEventRecord(h->ev_join2, h->gemm2));
+      TPF_HIP(hipStreamWaitEvent(stream_, h->ev_join, 0));
+      TPF_HIP(hipStreamWaitEvent(stream_, h->ev_join2, 0));
       return TPF_OK;
     }
     case TPF_SCHED_PERSISTENT: {
@@ -572,7 +630,7 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
       a.nseg = nseg;
       a.seg_start[nseg] = t;
       const int grid = std::min(t, h->num_cus * fused_occupancy(cfg, B_KN));
-      TPF_HIP(launch_fused(cfg, B_KN, a, grid, stream_));
+      TPF_TIMED(h, stream_, launch_fused(cfg, B_KN, a, grid, stream_));
       return TPF_OK;
     }
   }
@@ -603,6 +661,39 @@ int tpf_debug_set_timeline(tpf_handle h, void* events, int max_events) {
   h->timeline = max_events > 0 ? reinterpret_cast<TimelineEvent*>(events) : nullptr;
   h->timeline_cap = max_events;
   return TPF_OK;
+}
+
+int tpf_debug_set_kernel_timing(tpf_handle h, int enable) {
+  int st = check_handle(h);
+  if (st) return st;
+  if ((st = set_device(h))) return st;
+  if (enable && !h->kt0[0]) {
+    for (int i = 0; i < kKernelTimes; ++i) {
+      TPF_HIP(hipEventCreate(&h->kt0[i]));
+      TPF_HIP(hipEventCreate(&h->kt1[i]));
+    }
+  }
+  h->ktime = enable != 0;
+  h->kt_next = 0;
+  h->kt_count = 0;
+  return TPF_OK;
+}
+
+int tpf_debug_kernel_times(tpf_handle h, float* ms, int max) {
+  int st = check_handle(h);
+  if (st) return st;
+  if (max < 0 || (max > 0 && !ms)) return fail(TPF_ERR_INVALID_ARG, "bad output array");
+  if ((st = set_device(h))) return st;
+  const int n = std::min(max, h->kt_count);
+  const int first = (h->kt_next - h->kt_count + kKernelTimes) % kKernelTimes;
+  for (int i = 0; i < n; ++i) {
+    const int j = (first + i) % kKernelTimes;
+    TPF_HIP(hipEventSynchronize(h->kt1[j]));
+    TPF_HIP(hipEventElapsedTime(&ms[i], h->kt0[j], h->kt1[j]));
+  }
+  h->kt_next = 0;
+  h->kt_count = 0;
+  return n;
 }
 
 int tpf_debug_set_wait(tpf_handle h, int64_t spins, int unreachable) {

@@ -139,8 +139,17 @@ enum CfgId : int { CFG_LARGE = 0, CFG_SMALL = 1 };
 #ifndef TPF_LARGE_WN
 #define TPF_LARGE_WN 4
 #endif
-using CfgLarge = TileCfg<256, 256, 2, TPF_LARGE_WN, TPF_LARGE_STAGES, TPF_LARGE_BK, TPF_LARGE_L2PF, TPF_LARGE_PP,
-                         TPF_LARGE_PPMODE>;   // 2 x WN waves
+#ifndef TPF_LARGE_WM
+#define TPF_LARGE_WM 2
+#endif
+#ifndef TPF_LARGE_BM
+#define TPF_LARGE_BM 256
+#endif
+#ifndef TPF_LARGE_BN
+#define TPF_LARGE_BN 256
+#endif
+using CfgLarge = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN, TPF_LARGE_STAGES, TPF_LARGE_BK,
+                         TPF_LARGE_L2PF, TPF_LARGE_PP, TPF_LARGE_PPMODE>;
 using CfgSmall = TileCfg<32, 128, 1, 4, 4, 64, 0>;    // decode-shaped rows, 4 stages of 20 KiB
 
 int cfg_bm(int cfg);

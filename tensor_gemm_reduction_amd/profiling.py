@@ -1,9 +1,10 @@
 """Turn rocprofv3 CSV output into the small summaries kept under profiles/.
 
-  python -m tensor_gemm_reduction_amd.profiling stats  <kernel_stats.csv> <out.txt> <command...>
-      Kernel durations (calls, average, min, max) of the library's kernels.
+  python -m tensor_gemm_reduction_amd.profiling stats  <kernel_stats.csv> <out.txt> <bench.json|-> <command...>
+      Kernel durations (calls, average, min, max) of the library's kernels,
+      next to the HIP-event average the same bench run printed.
 
-  python -m tensor_gemm_reduction_amd.profiling traffic <workload> <kernel-substring>
+  python -m tensor_gemm_reduction_amd.profiling traffic <workload> <sched> <kernel-substring>
           <fetch.csv> <write.csv> <copy_fetch.csv> <copy_write.csv> <copy_bytes> <out.json>
       HBM bytes per dispatch of one kernel from the FETCH_SIZE and WRITE_SIZE
       counters (KiB per dispatch), each scaled by the ratio between the true
@@ -51,7 +52,7 @@ def counter_per_dispatch(path: str, counter: str, kernel_sub: str) -> float:
     return sum(vals) / len(vals)
 
 
-def stats(csv_path: str, out_path: str, command: str) -> None:
+def stats(csv_path: str, out_path: str, command: str, bench_json: str = "") -> None:
     lines = [f"# rocprofv3 kernel statistics (durations in microseconds)", f"# command: {command}", ""]
     lines.append(f"{'kernel':90s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
     for r in _rows(csv_path, "kernel_stats.csv"):
@@ -60,12 +61,23 @@ def stats(csv_path: str, out_path: str, command: str) -> None:
             continue
         lines.append(f"{name[:90]:90s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:10.2f} "
                      f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
+    if bench_json and os.path.exists(bench_json):
+        # The same command's own JSON line: its HIP-event average of the
+        # dominant kernel must agree with the rocprofv3 average above.
+        with open(bench_json) as f:
+            rec = json.loads(f.read().strip().splitlines()[-1])
+        r = rec["roofline"]
+        lines += ["", f"# bench.py (same run): dominant kernel = {r['kernel']}",
+                  f"#   HIP-event average over {r.get('timed_launches')} timed launches: "
+                  f"{1e3 * r['avg_kernel_ms']:.2f} us; roofline {r['achieved']} {r['unit']} of {r['peak']} "
+                  f"(frac {r['frac']}); value {rec['value']} {rec['unit']}"]
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def traffic(workload, kernel_sub, fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, out_path, command=""):
+def traffic(workload, sched, kernel_sub, fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, out_path,
+            command=""):
     copy_bytes = int(copy_bytes)
     cf = counter_per_dispatch(cfetch_csv, "FETCH_SIZE", "copyBuffer")
     cw = counter_per_dispatch(cwrite_csv, "WRITE_SIZE", "copyBuffer")
@@ -75,6 +87,7 @@ def traffic(workload, kernel_sub, fetch_csv, write_csv, cfetch_csv, cwrite_csv, 
     w = counter_per_dispatch(write_csv, "WRITE_SIZE", kernel_sub)
     rec = {
         "workload": workload,
+        "sched": sched,
         "kernel": kernel_sub,
         "source_hash": source_hash(),
         "fetch_kib_per_dispatch": f,
@@ -109,8 +122,9 @@ def load_traffic(workload: str, profiles_dir: str):
 if __name__ == "__main__":
     cmd = sys.argv[1]
     if cmd == "stats":
-        stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+        # stats <csv> <out.txt> <bench_json or -> <command...>
+        stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[5:]), "" if sys.argv[4] == "-" else sys.argv[4])
     elif cmd == "traffic":
-        traffic(*sys.argv[2:10], command=" ".join(sys.argv[10:]))
+        traffic(*sys.argv[2:11], command=" ".join(sys.argv[11:]))
     else:
         raise SystemExit(__doc__)

@@ -48,6 +48,8 @@ SIGNATURES = {
     "tpf_sync_status": (_I, [_VP, _VP]),
     "tpf_debug_set_wait": (_I, [_VP, _I64, _I]),
     "tpf_debug_set_timeline": (_I, [_VP, _VP, _I]),
+    "tpf_debug_set_kernel_timing": (_I, [_VP, _I]),
+    "tpf_debug_kernel_times": (_I, [_VP, ctypes.POINTER(ctypes.c_float), _I]),
     "tpf_status_string": (ctypes.c_char_p, [_I]),
     "tpf_last_error": (ctypes.c_char_p, []),
     "tpf_version": (_I, []),
@@ -146,6 +148,18 @@ class Handle:
             check(load().tpf_debug_set_timeline(self._h, None, 0))
         else:
             check(load().tpf_debug_set_timeline(self._h, events.data_ptr(), events.numel() // 32))
+
+    def set_kernel_timing(self, enable: bool) -> None:
+        """Record timing events around each later call's dominant kernel launch."""
+        check(load().tpf_debug_set_kernel_timing(self._h, 1 if enable else 0))
+
+    def kernel_times(self, max_records: int = 256) -> List[float]:
+        """Durations (ms) of the recorded launches, oldest first; clears the record."""
+        buf = (ctypes.c_float * max_records)()
+        n = load().tpf_debug_kernel_times(self._h, buf, max_records)
+        if n < 0:
+            check(n)
+        return [float(buf[i]) for i in range(n)]
 
 
 TIMELINE_DTYPE = [("ticket", "<u4"), ("kind", "<u2"), ("chunk", "<u2"), ("block", "<u2"), ("xcd", "<u2"),

@@ -164,5 +164,7 @@ def test_handle_calls_reject_null():
     lib = tp.load()
     assert lib.tpf_sync_status(None, None) == tp.ERR_INVALID_ARG
     assert lib.tpf_debug_set_wait(None, 10, 1) == tp.ERR_INVALID_ARG
+    assert lib.tpf_debug_set_kernel_timing(None, 1) == tp.ERR_INVALID_ARG
+    assert lib.tpf_debug_kernel_times(None, None, 0) == tp.ERR_INVALID_ARG
     assert lib.tpf_create(None, 0) == tp.ERR_INVALID_ARG
     assert lib.tpf_destroy(None) == tp.OK

@@ -158,6 +158,24 @@ def test_tile_counters_reset_between_calls():
     assert tp.default_handle().sync_status() == tp.OK
 
 
+def test_kernel_timing_records_one_launch_per_call():
+    p, M, N, K = 2, 520, 264, 136
+    say("debug kernel timing")
+    X = gpu(shards([(M, K)] * p, ("normal", 1.0), 71))
+    W = gpu(shards([(K, N)] * p, ("normal", 0.05), 72))
+    h = tp.Handle(0)
+    h.set_kernel_timing(True)
+    for sched in ("auto", "unfused", "gemm_only", "persistent", "tile", "two_stream"):
+        tp.matmul_allreduce(X, W, n_chunks=4, sched=sched, handle=h)
+    t = h.kernel_times()
+    assert len(t) == 5 and all(0.0 < v < 1000.0 for v in t), t    # two_stream records nothing
+    assert h.kernel_times() == []                                    # cleared
+    h.set_kernel_timing(False)
+    tp.matmul_allreduce(X, W, sched="unfused", handle=h)
+    assert h.kernel_times() == []
+    h.close()
+
+
 # ---------------------------------------------------------------------------
 # MatMul -> ReduceScatter
 # ---------------------------------------------------------------------------
