@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--chunks", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--sched", default="auto",
                     help="auto (= unfused on one GPU), unfused, persistent, two_stream, tile, gemm_only")
+    ap.add_argument("--message", default="fp32", choices=["fp32", "bf16"],
+                    help="precision of the shard partials (the 2-byte message variant: bf16)")
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated to defeat the 256 MB last-level cache")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -91,11 +93,12 @@ def main():
         sets.append(inp)
     M, N, K, p = wl.M, wl.N, wl.K, wl.p
     flops = wl.flops()
-    kbytes = kernel_bytes(wl)
+    kbytes = kernel_bytes(wl, 2 if args.message == "bf16" else 4)
+    msg = args.message
 
     if wl.op in ("allreduce", "reducescatter"):
         op_id = tp.OP_MATMUL_ALLREDUCE if wl.op == "allreduce" else tp.OP_MATMUL_REDUCESCATTER
-        ws = torch.empty(tp.workspace_size(op_id, p, M, N, K, n), dtype=torch.uint8, device=dev)
+        ws = torch.empty(tp.workspace_size(op_id, p, M, N, K, n, message=msg), dtype=torch.uint8, device=dev)
         if wl.op == "allreduce":
             Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         else:
@@ -104,17 +107,20 @@ def main():
         def call(i, sched):
             inp = sets[i % len(sets)]
             if wl.op == "allreduce":
-                tp.matmul_allreduce(inp.X, inp.W, n_chunks=n, sched=sched, Y=Y, ws=ws, handle=handle)
+                tp.matmul_allreduce(inp.X, inp.W, n_chunks=n, sched=sched, Y=Y, ws=ws, handle=handle, message=msg)
             else:
-                tp.matmul_reducescatter(inp.X, inp.W, n_chunks=n, sched=sched, Y=Y, ws=ws, handle=handle)
+                tp.matmul_reducescatter(inp.X, inp.W, n_chunks=n, sched=sched, Y=Y, ws=ws, handle=handle,
+                                        message=msg)
         ws_bytes = ws.numel()
     elif wl.op == "dx":
-        ws = torch.empty(tp.workspace_size(tp.OP_MATMUL_DX, p, M, K, N, n), dtype=torch.uint8, device=dev)
+        ws = torch.empty(tp.workspace_size(tp.OP_MATMUL_DX, p, M, K, N, n, message=msg), dtype=torch.uint8,
+                         device=dev)
         dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
 
         def call(i, sched):
             inp = sets[i % len(sets)]
-            tp.matmul_dx(inp.X, inp.W, tp.ALLREDUCE, n_chunks=n, sched=sched, dX=dX, ws=ws, handle=handle)
+            tp.matmul_dx(inp.X, inp.W, tp.ALLREDUCE, n_chunks=n, sched=sched, dX=dX, ws=ws, handle=handle,
+                         message=msg)
         ws_bytes = ws.numel()
     else:  # allgather
         XG = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
@@ -218,7 +224,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "op": wl.op, "p": p, "M": M, "N": N, "K_shard": K,
-                   "n_chunks": n, "sched": args.sched, "out": "bf16", "input_sets": args.sets,
+                   "n_chunks": n, "sched": args.sched, "out": "bf16", "message": args.message,
+                   "input_sets": args.sets,
                    "workspace_bytes": ws_bytes, "note": wl.note},
         "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -234,16 +241,16 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def kernel_bytes(wl):
+def kernel_bytes(wl, part_bytes=4):
     """Algorithmic HBM bytes of one launch of the shard-GEMM kernel: every
-    operand read once and every output written once (the fp32 partials of
-    the reducing ops, the bf16 output and gathered input of AllGather)."""
+    operand read once and every output written once (the partials of the
+    reducing ops, `part_bytes` per element; the bf16 output of AllGather)."""
     p, M, N, K = wl.p, wl.M, wl.N, wl.K
     if wl.op == "allgather":
         return 2.0 * M * K + 2.0 * K * N + 2.0 * M * N
     if wl.op == "dx":      # dY_k [M, N], W_k [K, N], partials [M, K]
-        return p * (2.0 * M * N + 2.0 * K * N + 4.0 * M * K)
-    return p * (2.0 * M * K + 2.0 * K * N + 4.0 * M * N)
+        return p * (2.0 * M * N + 2.0 * K * N + part_bytes * M * K)
+    return p * (2.0 * M * K + 2.0 * K * N + part_bytes * M * N)
 
 
 def kernel_name(sched):

@@ -96,6 +96,20 @@ extern "C" {
                                     beyond).  For AllGather->MatMul, which has no reduction, it runs as
                                     TPF_SCHED_PERSISTENT. */
 
+/* Message precision, OR-ed into the `sched` argument of the reducing calls
+ * (tpf_matmul_allreduce, tpf_matmul_reducescatter, tpf_matmul_dx, and
+ * tpf_workspace_size; ignored by tpf_allgather_matmul, which reduces
+ * nothing).  With TPF_MSG_BF16 each shard's local output (the message a rank
+ * would send; the M027 page's worked example sizes it at 2 bytes per element)
+ * is rounded once, RNE, from its fp32 tile accumulation to bf16 and kept in a
+ * workspace of p * M * N * 2 bytes; the sum over shards is still a left fold
+ * in fp32 in shard order, rounded once to the output type.  Every scheduler
+ * gives the same bits for the same flag.  Against the exact sum, each
+ * element then carries up to half a bf16 ulp of each shard's partial
+ * (relative 2^-9) in addition to the fp32-message error, so fp32 outputs no
+ * longer meet 1e-4 * rms; without the flag the partials are fp32. */
+#define TPF_MSG_BF16 0x100
+
 /* Output semantics of the column-parallel backward. */
 #define TPF_ALLREDUCE 0          /* one full [M, K_in] result */
 #define TPF_REDUCESCATTER 1      /* p row slices [M/p, K_in] */
@@ -120,10 +134,11 @@ int tpf_create(tpf_handle* h, int device);
 int tpf_destroy(tpf_handle h);
 
 /* Bytes of workspace a call needs (0 if none), a pure function of its
- * arguments.  For the reducing operations it is p * M * N * 4: one fp32
- * local output [M, N] per shard (N = output width: N for the row-parallel
- * ops, K_in for tpf_matmul_dx).  `K` is the per-shard reduction length.
- * AllGather->MatMul needs none.  Returns 0 for invalid arguments. */
+ * arguments.  For the reducing operations it is p * M * N * 4 (p * M * N * 2
+ * with TPF_MSG_BF16 in `sched`): one local output [M, N] per shard (N = output
+ * width: N for the row-parallel ops, K_in for tpf_matmul_dx).  `K` is the
+ * per-shard reduction length.  AllGather->MatMul needs none.  Returns 0 for
+ * invalid arguments. */
 size_t tpf_workspace_size(int op, int p, int64_t M, int64_t N, int64_t K, int n_chunks, int sched);
 
 /* MatMul -> AllReduce (row-parallel Linear, M027 page §01-§03; cnblogs §2.4).

@@ -33,7 +33,9 @@ Sources (web pages; section names as printed on them):
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository):
   R4  partial results are summed from exact per-shard products (the oracle
-      keeps them in float64; it has no "message" precision).
+      keeps them in float64; it has no "message" precision).  The separate
+      2-byte message functions at the end round each rank's local output to
+      bfloat16 and sum in binary32 in rank order.
   R5  reduction order is irrelevant to the oracle (float64, exact-enough).
   R6  shard k owns the k-th contiguous block of the split dimension.
   R7  chunks are contiguous row ranges in order; the last takes the remainder.
@@ -243,3 +245,54 @@ def matmul_dx(dY_shards: Sequence, W_shards: Sequence, rows=None) -> np.ndarray:
 def matmul_dx_reducescatter(dY_shards: Sequence, W_shards: Sequence) -> List[np.ndarray]:
     """dX delivered as p row slices (sequence-parallel layout, reading R11)."""
     return scatter_rows(matmul_dx(dY_shards, W_shards), len(dY_shards))
+
+
+# --------------------------------------------------------------------------
+# The 2-byte message variant (M027 page §03: a rank's local output is sized
+# at two bytes per element, 512 KiB per rank and 128 KiB per 32-row chunk in
+# the worked example)
+# --------------------------------------------------------------------------
+
+
+def bf16_message(part: np.ndarray) -> np.ndarray:
+    """A rank's local output as sent at two bytes per element.
+
+    Each value is rounded once, to nearest with ties to even, to bfloat16
+    (reading: the 2-byte element of the worked example is bfloat16, the
+    inputs' format); returned as float64 (exact).
+    """
+    return bf16_bits_to_f64(round_to_bf16_bits(part))
+
+
+def sum_messages_f32(messages: Sequence) -> np.ndarray:
+    """Fixed-order binary32 sum of received messages: ((m_0 + m_1) + m_2) + ...
+
+    Every addition is rounded to binary32 (numpy float32 arithmetic rounds to
+    nearest even), in rank order k = 0..p-1 (reading R5).  The messages are
+    bfloat16 values, hence exact in binary32.  Returned as float64 (exact).
+    """
+    acc = np.asarray(messages[0], dtype=np.float64).astype(np.float32)
+    for m in messages[1:]:
+        acc = (acc + np.asarray(m, dtype=np.float64).astype(np.float32)).astype(np.float32)
+    return acc.astype(np.float64)
+
+
+def matmul_allreduce_msg_bf16(X_shards: Sequence, W_shards: Sequence, rows=None) -> np.ndarray:
+    """Y = sum_k bf16(X_k W_k): the row-parallel sum over 2-byte messages.
+
+    M027 page §01 (Y = Y_0 + Y_1) with each rank's local output Y_k sent as a
+    bfloat16 message (§03) and summed in binary32 in rank order.  The result is
+    the binary32 sum before the final rounding to the output type.
+    """
+    return sum_messages_f32([bf16_message(part) for part in shard_products(X_shards, W_shards, rows)])
+
+
+def matmul_dx_msg_bf16(dY_shards: Sequence, W_shards: Sequence, rows=None) -> np.ndarray:
+    """dX = sum_k bf16(dY_k W_k^T) (cnblogs §三, §6.4) over 2-byte messages."""
+    terms = []
+    for dYk, Wk in zip(dY_shards, W_shards):
+        d = _f64(dYk)
+        if rows is not None:
+            d = d[np.asarray(rows)]
+        terms.append(bf16_message(d @ _f64(Wk).T))
+    return sum_messages_f32(terms)

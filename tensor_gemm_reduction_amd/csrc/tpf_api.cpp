@@ -70,7 +70,12 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool valid_sched(int s) { return s >= TPF_SCHED_AUTO && s <= TPF_SCHED_TILE; }
+// A scheduler id in the low byte, optionally OR-ed with TPF_MSG_BF16.
+bool valid_sched(int s) {
+  const int base = s & 0xff, flags = s & ~0xff;
+  return base >= TPF_SCHED_AUTO && base <= TPF_SCHED_TILE && (flags & ~TPF_MSG_BF16) == 0;
+}
+bool msg_bf16(int s) { return (s & TPF_MSG_BF16) != 0; }
 bool valid_dtype(int d) { return d == TPF_BF16 || d == TPF_F32; }
 
 int out_kind(int dtype) { return dtype == TPF_F32 ? OUT_F32 : OUT_BF16; }
@@ -114,7 +119,11 @@ int check_ptr(const void* ptr, const char* name) {
   return TPF_OK;
 }
 
-size_t partial_bytes(int p, int64_t M, int64_t N) { return (size_t)p * (size_t)M * (size_t)N * sizeof(float); }
+// Workspace of the reducing ops: one local output ("message") per shard,
+// fp32 or (TPF_MSG_BF16) bf16.
+size_t partial_bytes(int p, int64_t M, int64_t N, int sched) {
+  return (size_t)p * (size_t)M * (size_t)N * (msg_bf16(sched) ? 2 : 4);
+}
 
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return TPF_OK;
@@ -143,7 +152,8 @@ int check_handle(tpf_handle h) {
 // explicitly.
 int resolve_sched(int sched, int n_chunks) {
   (void)n_chunks;
-  return sched == TPF_SCHED_AUTO ? TPF_SCHED_UNFUSED : sched;
+  const int base = sched & 0xff;
+  return base == TPF_SCHED_AUTO ? TPF_SCHED_UNFUSED : base;
 }
 
 // A reducing op (row-parallel AR/RS, or dX with either semantic).
@@ -154,7 +164,7 @@ struct ReduceCall {
   const void* const* B;
   ReduceOut ro;
   int n_chunks, sched;
-  float* P;
+  void* P;                      // partials: fp32, or bf16 when ro.pbf16
 };
 
 int set_device(tpf_handle h) {
@@ -199,7 +209,7 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
   g.dst = rc.P;
   g.dst_shard_stride = (int64_t)rc.M * rc.N;
   g.ldd = rc.N;
-  g.dst_dtype = OUT_F32;
+  g.dst_dtype = rc.ro.pbf16 ? OUT_BF16 : OUT_F32;   // the message is rounded once, from the fp32 tile
   g.M = rc.M;
   g.N = rc.N;
   g.K = rc.K;
@@ -414,7 +424,7 @@ size_t tpf_workspace_size(int op, int p, int64_t M, int64_t N, int64_t K, int n_
     case TPF_OP_MATMUL_ALLREDUCE:
     case TPF_OP_MATMUL_REDUCESCATTER:
     case TPF_OP_MATMUL_DX:
-      return partial_bytes(p, M, N);
+      return partial_bytes(p, M, N, sched);
     case TPF_OP_ALLGATHER_MATMUL:
       return 0;
     default:
@@ -430,7 +440,7 @@ int tpf_matmul_allreduce(tpf_handle h, int p, int64_t M, int64_t N, int64_t K_sh
   if ((st = check_ptrs(X, p, "X"))) return st;
   if ((st = check_ptrs(W, p, "W"))) return st;
   if ((st = check_ptr(Y, "Y"))) return st;
-  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, M, N)))) return st;
+  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, M, N, sched)))) return st;
   if ((st = check_handle(h))) return st;
   ReduceCall rc{};
   rc.p = p;
@@ -446,7 +456,8 @@ int tpf_matmul_allreduce(tpf_handle h, int p, int64_t M, int64_t N, int64_t K_sh
   rc.ro.dtype = out_kind(y_dtype);
   rc.n_chunks = n_chunks;
   rc.sched = resolve_sched(sched, n_chunks);
-  rc.P = reinterpret_cast<float*>(ws);
+  rc.ro.pbf16 = msg_bf16(sched) ? 1 : 0;
+  rc.P = ws;
   return run_reduce_call(h, rc, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -458,7 +469,7 @@ int tpf_matmul_reducescatter(tpf_handle h, int p, int64_t M, int64_t N, int64_t 
   if ((st = check_ptrs(X, p, "X"))) return st;
   if ((st = check_ptrs(W, p, "W"))) return st;
   if ((st = check_ptrs(Y_slices, p, "Y_slices"))) return st;
-  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, M, N)))) return st;
+  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, M, N, sched)))) return st;
   if ((st = check_handle(h))) return st;
   ReduceCall rc{};
   rc.p = p;
@@ -474,7 +485,8 @@ int tpf_matmul_reducescatter(tpf_handle h, int p, int64_t M, int64_t N, int64_t 
   rc.ro.dtype = out_kind(y_dtype);
   rc.n_chunks = n_chunks;
   rc.sched = resolve_sched(sched, n_chunks);
-  rc.P = reinterpret_cast<float*>(ws);
+  rc.ro.pbf16 = msg_bf16(sched) ? 1 : 0;
+  rc.P = ws;
   return run_reduce_call(h, rc, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -488,7 +500,7 @@ int tpf_matmul_dx(tpf_handle h, int sem, int p, int64_t M, int64_t K_in, int64_t
   if ((st = check_ptrs(dY, p, "dY"))) return st;
   if ((st = check_ptrs(W, p, "W"))) return st;
   if ((st = check_ptrs(dX, rs ? p : 1, "dX"))) return st;
-  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, M, K_in)))) return st;
+  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, M, K_in, sched)))) return st;
   if ((st = check_handle(h))) return st;
   ReduceCall rc{};
   rc.p = p;
@@ -504,7 +516,8 @@ int tpf_matmul_dx(tpf_handle h, int sem, int p, int64_t M, int64_t K_in, int64_t
   rc.ro.dtype = out_kind(dx_dtype);
   rc.n_chunks = n_chunks;
   rc.sched = resolve_sched(sched, n_chunks);
-  rc.P = reinterpret_cast<float*>(ws);
+  rc.ro.pbf16 = msg_bf16(sched) ? 1 : 0;
+  rc.P = ws;
   return run_reduce_call(h, rc, reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -30,14 +30,34 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 //
 // Element e of the output (row-major, rows [row0, row1) of an [M][N] result)
 // is ((P_0[e] + P_1[e]) + P_2[e]) + ... + P_{p-1}[e] in fp32, then rounded
-// once.  P_k[e] lives at P + k * shard_stride + e.
+// once.  P_k[e] is element k * shard_stride + e of the partials, which are
+// fp32, or bf16 for the 2-byte message variant (widened exactly to fp32).
 // ---------------------------------------------------------------------------
 struct ReduceOut {
   void* y[16];          // AllReduce: y[0] is the full [M][N]; ReduceScatter: p slices
   int scatter;          // 0: AllReduce layout, 1: ReduceScatter layout
   int rows_per_slice;   // M / p for ReduceScatter
   int dtype;            // OUT_F32 or OUT_BF16
+  int pbf16;            // partials ("messages") stored as bf16 instead of fp32
 };
+
+// Four consecutive partials starting at element e, widened to fp32.  PB = 1:
+// the partials are bf16 (8 bytes), PB = 0: fp32 (16 bytes).
+template <int PB>
+__device__ __forceinline__ f32x4_t load_partial4(const void* P, int64_t e) {
+  if constexpr (PB) {
+    const u32x2_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(
+        reinterpret_cast<const uint16_t*>(P) + e));
+    f32x4_t v;
+    v[0] = __uint_as_float(w[0] << 16);
+    v[1] = __uint_as_float(w[0] & 0xffff0000u);
+    v[2] = __uint_as_float(w[1] << 16);
+    v[3] = __uint_as_float(w[1] & 0xffff0000u);
+    return v;
+  } else {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(P) + e));
+  }
+}
 
 template <int OUT>
 __device__ __forceinline__ void reduce_store4(const ReduceOut& o, int64_t e, int N, f32x4_t s) {
@@ -65,8 +85,8 @@ __device__ __forceinline__ void reduce_store4(const ReduceOut& o, int64_t e, int
 // Reduce elements [e0, e1) (multiples of 4) with `nthr` cooperating threads
 // numbered `t`.  P is compile-time when PP > 0 (loads of all shards are then
 // issued together), run-time otherwise.
-template <int PP, int OUT>
-__device__ __forceinline__ void reduce_range(const float* __restrict__ P, int64_t shard_stride, int p,
+template <int PP, int OUT, int PB>
+__device__ __forceinline__ void reduce_range(const void* __restrict__ P, int64_t shard_stride, int p,
                                              int64_t e0, int64_t e1, int N, const ReduceOut& o,
                                              int64_t t, int64_t nthr) {
   // About sixteen 16-byte loads in flight per thread.
@@ -77,7 +97,7 @@ __device__ __forceinline__ void reduce_range(const float* __restrict__ P, int64_
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t e = g + (int64_t)u * nthr * 4;
-      if (e < e1) s[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(P + e));
+      if (e < e1) s[u] = load_partial4<PB>(P, e);
     }
     if constexpr (PP > 0) {
       f32x4_t v[PP > 1 ? PP - 1 : 1][U];
@@ -86,9 +106,7 @@ __device__ __forceinline__ void reduce_range(const float* __restrict__ P, int64_
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int64_t e = g + (int64_t)u * nthr * 4;
-          if (e < e1)
-            v[k - 1][u] = __builtin_nontemporal_load(
-                reinterpret_cast<const f32x4_t*>(P + (int64_t)k * shard_stride + e));
+          if (e < e1) v[k - 1][u] = load_partial4<PB>(P, (int64_t)k * shard_stride + e);
         }
 #pragma unroll
       for (int k = 1; k < PP; ++k)
@@ -99,9 +117,7 @@ __device__ __forceinline__ void reduce_range(const float* __restrict__ P, int64_
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int64_t e = g + (int64_t)u * nthr * 4;
-          if (e < e1)
-            s[u] = s[u] + __builtin_nontemporal_load(
-                              reinterpret_cast<const f32x4_t*>(P + (int64_t)k * shard_stride + e));
+          if (e < e1) s[u] = s[u] + load_partial4<PB>(P, (int64_t)k * shard_stride + e);
         }
     }
 #pragma unroll
@@ -116,8 +132,8 @@ __device__ __forceinline__ void reduce_range(const float* __restrict__ P, int64_
 // [m0, m0 + rows) and columns [n0, n0 + ncols) (ncols a multiple of 4) of the
 // [M][N] result, with `nthr` threads numbered `t`.  Per element it performs
 // exactly the additions of reduce_range, so both give identical bits.
-template <int PP, int OUT>
-__device__ __forceinline__ void reduce_tile(const float* __restrict__ P, int64_t shard_stride, int p, int m0,
+template <int PP, int OUT, int PB>
+__device__ __forceinline__ void reduce_tile(const void* __restrict__ P, int64_t shard_stride, int p, int m0,
                                             int rows, int n0, int ncols, int N, const ReduceOut& o, int t, int nthr) {
   constexpr int U = PP >= 8 ? 2 : (PP >= 4 ? 4 : (PP >= 2 ? 8 : 4));
   const int np = PP > 0 ? PP : p;
@@ -131,7 +147,7 @@ __device__ __forceinline__ void reduce_tile(const float* __restrict__ P, int64_t
       const int i = g + u * nthr;
       const int r = i / gpr;
       e[u] = (int64_t)(m0 + r) * N + n0 + 4 * (i - r * gpr);
-      if (i < total) s[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(P + e[u]));
+      if (i < total) s[u] = load_partial4<PB>(P, e[u]);
     }
     if constexpr (PP > 0) {
       f32x4_t v[PP > 1 ? PP - 1 : 1][U];
@@ -139,9 +155,7 @@ __device__ __forceinline__ void reduce_tile(const float* __restrict__ P, int64_t
       for (int k = 1; k < PP; ++k)
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          if (g + u * nthr < total)
-            v[k - 1][u] = __builtin_nontemporal_load(
-                reinterpret_cast<const f32x4_t*>(P + (int64_t)k * shard_stride + e[u]));
+          if (g + u * nthr < total) v[k - 1][u] = load_partial4<PB>(P, (int64_t)k * shard_stride + e[u]);
 #pragma unroll
       for (int k = 1; k < PP; ++k)
 #pragma unroll
@@ -150,13 +164,119 @@ __device__ __forceinline__ void reduce_tile(const float* __restrict__ P, int64_t
       for (int k = 1; k < np; ++k)
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          if (g + u * nthr < total)
-            s[u] = s[u] + __builtin_nontemporal_load(
-                              reinterpret_cast<const f32x4_t*>(P + (int64_t)k * shard_stride + e[u]));
+          if (g + u * nthr < total) s[u] = s[u] + load_partial4<PB>(P, (int64_t)k * shard_stride + e[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (g + u * nthr < total) reduce_store4<OUT>(o, e[u], N, s[u]);
+  }
+}
+
+// Eight consecutive bf16 partials (16 bytes) at element e, widened to fp32.
+__device__ __forceinline__ void load_partial8_bf16(const void* P, int64_t e, f32x4_t& lo, f32x4_t& hi) {
+  const u32x4_t w =
+      __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(P) + e));
+  lo[0] = __uint_as_float(w[0] << 16);
+  lo[1] = __uint_as_float(w[0] & 0xffff0000u);
+  lo[2] = __uint_as_float(w[1] << 16);
+  lo[3] = __uint_as_float(w[1] & 0xffff0000u);
+  hi[0] = __uint_as_float(w[2] << 16);
+  hi[1] = __uint_as_float(w[2] & 0xffff0000u);
+  hi[2] = __uint_as_float(w[3] << 16);
+  hi[3] = __uint_as_float(w[3] & 0xffff0000u);
+}
+
+// reduce_range for bf16 partials, eight elements (one 16-byte load per shard)
+// per thread and step; [e0, e1) are multiples of 8.  The same additions in
+// the same order as reduce_range, so the same bits.
+template <int PP, int OUT>
+__device__ __forceinline__ void reduce_range_b16(const void* __restrict__ P, int64_t shard_stride, int p,
+                                                 int64_t e0, int64_t e1, int N, const ReduceOut& o, int64_t t,
+                                                 int64_t nthr) {
+  constexpr int U = PP >= 8 ? 1 : (PP >= 4 ? 2 : (PP >= 2 ? 4 : 2));
+  const int np = PP > 0 ? PP : p;
+  for (int64_t g = e0 + t * 8; g < e1; g += nthr * 8 * U) {
+    f32x4_t lo[U], hi[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = g + (int64_t)u * nthr * 8;
+      if (e < e1) load_partial8_bf16(P, e, lo[u], hi[u]);
+    }
+    if constexpr (PP > 0) {
+      f32x4_t vl[PP > 1 ? PP - 1 : 1][U], vh[PP > 1 ? PP - 1 : 1][U];
+#pragma unroll
+      for (int k = 1; k < PP; ++k)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t e = g + (int64_t)u * nthr * 8;
+          if (e < e1) load_partial8_bf16(P, (int64_t)k * shard_stride + e, vl[k - 1][u], vh[k - 1][u]);
+        }
+#pragma unroll
+      for (int k = 1; k < PP; ++k)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          lo[u] = lo[u] + vl[k - 1][u];
+          hi[u] = hi[u] + vh[k - 1][u];
+        }
+    } else {
+      for (int k = 1; k < np; ++k)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t e = g + (int64_t)u * nthr * 8;
+          if (e < e1) {
+            f32x4_t a, b;
+            load_partial8_bf16(P, (int64_t)k * shard_stride + e, a, b);
+            lo[u] = lo[u] + a;
+            hi[u] = hi[u] + b;
+          }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = g + (int64_t)u * nthr * 8;
+      if (e < e1) {
+        reduce_store4<OUT>(o, e, N, lo[u]);
+        reduce_store4<OUT>(o, e + 4, N, hi[u]);
+      }
+    }
+  }
+}
+
+// reduce_tile for bf16 partials, eight elements per thread and step (ncols is
+// a multiple of 8).
+template <int PP, int OUT>
+__device__ __forceinline__ void reduce_tile_b16(const void* __restrict__ P, int64_t shard_stride, int p, int m0,
+                                                int rows, int n0, int ncols, int N, const ReduceOut& o, int t,
+                                                int nthr) {
+  constexpr int U = PP >= 8 ? 1 : (PP >= 4 ? 2 : (PP >= 2 ? 4 : 2));
+  const int np = PP > 0 ? PP : p;
+  const int gpr = ncols / 8;
+  const int total = rows * gpr;
+  for (int g = t; g < total; g += nthr * U) {
+    f32x4_t lo[U], hi[U];
+    int64_t e[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = g + u * nthr;
+      const int r = i / gpr;
+      e[u] = (int64_t)(m0 + r) * N + n0 + 8 * (i - r * gpr);
+      if (i < total) load_partial8_bf16(P, e[u], lo[u], hi[u]);
+    }
+    for (int k = 1; k < np; ++k)
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (g + u * nthr < total) {
+          f32x4_t a, b;
+          load_partial8_bf16(P, (int64_t)k * shard_stride + e[u], a, b);
+          lo[u] = lo[u] + a;
+          hi[u] = hi[u] + b;
+        }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (g + u * nthr < total) {
+        reduce_store4<OUT>(o, e[u], N, lo[u]);
+        reduce_store4<OUT>(o, e[u] + 4, N, hi[u]);
+      }
   }
 }
 

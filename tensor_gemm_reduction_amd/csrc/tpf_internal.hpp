@@ -59,7 +59,7 @@ struct ChunkGeom {
 struct FusedArgs {
   GemmOperands g;
   ReduceOut ro;
-  const float* P;             // partials (reducing ops)
+  const void* P;              // partials (reducing ops): fp32, or bf16 when ro.pbf16
   int64_t p_stride;           // elements between shards' partials (M * N)
   int p;                      // shards summed by the reduction
   int64_t reduce_elems;      // output elements per separate reduce task (multiple of 4)
@@ -94,7 +94,7 @@ struct TileArgs {
   GemmOperands g;
   int row0, row1;             // output rows covered (the tile grid starts at row0)
   ReduceOut ro;
-  const float* P;             // fp32 partials, shard k at P + k * p_stride
+  const void* P;              // partials (fp32, or bf16 when ro.pbf16), shard k at element k * p_stride
   int64_t p_stride;
   int p;
   int tiles_m, tiles_n;       // output tile grid
@@ -157,7 +157,7 @@ int cfg_bn(int cfg);
 
 // Shard GEMM tiles of rows [row0, row1) into g.dst (no reduction).
 hipError_t launch_gemm_rows(int cfg, int bl, const GemmOperands& g, int row0, int row1, hipStream_t s);
-hipError_t launch_reduce_rows(const float* P, int64_t stride, int p, int row0, int row1, int N,
+hipError_t launch_reduce_rows(const void* P, int64_t stride, int p, int row0, int row1, int N,
                               const ReduceOut& o, int num_cus, hipStream_t s);
 hipError_t launch_fused(int cfg, int bl, const FusedArgs& a, int grid, hipStream_t s);
 int fused_occupancy(int cfg, int bl);   // resident fused workgroups per CU

@@ -85,26 +85,42 @@ __device__ __forceinline__ void tile_coords(int u, int tiles_m, int tiles_n, int
   tn = w / gsize;
 }
 
-template <int OUT>
-__device__ __forceinline__ void reduce_dispatch_p(const float* P, int64_t stride, int p, int64_t e0, int64_t e1,
+template <int OUT, int PB>
+__device__ __forceinline__ void reduce_dispatch_p(const void* P, int64_t stride, int p, int64_t e0, int64_t e1,
                                                   int N, const ReduceOut& o, int64_t t, int64_t nthr) {
-  switch (p) {
-    case 2: reduce_range<2, OUT>(P, stride, p, e0, e1, N, o, t, nthr); break;
-    case 4: reduce_range<4, OUT>(P, stride, p, e0, e1, N, o, t, nthr); break;
-    case 8: reduce_range<8, OUT>(P, stride, p, e0, e1, N, o, t, nthr); break;
-    default: reduce_range<0, OUT>(P, stride, p, e0, e1, N, o, t, nthr); break;
+  if constexpr (PB) {   // bf16 partials: 16-byte loads of eight elements
+    switch (p) {
+      case 2: reduce_range_b16<2, OUT>(P, stride, p, e0, e1, N, o, t, nthr); break;
+      case 4: reduce_range_b16<4, OUT>(P, stride, p, e0, e1, N, o, t, nthr); break;
+      case 8: reduce_range_b16<8, OUT>(P, stride, p, e0, e1, N, o, t, nthr); break;
+      default: reduce_range_b16<0, OUT>(P, stride, p, e0, e1, N, o, t, nthr); break;
+    }
+  } else {
+    switch (p) {
+      case 2: reduce_range<2, OUT, 0>(P, stride, p, e0, e1, N, o, t, nthr); break;
+      case 4: reduce_range<4, OUT, 0>(P, stride, p, e0, e1, N, o, t, nthr); break;
+      case 8: reduce_range<8, OUT, 0>(P, stride, p, e0, e1, N, o, t, nthr); break;
+      default: reduce_range<0, OUT, 0>(P, stride, p, e0, e1, N, o, t, nthr); break;
+    }
   }
 }
 
-__device__ __forceinline__ void reduce_any(const float* P, int64_t stride, int p, int64_t e0, int64_t e1, int N,
+__device__ __forceinline__ void reduce_any(const void* P, int64_t stride, int p, int64_t e0, int64_t e1, int N,
                                            const ReduceOut& o, int64_t t, int64_t nthr) {
-  if (o.dtype == OUT_F32)
-    reduce_dispatch_p<OUT_F32>(P, stride, p, e0, e1, N, o, t, nthr);
-  else
-    reduce_dispatch_p<OUT_BF16>(P, stride, p, e0, e1, N, o, t, nthr);
+  if (o.pbf16) {
+    if (o.dtype == OUT_F32)
+      reduce_dispatch_p<OUT_F32, 1>(P, stride, p, e0, e1, N, o, t, nthr);
+    else
+      reduce_dispatch_p<OUT_BF16, 1>(P, stride, p, e0, e1, N, o, t, nthr);
+  } else {
+    if (o.dtype == OUT_F32)
+      reduce_dispatch_p<OUT_F32, 0>(P, stride, p, e0, e1, N, o, t, nthr);
+    else
+      reduce_dispatch_p<OUT_BF16, 0>(P, stride, p, e0, e1, N, o, t, nthr);
+  }
 }
 
-__global__ __launch_bounds__(256) void reduce_rows_kernel(const float* P, int64_t stride, int p, int64_t e0,
+__global__ __launch_bounds__(256) void reduce_rows_kernel(const void* P, int64_t stride, int p, int64_t e0,
                                                           int64_t e1, int N, ReduceOut o) {
   reduce_any(P, stride, p, e0, e1, N, o, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256);
 }
@@ -239,7 +255,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void fused_kernel(FusedArgs args) {
           t_mid = a.timeline ? __builtin_amdgcn_s_memrealtime() : 0;
           const int G = a.gemm_tasks[c];
           const int64_t cb = (int64_t)a.ch.row0(c - 1) * a.g.N, ce = (int64_t)a.ch.row1(c - 1) * a.g.N;
-          const int64_t per = ((ce - cb + G - 1) / G + 3) / 4 * 4;
+          const int64_t per = ((ce - cb + G - 1) / G + 7) / 8 * 8;   // whole 8-element groups
           const int64_t e0 = cb + (int64_t)u * per, e1 = min(e0 + per, ce);
           if (e0 < e1) {
             if (tid == 0) wait_at_least(&ctl->ready[c - 1], a.gemm_tasks[c - 1], a);
@@ -300,23 +316,35 @@ __device__ __forceinline__ int xcd_task(int b, int total) {
 }
 
 // Sum output tile (m0, rows, n0, ncols) over the p shards' partials.
-__device__ __forceinline__ void reduce_tile_any(const TileArgs& a, int m0, int rows, int n0, int ncols, int tid,
-                                                int nthr) {
+template <int OUT, int PB>
+__device__ __forceinline__ void reduce_tile_p(const TileArgs& a, int m0, int rows, int n0, int ncols, int tid,
+                                              int nthr) {
   const int N = a.g.N;
-  if (a.ro.dtype == OUT_F32) {
+  if constexpr (PB) {
     switch (a.p) {
-      case 2: reduce_tile<2, OUT_F32>(a.P, a.p_stride, 2, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
-      case 4: reduce_tile<4, OUT_F32>(a.P, a.p_stride, 4, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
-      case 8: reduce_tile<8, OUT_F32>(a.P, a.p_stride, 8, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
-      default: reduce_tile<0, OUT_F32>(a.P, a.p_stride, a.p, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+      case 2: reduce_tile_b16<2, OUT>(a.P, a.p_stride, 2, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+      case 4: reduce_tile_b16<4, OUT>(a.P, a.p_stride, 4, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+      case 8: reduce_tile_b16<8, OUT>(a.P, a.p_stride, 8, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+      default: reduce_tile_b16<0, OUT>(a.P, a.p_stride, a.p, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
     }
   } else {
     switch (a.p) {
-      case 2: reduce_tile<2, OUT_BF16>(a.P, a.p_stride, 2, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
-      case 4: reduce_tile<4, OUT_BF16>(a.P, a.p_stride, 4, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
-      case 8: reduce_tile<8, OUT_BF16>(a.P, a.p_stride, 8, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
-      default: reduce_tile<0, OUT_BF16>(a.P, a.p_stride, a.p, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+      case 2: reduce_tile<2, OUT, 0>(a.P, a.p_stride, 2, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+      case 4: reduce_tile<4, OUT, 0>(a.P, a.p_stride, 4, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+      case 8: reduce_tile<8, OUT, 0>(a.P, a.p_stride, 8, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
+      default: reduce_tile<0, OUT, 0>(a.P, a.p_stride, a.p, m0, rows, n0, ncols, N, a.ro, tid, nthr); break;
     }
+  }
+}
+
+__device__ __forceinline__ void reduce_tile_any(const TileArgs& a, int m0, int rows, int n0, int ncols, int tid,
+                                                int nthr) {
+  if (a.ro.pbf16) {
+    if (a.ro.dtype == OUT_F32) reduce_tile_p<OUT_F32, 1>(a, m0, rows, n0, ncols, tid, nthr);
+    else reduce_tile_p<OUT_BF16, 1>(a, m0, rows, n0, ncols, tid, nthr);
+  } else {
+    if (a.ro.dtype == OUT_F32) reduce_tile_p<OUT_F32, 0>(a, m0, rows, n0, ncols, tid, nthr);
+    else reduce_tile_p<OUT_BF16, 0>(a, m0, rows, n0, ncols, tid, nthr);
   }
 }
 
@@ -327,7 +355,7 @@ __device__ __forceinline__ void reduce_tile_any(const TileArgs& a, int m0, int r
 // panels of one shard, and the XCDs of different shards advance through the
 // same output tiles at the same time.
 //
-// RED = 1: after storing its fp32 partial, a workgroup bumps the output
+// RED = 1: after storing its partial, a workgroup bumps the output
 // tile's counter (release); the one that brings it to p acquires and sums
 // the tile in shard order.  No workgroup ever waits for another.
 template <class Cfg, int BL, int RED>
@@ -348,8 +376,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void tile_kernel(TileArgs args) {
     const uint64_t t_start = a.timeline ? __builtin_amdgcn_s_memrealtime() : 0;
     uint64_t t_mid = 0;
     gemm_tile<Cfg, BL>(f, j);
-    store_tile<Cfg, OUT_F32>(f, j, reinterpret_cast<float*>(a.g.dst) + (int64_t)shard * a.g.dst_shard_stride,
-                             a.g.ldd);
+    store_any<Cfg>(f, j, a.g, shard);   // fp32 partial, or bf16 for the 2-byte message
     const int T = tm * a.tiles_n + tn;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
@@ -386,7 +413,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void tile_kernel(TileArgs args) {
 // Launchers
 // ---------------------------------------------------------------------------
 
-hipError_t launch_reduce_rows(const float* P, int64_t stride, int p, int row0, int row1, int N,
+hipError_t launch_reduce_rows(const void* P, int64_t stride, int p, int row0, int row1, int N,
                               const ReduceOut& o, int num_cus, hipStream_t s) {
   const int64_t e0 = (int64_t)row0 * N, e1 = (int64_t)row1 * N;
   const int64_t groups = (e1 - e0) / 4;

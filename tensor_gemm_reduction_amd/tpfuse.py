@@ -101,8 +101,12 @@ def _dtype_code(dt: torch.dtype) -> int:
     raise ValueError(f"output dtype must be bfloat16 or float32, got {dt}")
 
 
-def _sched(s) -> int:
-    return SCHEDS[s] if isinstance(s, str) else int(s)
+MSG_BF16 = 0x100           # TPF_MSG_BF16: shard partials ("messages") kept as bf16
+MESSAGES = {"fp32": 0, "bf16": MSG_BF16}
+
+
+def _sched(s, message: str = "fp32") -> int:
+    return (SCHEDS[s] if isinstance(s, str) else int(s)) | MESSAGES[message]
 
 
 def _stream_ptr(stream) -> int:
@@ -185,12 +189,13 @@ def default_handle(device: Optional[int] = None) -> Handle:
     return h
 
 
-def workspace_size(op: int, p: int, M: int, N: int, K: int, n_chunks: int = 1, sched=SCHED_AUTO) -> int:
-    return int(load().tpf_workspace_size(op, p, M, N, K, n_chunks, _sched(sched)))
+def workspace_size(op: int, p: int, M: int, N: int, K: int, n_chunks: int = 1, sched=SCHED_AUTO,
+                   message: str = "fp32") -> int:
+    return int(load().tpf_workspace_size(op, p, M, N, K, n_chunks, _sched(sched, message)))
 
 
-def _ws(op, p, M, N, K, n_chunks, sched, ws, device):
-    need = workspace_size(op, p, M, N, K, n_chunks, sched)
+def _ws(op, p, M, N, K, n_chunks, sched, ws, device, message="fp32"):
+    need = workspace_size(op, p, M, N, K, n_chunks, sched, message)
     if need == 0:
         return ws, 0 if ws is None else ws.numel() * ws.element_size()
     if ws is None:
@@ -200,7 +205,7 @@ def _ws(op, p, M, N, K, n_chunks, sched, ws, device):
 
 def matmul_allreduce(X: List[torch.Tensor], W: List[torch.Tensor], out_dtype=torch.bfloat16, n_chunks: int = 1,
                      sched="auto", Y: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                     handle: Optional[Handle] = None, stream=None) -> torch.Tensor:
+                     handle: Optional[Handle] = None, stream=None, message: str = "fp32") -> torch.Tensor:
     """Y = sum_k X[k] @ W[k] (row-parallel Linear, AllReduce layout)."""
     p = len(X)
     M, K = X[0].shape
@@ -208,18 +213,18 @@ def matmul_allreduce(X: List[torch.Tensor], W: List[torch.Tensor], out_dtype=tor
     dev = X[0].device
     if Y is None:
         Y = torch.empty((M, N), dtype=out_dtype, device=dev)
-    ws, ws_bytes = _ws(OP_MATMUL_ALLREDUCE, p, M, N, K, n_chunks, sched, ws, dev)
+    ws, ws_bytes = _ws(OP_MATMUL_ALLREDUCE, p, M, N, K, n_chunks, sched, ws, dev, message)
     h = handle or default_handle(dev.index)
     check(load().tpf_matmul_allreduce(h.ptr, p, M, N, K, ptr_array([x.data_ptr() for x in X]),
                                       ptr_array([w.data_ptr() for w in W]), Y.data_ptr(), _dtype_code(Y.dtype),
-                                      n_chunks, _sched(sched), ws.data_ptr() if ws is not None else None, ws_bytes,
+                                      n_chunks, _sched(sched, message), ws.data_ptr() if ws is not None else None, ws_bytes,
                                       _stream_ptr(stream)))
     return Y
 
 
 def matmul_reducescatter(X: List[torch.Tensor], W: List[torch.Tensor], out_dtype=torch.bfloat16, n_chunks: int = 1,
                          sched="auto", Y: Optional[List[torch.Tensor]] = None, ws: Optional[torch.Tensor] = None,
-                         handle: Optional[Handle] = None, stream=None) -> List[torch.Tensor]:
+                         handle: Optional[Handle] = None, stream=None, message: str = "fp32") -> List[torch.Tensor]:
     """Slice r = rows [r*M/p, (r+1)*M/p) of sum_k X[k] @ W[k] (ReduceScatter layout)."""
     p = len(X)
     M, K = X[0].shape
@@ -227,11 +232,11 @@ def matmul_reducescatter(X: List[torch.Tensor], W: List[torch.Tensor], out_dtype
     dev = X[0].device
     if Y is None:
         Y = [torch.empty((M // p, N), dtype=out_dtype, device=dev) for _ in range(p)]
-    ws, ws_bytes = _ws(OP_MATMUL_REDUCESCATTER, p, M, N, K, n_chunks, sched, ws, dev)
+    ws, ws_bytes = _ws(OP_MATMUL_REDUCESCATTER, p, M, N, K, n_chunks, sched, ws, dev, message)
     h = handle or default_handle(dev.index)
     check(load().tpf_matmul_reducescatter(h.ptr, p, M, N, K, ptr_array([x.data_ptr() for x in X]),
                                           ptr_array([w.data_ptr() for w in W]), ptr_array([y.data_ptr() for y in Y]),
-                                          _dtype_code(Y[0].dtype), n_chunks, _sched(sched),
+                                          _dtype_code(Y[0].dtype), n_chunks, _sched(sched, message),
                                           ws.data_ptr() if ws is not None else None, ws_bytes, _stream_ptr(stream)))
     return Y
 
@@ -258,7 +263,7 @@ def allgather_matmul(X_slices: List[torch.Tensor], W: torch.Tensor, out_dtype=to
 
 def matmul_dx(dY: List[torch.Tensor], W: List[torch.Tensor], semantic: int = ALLREDUCE, out_dtype=torch.bfloat16,
               n_chunks: int = 1, sched="auto", dX=None, ws: Optional[torch.Tensor] = None,
-              handle: Optional[Handle] = None, stream=None):
+              handle: Optional[Handle] = None, stream=None, message: str = "fp32"):
     """dX = sum_k dY[k] @ W[k]^T; one tensor (ALLREDUCE) or p row slices (REDUCESCATTER)."""
     p = len(dY)
     M, Ns = dY[0].shape
@@ -270,10 +275,10 @@ def matmul_dx(dY: List[torch.Tensor], W: List[torch.Tensor], semantic: int = ALL
         else:
             dX = [torch.empty((M // p, Kin), dtype=out_dtype, device=dev) for _ in range(p)]
     outs = [dX] if semantic == ALLREDUCE else list(dX)
-    ws, ws_bytes = _ws(OP_MATMUL_DX, p, M, Kin, Ns, n_chunks, sched, ws, dev)
+    ws, ws_bytes = _ws(OP_MATMUL_DX, p, M, Kin, Ns, n_chunks, sched, ws, dev, message)
     h = handle or default_handle(dev.index)
     check(load().tpf_matmul_dx(h.ptr, semantic, p, M, Kin, Ns, ptr_array([d.data_ptr() for d in dY]),
                                ptr_array([w.data_ptr() for w in W]), ptr_array([o.data_ptr() for o in outs]),
-                               _dtype_code(outs[0].dtype), n_chunks, _sched(sched),
+                               _dtype_code(outs[0].dtype), n_chunks, _sched(sched, message),
                                ws.data_ptr() if ws is not None else None, ws_bytes, _stream_ptr(stream)))
     return dX

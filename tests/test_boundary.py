@@ -67,6 +67,11 @@ def test_workspace_size():
     assert ws(tp.OP_MATMUL_REDUCESCATTER, 3, 16, 16, 16, 1) == 0      # M % p
     assert ws(tp.OP_MATMUL_ALLREDUCE, 2, 16, 12, 16, 1) == 0          # N % 8
     assert ws(tp.OP_MATMUL_ALLREDUCE, 2, 16, 16, 16, 17) == 0         # n_chunks > M
+    # 2-byte messages halve the partials' workspace
+    assert ws(tp.OP_MATMUL_ALLREDUCE, 4, 4096, 4096, 4096, 8, message="bf16") == 4 * 4096 * 4096 * 2
+    assert ws(tp.OP_MATMUL_DX, 8, 2048, 12288, 6144, 8, "unfused", "bf16") == 8 * 2048 * 12288 * 2
+    assert ws(tp.OP_ALLGATHER_MATMUL, 8, 2048, 6144, 12288, 8, message="bf16") == 0
+    assert ws(tp.OP_MATMUL_ALLREDUCE, 4, 64, 64, 64, 1, tp.SCHED_TILE | 0x200) == 0   # unknown flag
 
 
 def _ar(p=2, M=64, N=64, K=64, X=None, W=None, Y=A16, dtype=tp.BF16, n=1, sched=tp.SCHED_AUTO, ws=A16,
@@ -96,6 +101,10 @@ def _err(call):
     (dict(K=20), tp.ERR_ALIGNMENT),
     (dict(dtype=7), tp.ERR_INVALID_ARG),
     (dict(sched=9), tp.ERR_INVALID_ARG),
+    (dict(sched=tp.SCHED_UNFUSED | 0x200), tp.ERR_INVALID_ARG),       # unknown flag bit
+    (dict(sched=7 | tp.MSG_BF16), tp.ERR_INVALID_ARG),                # unknown scheduler with the message flag
+    (dict(sched=tp.SCHED_UNFUSED | tp.MSG_BF16, ws_bytes=2 * 64 * 64 * 2 - 1), tp.ERR_WORKSPACE),
+    (dict(sched=tp.SCHED_UNFUSED | tp.MSG_BF16, ws_bytes=2 * 64 * 64 * 2), tp.ERR_INVALID_ARG),  # enough: NULL handle
     (dict(Y=None), tp.ERR_INVALID_ARG),
     (dict(Y=MIS), tp.ERR_ALIGNMENT),
     (dict(ws=None), tp.ERR_WORKSPACE),

@@ -177,6 +177,98 @@ def test_kernel_timing_records_one_launch_per_call():
 
 
 # ---------------------------------------------------------------------------
+# 2-byte messages (TPF_MSG_BF16)
+# ---------------------------------------------------------------------------
+
+def _ulp_bf16(x):
+    """Spacing of bfloat16 numbers at |x| (8 significant bits)."""
+    return np.ldexp(1.0, np.frexp(np.abs(x))[1] - 8)
+
+
+def assert_message_bf16(y32, parts, ref16, what):
+    """GPU fp32 output with bf16 messages against the oracle's message sum.
+
+    The GPU rounds each partial from its fp32 tile accumulation, the oracle
+    from the exact product; the two roundings can differ by one bfloat16 ulp
+    where a partial sits next to a rounding boundary, and the binary32 folds
+    then differ by the same amount plus their own rounding."""
+    y = y32.detach().cpu().double().numpy()
+    tol = sum(_ulp_bf16(q) for q in parts) + 4 * len(parts) * 2.0 ** -24 * sum(np.abs(q) for q in parts)
+    bad = np.abs(y - ref16) > tol
+    assert not bad.any(), f"{what}: {bad.sum()} elements off by more than one bf16 ulp per message"
+    # and most elements agree exactly: a flip needs a partial within 2^-16 relative of a boundary
+    assert (y == ref16).mean() > 0.9, f"{what}: only {(y == ref16).mean():.3f} exact"
+
+
+@pytest.mark.parametrize("p,M,N,K", [(3, 300, 328, 200), (4, 64, 392, 136), (8, 16, 1024, 256)])
+def test_message_bf16_allreduce(p, M, N, K):
+    say(f"message bf16 allreduce p={p} M={M} N={N} K={K}")
+    Xh = shards([(M, K)] * p, ("normal", 1.0), 81)
+    Wh = shards([(K, N)] * p, ("normal", 0.05), 82)
+    parts = O.shard_products(bits(Xh), bits(Wh))
+    ref16 = O.matmul_allreduce_msg_bf16(bits(Xh), bits(Wh))
+    X, W = gpu(Xh), gpu(Wh)
+    outs = {}
+    for sched in SCHEDS:
+        for n in sorted({1, 3, min(M, 8)}):
+            y32 = tp.matmul_allreduce(X, W, torch.float32, n_chunks=n, sched=sched, message="bf16")
+            y16 = tp.matmul_allreduce(X, W, torch.bfloat16, n_chunks=n, sched=sched, message="bf16")
+            torch.cuda.synchronize()
+            what = f"AR msg16 p={p} {sched} n={n}"
+            assert_message_bf16(y32, parts, ref16, what)
+            assert_bf16_is_rne_of_f32(y16, y32, what)
+            outs[(sched, n)] = y32
+    base = outs[("unfused", 1)]
+    for key, y in outs.items():
+        assert_bitwise(y, base, f"msg16 {key} vs unfused n=1")
+    # the fp32-message result differs (that is the point of the flag)
+    y_fp32 = tp.matmul_allreduce(X, W, torch.float32, sched="unfused")
+    torch.cuda.synchronize()
+    assert not torch.equal(y_fp32, base)
+
+
+def test_message_bf16_integer_exact():
+    # integers of magnitude <= 32 per partial are exact in bfloat16: the
+    # 2-byte message loses nothing and the result is the exact sum
+    p, M, N, K = 4, 70, 136, 8
+    rng = np.random.default_rng(83)
+    Xh = [torch.from_numpy(rng.integers(-2, 3, (M, K)).astype(np.float32)).to(torch.bfloat16) for _ in range(p)]
+    Wh = [torch.from_numpy(rng.integers(-2, 3, (K, N)).astype(np.float32)).to(torch.bfloat16) for _ in range(p)]
+    ref = O.matmul_allreduce(bits(Xh), bits(Wh))
+    for sched in SCHEDS:
+        y = tp.matmul_allreduce(gpu(Xh), gpu(Wh), torch.float32, n_chunks=3, sched=sched, message="bf16")
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().double().numpy(), ref), sched
+
+
+def test_message_bf16_reducescatter_and_dx():
+    p, M, N, K = 4, 256, 264, 136
+    say("message bf16 reducescatter / dX")
+    Xh = shards([(M, K)] * p, ("normal", 1.0), 84)
+    Wh = shards([(K, N)] * p, ("normal", 0.05), 85)
+    X, W = gpu(Xh), gpu(Wh)
+    ar = tp.matmul_allreduce(X, W, torch.bfloat16, sched="unfused", message="bf16")
+    for sched in SCHEDS:
+        sl = tp.matmul_reducescatter(X, W, torch.bfloat16, n_chunks=4, sched=sched, message="bf16")
+        torch.cuda.synchronize()
+        for r in range(p):
+            assert_bitwise(sl[r], ar[r * (M // p):(r + 1) * (M // p)], f"RS msg16 {sched} slice {r}")
+    # dX with bf16 messages: W_k [K_in, N_shard] used transposed
+    dYh = shards([(M, N)] * p, ("normal", 1.0), 86)
+    Wd = shards([(K, N)] * p, ("normal", 0.05), 87)
+    parts = [O.bf16_bits_to_f64(d) @ O.bf16_bits_to_f64(w).T for d, w in zip(bits(dYh), bits(Wd))]
+    ref16 = O.matmul_dx_msg_bf16(bits(dYh), bits(Wd))
+    outs = []
+    for sched in SCHEDS:
+        d32 = tp.matmul_dx(gpu(dYh), gpu(Wd), tp.ALLREDUCE, torch.float32, n_chunks=4, sched=sched, message="bf16")
+        torch.cuda.synchronize()
+        assert_message_bf16(d32, parts, ref16, f"dX msg16 {sched}")
+        outs.append(d32)
+    for d in outs[1:]:
+        assert_bitwise(d, outs[0], "dX msg16 schedulers")
+
+
+# ---------------------------------------------------------------------------
 # MatMul -> ReduceScatter
 # ---------------------------------------------------------------------------
 

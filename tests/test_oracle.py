@@ -247,10 +247,68 @@ def pin_round_bf16(o):
     return all(int(g) == _nearest_bf16_bruteforce(x) for g, x in zip(got, xs))
 
 
+def pin_message_bf16_golden(o):
+    """Hand-worked 2-byte message cases (ties, binary32 absorption, rank order)."""
+    g = _load("message_bf16.json")
+    for case in g["cases"]:
+        Xs = [_bits(x) for x in case["X"]]
+        Ws = [_bits(w) for w in case["W"]]
+        if not np.array_equal(o.matmul_allreduce_msg_bf16(Xs, Ws), case["Y"]):
+            return False
+        if not np.array_equal(o.matmul_allreduce(Xs, Ws), case["Y_exact"]):
+            return False
+        if not all(np.array_equal(o.bf16_message(part), m)
+                   for part, m in zip(o.shard_products(Xs, Ws), case["messages"])):
+            return False
+    return True
+
+
+def pin_message_bf16_integer_exact(o):
+    """Small integers with short shards: every local output is an integer of
+    magnitude <= 2*2*8 = 32 (exact in bfloat16) and every partial sum of p <= 4
+    of them is exact in binary32, so the 2-byte-message result is the exact sum."""
+    rng = np.random.default_rng(5)
+    for p in (1, 2, 3, 4):
+        Xs = [_bits(rng.integers(-2, 3, (9, 8))) for _ in range(p)]
+        Ws = [_bits(rng.integers(-2, 3, (8, 7))) for _ in range(p)]
+        if not np.array_equal(o.matmul_allreduce_msg_bf16(Xs, Ws), o.matmul_allreduce(Xs, Ws)):
+            return False
+    return True
+
+
+def pin_message_bf16_error_bound(o):
+    """Against the exact sum, each element is off by at most half a bfloat16
+    ulp of every local output plus the binary32 fold's rounding (p - 1
+    additions, each within 2^-24 of a partial sum bounded by sum_k |m_k|)."""
+    rng = np.random.default_rng(6)
+    p, M, K, N = 4, 24, 40, 20
+    Xs = [_bits(rng.standard_normal((M, K))) for _ in range(p)]
+    Ws = [_bits(rng.standard_normal((K, N)) * 0.1) for _ in range(p)]
+    parts = o.shard_products(Xs, Ws)
+    got = o.matmul_allreduce_msg_bf16(Xs, Ws)
+    exact = sum(parts)
+    half_ulp = sum(np.ldexp(1.0, np.frexp(np.abs(q))[1] - 9) for q in parts)
+    fold = (p - 1) * 2.0 ** -24 * sum(np.abs(q) for q in parts) * (1 + 2.0 ** -8)
+    err = np.abs(got - exact)
+    # the bound is attained only in rare corners; it must hold everywhere and not be vacuous
+    return bool(np.all(err <= half_ulp + fold)) and float(err.max()) > 0.0
+
+
+def pin_message_bf16_dx(o):
+    """dX over 2-byte messages equals the row-parallel message sum with the
+    transposed weight shards (cnblogs §6.4: dX = sum_k dY_k A_k^T)."""
+    rng = np.random.default_rng(7)
+    dY = [_bits(rng.standard_normal((6, 5))) for _ in range(3)]
+    W = [_bits(rng.standard_normal((9, 5))) for _ in range(3)]
+    Wt = [np.ascontiguousarray(w.T) for w in W]
+    return np.array_equal(o.matmul_dx_msg_bf16(dY, W), o.matmul_allreduce_msg_bf16(dY, Wt))
+
+
 PINS = [pin_tiny_row_parallel, pin_tiny_reducescatter, pin_tiny_column_backward, pin_tiny_allgather,
         pin_worked_example, pin_brute_force_unsharded, pin_brute_force_dx, pin_dx_autograd,
         pin_column_identity, pin_chunked_equals_whole, pin_rs_slices, pin_chunk_bounds,
-        pin_round_bf16]
+        pin_round_bf16, pin_message_bf16_golden, pin_message_bf16_integer_exact,
+        pin_message_bf16_error_bound, pin_message_bf16_dx]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -360,8 +418,43 @@ def _m_pipeline_serial():
     return _Mutant(pipeline_time=lambda n, tc, tm: n * max(tc, tm))
 
 
+def _msg_mutant(message=None, fold=None):
+    """Copies of the 2-byte-message functions with one step replaced."""
+    message = message or O.bf16_message
+    fold = fold or O.sum_messages_f32
+
+    def matmul_allreduce_msg_bf16(Xs, Ws, rows=None):
+        return fold([message(q) for q in O.shard_products(Xs, Ws, rows)])
+
+    def matmul_dx_msg_bf16(dY, W, rows=None):
+        return fold([message(O.bf16_bits_to_f64(d) @ O.bf16_bits_to_f64(w).T) for d, w in zip(dY, W)])
+    return _Mutant(bf16_message=message, sum_messages_f32=fold, matmul_allreduce_msg_bf16=matmul_allreduce_msg_bf16,
+                   matmul_dx_msg_bf16=matmul_dx_msg_bf16)
+
+
+def _m_message_truncated():
+    # round toward zero instead of to nearest even
+    return _msg_mutant(message=lambda q: np.trunc(np.ldexp(q, 7 - np.frexp(q)[1] + 1)) *
+                       np.ldexp(1.0, np.frexp(q)[1] - 8))
+
+
+def _m_message_unrounded():
+    # the message kept in binary32 (no 2-byte rounding)
+    return _msg_mutant(message=lambda q: np.asarray(q, np.float64).astype(np.float32).astype(np.float64))
+
+
+def _m_message_fold_f64():
+    # the sum carried in float64 instead of binary32
+    return _msg_mutant(fold=lambda ms: sum(np.asarray(m, np.float64) for m in ms))
+
+
+def _m_message_fold_reversed():
+    return _msg_mutant(fold=lambda ms: O.sum_messages_f32(list(ms)[::-1]))
+
+
 MUTANTS = [_m_dropped_shard, _m_sign, _m_dx_untransposed, _m_slices_reversed, _m_gather_reversed,
-           _m_round_truncate, _m_round_via_f32, _m_chunk_lastshort, _m_pipeline_serial]
+           _m_round_truncate, _m_round_via_f32, _m_chunk_lastshort, _m_pipeline_serial,
+           _m_message_truncated, _m_message_unrounded, _m_message_fold_f64, _m_message_fold_reversed]
 
 
 @pytest.mark.parametrize("mut", MUTANTS, ids=[m.__name__ for m in MUTANTS])
