@@ -122,6 +122,16 @@ def main():
             tp.matmul_dx(inp.X, inp.W, tp.ALLREDUCE, n_chunks=n, sched=sched, dX=dX, ws=ws, handle=handle,
                          message=msg)
         ws_bytes = ws.numel()
+    elif wl.op.startswith("wgrad"):
+        # dW_k [K, N] = A_k^T B_k over M rows, fp32 out (the optimizer's input)
+        dWs = [torch.empty((K, N), dtype=torch.float32, device=dev) for _ in range(p)]
+        operands = [inputs.weight_grad_operands(inp) for inp in sets]
+
+        def call(i, sched):
+            A, B = operands[i % len(operands)]
+            tp.weight_grad(A, B, dW=dWs, handle=handle)
+        ws_bytes = 0
+        args.modes = "none"      # no reduction: there are no schedules to compare
     else:  # allgather
         XG = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -230,7 +240,7 @@ def main():
         "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
                      "algorithmic_bytes": kbytes, "algorithmic_flops": flops,
-                     "kernel": kernel_name(args.sched),
+                     "kernel": kernel_name(args.sched, wl.op),
                      "avg_kernel_ms": round(avg_kernel_ms, 4),
                      "timed_launches": len(kern_ms),
                      "avg_step_event_ms": round(sum(step_ms) / len(step_ms), 4)},
@@ -248,13 +258,17 @@ def kernel_bytes(wl, part_bytes=4):
     p, M, N, K = wl.p, wl.M, wl.N, wl.K
     if wl.op == "allgather":
         return 2.0 * M * K + 2.0 * K * N + 2.0 * M * N
+    if wl.op.startswith("wgrad"):   # A_k [M, K], B_k [M, N], dW_k [K, N] fp32
+        return p * (2.0 * M * K + 2.0 * M * N + 4.0 * K * N)
     if wl.op == "dx":      # dY_k [M, N], W_k [K, N], partials [M, K]
         return p * (2.0 * M * N + 2.0 * K * N + part_bytes * M * K)
     return p * (2.0 * M * K + 2.0 * K * N + part_bytes * M * N)
 
 
-def kernel_name(sched):
+def kernel_name(sched, op=""):
     """The kernel that dominates one step of `sched` (what `roofline` prices)."""
+    if op.startswith("wgrad"):
+        return "tile_kernel A_KM (weight-gradient GEMM tiles, transposed A)"
     if sched == "persistent":
         return "fused_kernel (persistent: shard GEMM tiles + chunk reductions)"
     if sched == "tile":
@@ -277,7 +291,8 @@ def cpu_baseline(wl, inp, seconds):
         threads = os.cpu_count() or 1
     Xb = [inputs.bf16_to_bits(x) for x in inp.X]
     Wb = [inputs.bf16_to_bits(w) for w in inp.W]
-    M = wl.M
+    # output rows the sample is drawn from (a weight gradient's rows are K)
+    M = wl.K if wl.op.startswith("wgrad") else wl.M
 
     def run(rows):
         r = np.arange(rows)
@@ -286,6 +301,9 @@ def cpu_baseline(wl, inp, seconds):
             O.matmul_allreduce(Xb, Wb, rows=r)
         elif wl.op == "dx":
             O.matmul_dx(Xb, Wb, rows=r)
+        elif wl.op.startswith("wgrad"):
+            A, B = (Xb * wl.p, Wb) if wl.op == "wgrad_col" else (Xb, Wb * wl.p)
+            O.weight_grad([a[:, :rows] for a in A], B)
         else:
             xg = O.allgather(Xb)[:rows]
             _ = xg @ O.bf16_bits_to_f64(Wb[0])

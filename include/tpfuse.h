@@ -184,6 +184,21 @@ int tpf_matmul_dx(tpf_handle h, int sem, int p, int64_t M, int64_t K_in, int64_t
                   const void* const* dY, const void* const* W, void* const* dX, int dx_dtype,
                   int n_chunks, int sched, void* ws, size_t ws_bytes, void* stream);
 
+/* Weight gradients of the tensor-parallel Linear (cnblogs §三 / §四 backward:
+ * each rank's weight gradient is a local GEMM, no communication).
+ *   dW[k] = A[k]^T B[k], k = 0..p-1, summed over the M rows in fp32 and
+ *   rounded once to dw_dtype (TPF_BF16 or TPF_F32):
+ *   A[k]: [M, R] bf16, B[k]: [M, C] bf16, dW[k]: [R, C].
+ *   Row-parallel layer (W_k [K_shard, N]): A[k] = X_k [M, K_shard] (the
+ *   shard's input), B[k] = dY [M, N] (the full output gradient; pass the same
+ *   pointer p times).  Column-parallel layer (W_k [K, N_shard]): A[k] = the
+ *   gathered input X [M, K] (the same pointer p times, e.g. X_gathered of
+ *   tpf_allgather_matmul), B[k] = dY_k [M, N_shard].
+ *   R and C must be multiples of 8; no workspace; the kernel timed by
+ *   tpf_debug_set_kernel_timing is this call's only launch. */
+int tpf_weight_grad(tpf_handle h, int p, int64_t M, int64_t R, int64_t C, const void* const* A,
+                    const void* const* B, void* const* dW, int dw_dtype, void* stream);
+
 /* Wait for the handle's work on `stream` to finish and report whether a
  * bounded wait inside the persistent kernel gave up since the last query
  * (TPF_ERR_TIMEOUT; the outputs of that call are then undefined).  Clears

@@ -296,3 +296,20 @@ def matmul_dx_msg_bf16(dY_shards: Sequence, W_shards: Sequence, rows=None) -> np
             d = d[np.asarray(rows)]
         terms.append(bf16_message(d @ _f64(Wk).T))
     return sum_messages_f32(terms)
+
+
+# --------------------------------------------------------------------------
+# Weight gradients (cnblogs §三 / §四 backward: local GEMMs, no communication)
+# --------------------------------------------------------------------------
+
+
+def weight_grad(A_shards: Sequence, B_shards: Sequence) -> List[np.ndarray]:
+    """dW_k = A_k^T B_k for every shard, float64.
+
+    Row-parallel Linear Y = sum_k X_k W_k: dL/dW_k = X_k^T dY (A_k = X_k,
+    B_k = dY for every k).  Column-parallel Y_k = X W_k: dL/dW_k = X^T dY_k
+    (A_k = the gathered X for every k, B_k = dY_k).
+    """
+    if len(A_shards) != len(B_shards):
+        raise ValueError("A and B need one block per shard")
+    return [_f64(a).T @ _f64(b) for a, b in zip(A_shards, B_shards)]

@@ -205,6 +205,7 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
     g.B[k] = reinterpret_cast<const __bf16*>(rc.B[k]);
   }
   g.lda = rc.K;
+  g.a_rows = rc.M;
   g.ldb = rc.bl == B_KN ? rc.N : rc.K;
   g.dst = rc.P;
   g.dst_shard_stride = (int64_t)rc.M * rc.N;
@@ -541,6 +542,7 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
   g.A[0] = reinterpret_cast<const __bf16*>(X_gathered);
   g.B[0] = reinterpret_cast<const __bf16*>(W);
   g.lda = Ki;
+  g.a_rows = Mi;
   g.ldb = Ni;
   g.dst = Y;
   g.dst_shard_stride = 0;
@@ -648,6 +650,46 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
     }
   }
   return fail(TPF_ERR_INVALID_ARG, "unknown scheduler");
+}
+
+int tpf_weight_grad(tpf_handle h, int p, int64_t M, int64_t R, int64_t C, const void* const* A,
+                    const void* const* B, void* const* dW, int dw_dtype, void* stream) {
+  if (p < 1 || p > kMaxShards) return fail(TPF_ERR_SHAPE, "p must be in [1, " + std::to_string(kMaxShards) + "]");
+  if (M <= 0 || R <= 0 || C <= 0) return fail(TPF_ERR_SHAPE, "M, R and C must be positive");
+  if (M > INT32_MAX || R > INT32_MAX || C > INT32_MAX) return fail(TPF_ERR_SHAPE, "M, R and C must fit in 31 bits");
+  if (R % 8 != 0 || C % 8 != 0) return fail(TPF_ERR_ALIGNMENT, "R and C must be multiples of 8");
+  const int64_t lim = ((int64_t)1 << 31) - 1;
+  if (M * R * 2 > lim || M * C * 2 > lim || R * C * 4 > lim)
+    return fail(TPF_ERR_UNSUPPORTED, "each operand and each output must be smaller than 2 GiB");
+  if (!valid_dtype(dw_dtype)) return fail(TPF_ERR_INVALID_ARG, "unknown output dtype");
+  int st;
+  if ((st = check_ptrs(A, p, "A"))) return st;
+  if ((st = check_ptrs(B, p, "B"))) return st;
+  if ((st = check_ptrs(const_cast<const void* const*>(dW), p, "dW"))) return st;
+  if ((st = check_handle(h))) return st;
+  if ((st = set_device(h))) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // dW[k] [R, C] = A[k]^T B[k]: output rows index A's columns, the contraction
+  // runs over the M rows of both operands (A stored [M][R]: transposed-A
+  // tiles; B stored [M][C]: KN tiles).
+  GemmOperands g{};
+  for (int k = 0; k < p; ++k) {
+    g.A[k] = reinterpret_cast<const __bf16*>(A[k]);
+    g.B[k] = reinterpret_cast<const __bf16*>(B[k]);
+    g.dstv[k] = dW[k];
+  }
+  g.lda = R;
+  g.a_rows = (int)M;
+  g.ldb = C;
+  g.b_rows = (int)M;
+  g.ldd = C;
+  g.dst_dtype = out_kind(dw_dtype);
+  g.M = (int)R;
+  g.N = (int)C;
+  g.K = (int)M;
+  g.nshard = p;
+  TPF_TIMED(h, s, launch_gemm_rows(CFG_LARGE, A_KM | B_KN, g, 0, (int)R, s));
+  return TPF_OK;
 }
 
 int tpf_sync_status(tpf_handle h, void* stream) {

@@ -14,7 +14,12 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-enum BLayout : int { B_KN = 0, B_NK = 1 };
+// Operand layouts of a GEMM tile, as one template parameter: bit 0 is the B
+// layout (B_KN: B stored [K][N]; B_NK: [N][K]); bit 1 (A_KM) stores A as
+// [K][M] (the contraction index runs down the rows) instead of [M][K].
+enum BLayout : int { B_KN = 0, B_NK = 1, A_KM = 2 };
+constexpr int b_layout(int L) { return L & 1; }
+constexpr bool a_trans(int L) { return (L & A_KM) != 0; }
 enum OutKind : int { OUT_F32 = 1, OUT_BF16 = 0 };
 
 // Round-to-nearest-even binary32 -> bfloat16 (NaN stays a quiet NaN).

@@ -1,7 +1,8 @@
 // bf16 matrix-core GEMM tile for gfx950.
 //
 // A workgroup of NW wave64s (arranged WAVES_M x WAVES_N) computes a BM x BN
-// block of C = A B in fp32, with A row-major [M][K] and B either row-major
+// block of C = A B in fp32, with A row-major [M][K] (or [K][M], "KM": an
+// activation used transposed, as in dW = X^T dY) and B either row-major
 // [K][N] ("KN": a forward weight W_k) or row-major [N][K] ("NK": a weight
 // used transposed, as in dX = dY W^T).
 //
@@ -25,7 +26,8 @@
 //    values B[k0..k0+3][n0+i]: two such reads give the eight consecutive k of
 //    one column that the MFMA B operand needs.  32-byte blocks are
 //    XOR-swizzled by k so that the four rows of a read land in distinct banks.
-//  * NK B tiles are stored like A.
+//  * NK B tiles are stored like A.  KM A tiles are stored and read like KN B
+//    tiles (the A and B operands of the MFMA have the same lane layout).
 //
 // Every output element is accumulated by the same sequence of MFMAs in
 // increasing k whatever the tile shape, origin or number of valid rows, so the
@@ -84,6 +86,9 @@ struct TileCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert((STAGES - 2) * LOADS_PER_WAVE + TOUCH_PER_WAVE <= 63, "vmcnt range");
   static_assert(L2PF == 0 || (BK == 64 && BM % 64 == 0 && !PP), "line touches: 128-byte A rows, A/B split on a wave");
+  // A stored [K][M] (transposed A) uses the KN-style layout: rows of BM
+  // elements that tile 1 KiB.
+  static constexpr bool KM_OK = BM >= 128 && (BM * 2) % 256 == 0 && 1024 % (BM * 2 > 1024 ? 1024 : BM * 2) == 0;
 };
 
 // Operand description of one tile job.
@@ -172,14 +177,30 @@ struct TileLoader {
     lda_bytes = (uint32_t)(j.lda * 2);
     ra = make_rsrc(j.A, (int64_t)j.a_rows * j.lda * 2);
     rb = make_rsrc(j.B, (int64_t)j.b_rows * j.ldb * 2);
+    if constexpr (a_trans(BL)) {
+      // A stored [K][M]: the tile is 64 rows of k, each BM elements of m.
+      static_assert(Cfg::KM_OK && Cfg::L2PF == 0, "transposed A needs BM-wide rows tiling 1 KiB, no touch");
+      constexpr int ROW_BYTES = Cfg::BM * 2;
 #pragma unroll
-    for (int i = 0; i < Cfg::A_PER_WAVE; ++i) {
-      const int row = (wave * Cfg::A_PER_WAVE + i) * (1024 / Cfg::RB) + lane / Cfg::KCH;
-      const int kc = (lane % Cfg::KCH) ^ swz_row<Cfg>(row);
-      const int gm = j.m0 + row;
-      a_off[i] = gm < j.a_rows ? (uint32_t)(((int64_t)gm * j.lda + kc * 8) * 2) : kOOB;
+      for (int i = 0; i < Cfg::A_PER_WAVE; ++i) {
+        const int byte = (wave * Cfg::A_PER_WAVE + i) * 1024 + lane * 16;
+        const int k = byte / ROW_BYTES;
+        const int pchunk = (byte % ROW_BYTES) / 16;
+        const int cblk = (pchunk >> 1) ^ (Cfg::SWB * (k & 3));
+        const int c = cblk * 2 + (pchunk & 1);           // logical 16-byte chunk: m = 8c
+        const int gm = j.m0 + c * 8;
+        a_off[i] = c * 8 < j.rows ? (uint32_t)(((int64_t)k * j.lda + gm) * 2) : kOOB;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < Cfg::A_PER_WAVE; ++i) {
+        const int row = (wave * Cfg::A_PER_WAVE + i) * (1024 / Cfg::RB) + lane / Cfg::KCH;
+        const int kc = (lane % Cfg::KCH) ^ swz_row<Cfg>(row);
+        const int gm = j.m0 + row;
+        a_off[i] = gm < j.a_rows ? (uint32_t)(((int64_t)gm * j.lda + kc * 8) * 2) : kOOB;
+      }
     }
-    if constexpr (BL == B_NK) {
+    if constexpr (b_layout(BL) == B_NK) {
 #pragma unroll
       for (int i = 0; i < Cfg::B_PER_WAVE; ++i) {
         const int row = (wave * Cfg::B_PER_WAVE + i) * (1024 / Cfg::RB) + lane / Cfg::KCH;
@@ -211,7 +232,7 @@ struct TileLoader {
       } else if (line < Cfg::TOUCH_LINES) {
         const int bl = line - Cfg::BM;
         isb = 1;
-        if constexpr (BL == B_NK) {               // B row n, 64 k = 128 bytes
+        if constexpr (b_layout(BL) == B_NK) {     // B row n, 64 k = 128 bytes
           const int gn = j.n0 + bl;
           if (gn < j.b_rows) off = (uint32_t)((int64_t)gn * j.ldb * 2);
         } else {                                  // B row k, segment of 64 n
@@ -233,7 +254,7 @@ struct TileLoader {
     for (int i = 0; i < Cfg::TOUCH_PER_WAVE; ++i) {
       uint32_t off = t_off[i];
       if (off != kOOB) {
-        if (t_isb[i] && BL == B_KN)
+        if (t_isb[i] && b_layout(BL) == B_KN)
           off += (uint32_t)k0 * ldb_bytes;
         else
           off += (uint32_t)k0 * 2;
@@ -261,12 +282,16 @@ struct TileLoader {
   // Logical k chunk (A, NK B) of this lane's i-th A or B load, or (KN B) its
   // k row within the step.  Only the K tail step needs them, so they are
   // recomputed there instead of being kept in registers.
-  __device__ __forceinline__ static int a_kchunk(int wave, int lane, int i) {
-    const int row = (wave * Cfg::A_PER_WAVE + i) * (1024 / Cfg::RB) + lane / Cfg::KCH;
-    return (lane % Cfg::KCH) ^ swz_row<Cfg>(row);
+  __device__ __forceinline__ static int a_kpos(int wave, int lane, int i) {
+    if constexpr (a_trans(BL)) {
+      return ((wave * Cfg::A_PER_WAVE + i) * 1024 + lane * 16) / (Cfg::BM * 2);
+    } else {
+      const int row = (wave * Cfg::A_PER_WAVE + i) * (1024 / Cfg::RB) + lane / Cfg::KCH;
+      return ((lane % Cfg::KCH) ^ swz_row<Cfg>(row)) * 8;
+    }
   }
   __device__ __forceinline__ static int b_kpos(int wave, int lane, int i) {
-    if constexpr (BL == B_NK) {
+    if constexpr (b_layout(BL) == B_NK) {
       const int row = (wave * Cfg::B_PER_WAVE + i) * (1024 / Cfg::RB) + lane / Cfg::KCH;
       return ((lane % Cfg::KCH) ^ swz_row<Cfg>(row)) * 8;
     } else {
@@ -287,15 +312,16 @@ struct TileLoader {
     if (tail) asm volatile("" : "+v"(tl));
 #pragma unroll
     for (int i = 0; i < Cfg::A_PER_WAVE; ++i) {
-      uint32_t off = a_off[i] != kOOB ? a_off[i] + (uint32_t)k0 * 2 : kOOB;
-      if (tail && k0 + a_kchunk(wave, tl, i) * 8 >= K) off = kOOB;
+      // MK: k runs along the row; KM: the tile's row k is operand row k0 + k
+      uint32_t off = a_off[i] != kOOB ? a_off[i] + (uint32_t)k0 * (a_trans(BL) ? lda_bytes : 2u) : kOOB;
+      if (tail && k0 + a_kpos(wave, tl, i) >= K) off = kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(la + (wave * Cfg::A_PER_WAVE + i) * 1024), 16,
                                                off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < Cfg::B_PER_WAVE; ++i) {
       // NK: k runs along the row; KN: the tile's row k is operand row k0 + k
-      uint32_t off = b_off[i] != kOOB ? b_off[i] + (uint32_t)k0 * (BL == B_NK ? 2u : ldb_bytes) : kOOB;
+      uint32_t off = b_off[i] != kOOB ? b_off[i] + (uint32_t)k0 * (b_layout(BL) == B_NK ? 2u : ldb_bytes) : kOOB;
       if (tail && k0 + b_kpos(wave, tl, i) >= K) off = kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(lb + (wave * Cfg::B_PER_WAVE + i) * 1024), 16,
                                                off, 0, 0, 0);
@@ -316,12 +342,32 @@ __device__ __forceinline__ void read_operands(Operands<Cfg>& o, const char* stag
   const char* lb = stage + Cfg::LDS_A;
   const int r32 = lane & 31, half = lane >> 5;
   const int kc = s * 2 + half;
+  if constexpr (a_trans(BL)) {
+    // [64 k][BM m] tile, read with transposes exactly like a KN B tile
+    constexpr int ROW_BYTES = Cfg::BM * 2;
+    const int g = lane >> 4, jl = lane & 15;
+    const int r = jl >> 2, q = jl & 3;
+    const int k = s * 16 + (g >> 1) * 8 + r;
 #pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i) {
-    const int m = wm * Cfg::WM + i * 32 + r32;
-    o.a[i] = *reinterpret_cast<const bf16x8_t*>(la + m * Cfg::RB + ((kc ^ swz_row<Cfg>(m)) * 16));
+    for (int i = 0; i < Cfg::TM; ++i) {
+      const int m = wm * Cfg::WM + i * 32 + (g & 1) * 16 + q * 4;
+      const int c = m >> 3;
+      const int pblk = (c >> 1) ^ (Cfg::SWB * (k & 3));
+      const int off = (pblk * 2 + (c & 1)) * 16 + (q & 1) * 8;
+      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(
+          (lds_void_t*)(la + k * ROW_BYTES + off)));
+      const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(
+          (lds_void_t*)(la + (k + 4) * ROW_BYTES + off)));
+      o.a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i) {
+      const int m = wm * Cfg::WM + i * 32 + r32;
+      o.a[i] = *reinterpret_cast<const bf16x8_t*>(la + m * Cfg::RB + ((kc ^ swz_row<Cfg>(m)) * 16));
+    }
   }
-  if constexpr (BL == B_NK) {
+  if constexpr (b_layout(BL) == B_NK) {
 #pragma unroll
     for (int jn = 0; jn < Cfg::TN; ++jn) {
       const int n = wn * Cfg::WN + jn * 32 + r32;

@@ -39,7 +39,9 @@ struct GemmOperands {
   const __bf16* A[kMaxShards];
   const __bf16* B[kMaxShards];
   int64_t lda, ldb;
+  int a_rows;                 // rows of each A operand as stored (M, or K for A stored [K][M])
   void* dst;                  // fp32 partials (reducing ops) or the output (AllGather->MatMul)
+  void* dstv[kMaxShards];     // if dstv[0] is set: shard k's output at dstv[k] (weight gradients)
   int64_t dst_shard_stride;   // elements
   int64_t ldd;
   int dst_dtype;              // OUT_F32 or OUT_BF16
@@ -128,7 +130,10 @@ enum CfgId : int { CFG_LARGE = 0, CFG_SMALL = 1 };
 #define TPF_LARGE_BK 64
 #endif
 #ifndef TPF_LARGE_L2PF
-#define TPF_LARGE_L2PF 1
+#define TPF_LARGE_L2PF 0
+#endif
+#ifndef TPF_FUSED_L2PF
+#define TPF_FUSED_L2PF 1
 #endif
 #ifndef TPF_LARGE_PP
 #define TPF_LARGE_PP 0
@@ -148,14 +153,22 @@ enum CfgId : int { CFG_LARGE = 0, CFG_SMALL = 1 };
 #ifndef TPF_LARGE_BN
 #define TPF_LARGE_BN 256
 #endif
+// The one-tile-per-workgroup kernels run without the L2 line touch (measured
+// 1-2 % faster under sustained load); the persistent kernel, whose
+// workgroups move between chunks and re-stream weights, keeps it (measured
+// 30 % faster with it).  The touch moves no data into registers, so both
+// compute the same bits.
 using CfgLarge = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN, TPF_LARGE_STAGES, TPF_LARGE_BK,
                          TPF_LARGE_L2PF, TPF_LARGE_PP, TPF_LARGE_PPMODE>;
+using CfgLargeFused = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN, TPF_LARGE_STAGES,
+                              TPF_LARGE_BK, TPF_FUSED_L2PF, TPF_LARGE_PP, TPF_LARGE_PPMODE>;
 using CfgSmall = TileCfg<32, 128, 1, 4, 4, 64, 0>;    // decode-shaped rows, 4 stages of 20 KiB
 
 int cfg_bm(int cfg);
 int cfg_bn(int cfg);
 
-// Shard GEMM tiles of rows [row0, row1) into g.dst (no reduction).
+// Shard GEMM tiles of rows [row0, row1) into g.dst (no reduction).  bl may
+// include A_KM (transposed A) for the large tile configuration only.
 hipError_t launch_gemm_rows(int cfg, int bl, const GemmOperands& g, int row0, int row1, hipStream_t s);
 hipError_t launch_reduce_rows(const void* P, int64_t stride, int p, int row0, int row1, int N,
                               const ReduceOut& o, int num_cus, hipStream_t s);

@@ -43,10 +43,12 @@ int cfg_bn(int cfg) { return cfg == CFG_SMALL ? CfgSmall::BN : CfgLarge::BN; }
 template <class Cfg>
 __device__ __forceinline__ void store_any(const Frag<Cfg>& f, const TileJob& j, const GemmOperands& g, int shard) {
   if (g.dst_dtype == OUT_F32) {
-    float* d = reinterpret_cast<float*>(g.dst) + (int64_t)shard * g.dst_shard_stride;
+    float* d = g.dstv[0] ? reinterpret_cast<float*>(g.dstv[shard])
+                         : reinterpret_cast<float*>(g.dst) + (int64_t)shard * g.dst_shard_stride;
     store_tile<Cfg, OUT_F32>(f, j, d, g.ldd);
   } else {
-    uint16_t* d = reinterpret_cast<uint16_t*>(g.dst) + (int64_t)shard * g.dst_shard_stride;
+    uint16_t* d = g.dstv[0] ? reinterpret_cast<uint16_t*>(g.dstv[shard])
+                            : reinterpret_cast<uint16_t*>(g.dst) + (int64_t)shard * g.dst_shard_stride;
     store_tile<Cfg, OUT_BF16>(f, j, d, g.ldd);
   }
 }
@@ -58,7 +60,7 @@ __device__ __forceinline__ TileJob make_job(const GemmOperands& g, int shard, in
   j.B = g.B[shard];
   j.lda = g.lda;
   j.ldb = g.ldb;
-  j.a_rows = g.M;
+  j.a_rows = g.a_rows;
   j.b_rows = g.b_rows;
   j.m0 = row0 + tm * Cfg::BM;
   j.rows = min(Cfg::BM, row1 - j.m0);
@@ -450,7 +452,7 @@ static int fused_blocks_per_cu() {
 
 int fused_occupancy(int cfg, int bl) {
   if (cfg == CFG_SMALL) return bl == B_KN ? fused_blocks_per_cu<CfgSmall, B_KN>() : fused_blocks_per_cu<CfgSmall, B_NK>();
-  return bl == B_KN ? fused_blocks_per_cu<CfgLarge, B_KN>() : fused_blocks_per_cu<CfgLarge, B_NK>();
+  return bl == B_KN ? fused_blocks_per_cu<CfgLargeFused, B_KN>() : fused_blocks_per_cu<CfgLargeFused, B_NK>();
 }
 
 hipError_t launch_fused(int cfg, int bl, const FusedArgs& a, int grid, hipStream_t s) {
@@ -461,15 +463,21 @@ hipError_t launch_fused(int cfg, int bl, const FusedArgs& a, int grid, hipStream
       hipLaunchKernelGGL((fused_kernel<CfgSmall, B_NK>), dim3(grid), dim3(CfgSmall::THREADS), 0, s, a);
   } else {
     if (bl == B_KN)
-      hipLaunchKernelGGL((fused_kernel<CfgLarge, B_KN>), dim3(grid), dim3(CfgLarge::THREADS), 0, s, a);
+      hipLaunchKernelGGL((fused_kernel<CfgLargeFused, B_KN>), dim3(grid), dim3(CfgLargeFused::THREADS), 0, s, a);
     else
-      hipLaunchKernelGGL((fused_kernel<CfgLarge, B_NK>), dim3(grid), dim3(CfgLarge::THREADS), 0, s, a);
+      hipLaunchKernelGGL((fused_kernel<CfgLargeFused, B_NK>), dim3(grid), dim3(CfgLargeFused::THREADS), 0, s, a);
   }
   return hipGetLastError();
 }
 
 template <class Cfg, int RED>
 static void launch_tile_cfg(int bl, const TileArgs& a, int grid, hipStream_t s) {
+  if constexpr (Cfg::KM_OK && RED == 0) {
+    if (bl == (A_KM | B_KN)) {
+      hipLaunchKernelGGL((tile_kernel<Cfg, A_KM | B_KN, 0>), dim3(grid), dim3(Cfg::THREADS), 0, s, a);
+      return;
+    }
+  }
   if (bl == B_KN)
     hipLaunchKernelGGL((tile_kernel<Cfg, B_KN, RED>), dim3(grid), dim3(Cfg::THREADS), 0, s, a);
   else

@@ -22,6 +22,10 @@ tensor-parallel Linear it stands for:
   layer: dY_k [2048,6144] N(0,1), W_k [12288,6144] N(0,0.02), 8 chunks.
 * ``decode16`` / ``decode64`` – decode-shaped row-parallel GEMMs, p=8:
   X_k [M,1024], W_k [1024,8192], both N(0,0.02), chunk counts 1/2/4.
+* ``dw_col`` – the weight gradient of the ``ag_fwd`` column shard layer,
+  dW_k = X^T dY_k: gathered X [2048,12288], dY_k [2048,6144], both N(0,1).
+* ``dw_row`` – the weight gradient of the ``mlp_down`` row-parallel layer,
+  dW_k = X_k^T dY: X_k [4096,4096], dY [4096,4096], both N(0,1).
 
 ``N(0, s)`` is read as standard deviation ``s``.
 
@@ -69,6 +73,9 @@ class Workload:
         """Algorithmic multiply-add FLOPs of the whole op (2 per MAC)."""
         if self.op == "allgather":
             return 2.0 * self.M * self.K * self.N
+        if self.op in ("wgrad_col", "wgrad_row"):
+            # p GEMMs dW_k [K, N] = A_k^T B_k over M rows
+            return 2.0 * self.M * self.K * self.N * self.p
         if self.op == "dx":
             # dX [M, K] = sum over p shards of dY_k [M, N] . W_k^T
             return 2.0 * self.M * self.N * self.K * self.p
@@ -102,6 +109,12 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("decode64", "allreduce", 8, 64, 8192, 1024, (1, 2, 4),
                  ("normal", 0.02), ("normal", 0.02), index=6,
                  note="decode step, 64 tokens"),
+        Workload("dw_col", "wgrad_col", 8, 2048, 6144, 12288, (1,),
+                 ("normal", 1.0), ("normal", 1.0), index=7, out_dtypes=("f32",),
+                 note="column-parallel weight gradient dW_k = X^T dY_k of the GPT-3 FC1 shard"),
+        Workload("dw_row", "wgrad_row", 4, 4096, 4096, 4096, (1,),
+                 ("normal", 1.0), ("normal", 1.0), index=8, out_dtypes=("f32",),
+                 note="row-parallel weight gradient dW_k = X_k^T dY of the MLP down projection"),
     ]
 }
 
@@ -161,6 +174,8 @@ def make_inputs(wl: Workload, seed: int = 0, mode: str = "random", device: str =
       allreduce / reducescatter: X[k] [M, K], W[k] [K, N]     (k < p)
       allgather:                 X[r] [M/p, K] (slices), W[0] [K, N]
       dx:                        X[k] = dY_k [M, N], W[k] [K, N]  (K = K_in, N = N_shard)
+      wgrad_col:                 X[0] = gathered input [M, K], W[k] = dY_k [M, N]
+      wgrad_row:                 X[k] = X_k [M, K], W[0] = dY [M, N]
     """
     M = wl.M if M is None else M
     N = wl.N if N is None else N
@@ -182,9 +197,24 @@ def make_inputs(wl: Workload, seed: int = 0, mode: str = "random", device: str =
         for k in range(p):
             inp.X.append(draw((M, N), wl.x_dist, tensor_seed(idx, "dY", k, seed), mode, device))
             inp.W.append(draw((K, N), wl.w_dist, tensor_seed(idx, "W", k, seed), mode, device))
+    elif wl.op == "wgrad_col":
+        inp.X.append(draw((M, K), wl.x_dist, tensor_seed(idx, "X", 0, seed), mode, device))
+        for k in range(p):
+            inp.W.append(draw((M, N), wl.w_dist, tensor_seed(idx, "dY", k, seed), mode, device))
+    elif wl.op == "wgrad_row":
+        for k in range(p):
+            inp.X.append(draw((M, K), wl.x_dist, tensor_seed(idx, "X", k, seed), mode, device))
+        inp.W.append(draw((M, N), wl.w_dist, tensor_seed(idx, "dY", 0, seed), mode, device))
     else:
         raise ValueError(f"unknown op {wl.op!r}")
     return inp
+
+
+def weight_grad_operands(inp: Inputs):
+    """The per-shard (A, B) lists of a weight-gradient workload: dW_k = A_k^T B_k."""
+    if inp.workload.op == "wgrad_col":
+        return [inp.X[0]] * inp.p, list(inp.W)
+    return list(inp.X), [inp.W[0]] * inp.p
 
 
 def bf16_to_bits(t: torch.Tensor):

@@ -45,6 +45,7 @@ SIGNATURES = {
     "tpf_matmul_reducescatter": (_I, [_VP, _I, _I64, _I64, _I64, _PP, _PP, _PP, _I, _I, _I, _VP, _SZ, _VP]),
     "tpf_allgather_matmul": (_I, [_VP, _I, _I64, _I64, _I64, _PP, _VP, _VP, _VP, _I, _I, _I, _VP, _SZ, _VP]),
     "tpf_matmul_dx": (_I, [_VP, _I, _I, _I64, _I64, _I64, _PP, _PP, _PP, _I, _I, _I, _VP, _SZ, _VP]),
+    "tpf_weight_grad": (_I, [_VP, _I, _I64, _I64, _I64, _PP, _PP, _PP, _I, _VP]),
     "tpf_sync_status": (_I, [_VP, _VP]),
     "tpf_debug_set_wait": (_I, [_VP, _I64, _I]),
     "tpf_debug_set_timeline": (_I, [_VP, _VP, _I]),
@@ -282,3 +283,22 @@ def matmul_dx(dY: List[torch.Tensor], W: List[torch.Tensor], semantic: int = ALL
                                _dtype_code(outs[0].dtype), n_chunks, _sched(sched, message),
                                ws.data_ptr() if ws is not None else None, ws_bytes, _stream_ptr(stream)))
     return dX
+
+
+def weight_grad(A: List[torch.Tensor], B: List[torch.Tensor], out_dtype=torch.float32, dW=None,
+                handle: Optional[Handle] = None, stream=None) -> List[torch.Tensor]:
+    """dW[k] = A[k]^T @ B[k] for every shard k (A[k] [M, R], B[k] [M, C]).
+
+    Row-parallel: A = X_k per shard, B = [dY] * p.  Column-parallel:
+    A = [X_gathered] * p, B = dY_k per shard."""
+    p = len(A)
+    M, R = A[0].shape
+    C = B[0].shape[1]
+    dev = A[0].device
+    if dW is None:
+        dW = [torch.empty((R, C), dtype=out_dtype, device=dev) for _ in range(p)]
+    h = handle or default_handle(dev.index)
+    check(load().tpf_weight_grad(h.ptr, p, M, R, C, ptr_array([a.data_ptr() for a in A]),
+                                 ptr_array([b.data_ptr() for b in B]), ptr_array([d.data_ptr() for d in dW]),
+                                 _dtype_code(dW[0].dtype), _stream_ptr(stream)))
+    return dW

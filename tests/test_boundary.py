@@ -169,6 +169,25 @@ def test_dx_checks():
                              None) == tp.ERR_WORKSPACE
 
 
+def test_weight_grad_checks():
+    lib = tp.load()
+    P2 = tp.ptr_array([A16] * 2)
+
+    def call(p=2, M=64, R=64, C=64, A=P2, B=P2, D=P2, dtype=tp.F32):
+        return lib.tpf_weight_grad(None, p, M, R, C, A, B, D, dtype, None)
+    assert call(p=0) == tp.ERR_SHAPE
+    assert call(M=0) == tp.ERR_SHAPE
+    assert call(R=12) == tp.ERR_ALIGNMENT
+    assert call(C=20) == tp.ERR_ALIGNMENT
+    assert call(dtype=5) == tp.ERR_INVALID_ARG
+    assert call(A=None) == tp.ERR_INVALID_ARG
+    assert call(B=tp.ptr_array([A16, MIS])) == tp.ERR_ALIGNMENT
+    assert call(D=tp.ptr_array([A16, 0])) == tp.ERR_INVALID_ARG
+    assert call(M=1 << 20, R=1 << 12) == tp.ERR_UNSUPPORTED       # 8 GiB operand
+    assert call() == tp.ERR_INVALID_ARG                             # all valid: the NULL handle
+    assert "handle" in _err(None)
+
+
 def test_handle_calls_reject_null():
     lib = tp.load()
     assert lib.tpf_sync_status(None, None) == tp.ERR_INVALID_ARG

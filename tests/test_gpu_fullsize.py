@@ -53,7 +53,11 @@ def oracle_rows(wl, inp, rows):
     return xg @ O.bf16_bits_to_f64(bits(inp.W)[0])
 
 
-@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+REDUCING = [n for n, w in inputs.WORKLOADS.items() if not w.op.startswith("wgrad")]
+WGRAD = [n for n, w in inputs.WORKLOADS.items() if w.op.startswith("wgrad")]
+
+
+@pytest.mark.parametrize("name", REDUCING)
 def test_fullsize_parity(name):
     wl = inputs.WORKLOADS[name]
     n = wl.default_chunks
@@ -77,6 +81,30 @@ def test_fullsize_parity(name):
             y = run(wl, inp, torch.bfloat16, m, sched)
             torch.cuda.synchronize()
             assert_bitwise(y, y16, f"{name}: {sched} n={m} vs auto n={n}")
+
+
+@pytest.mark.parametrize("name", WGRAD)
+def test_fullsize_weight_grad(name):
+    """Weight gradients at full size: sampled rows of every dW_k against the
+    oracle (row i of A_k^T B_k is column i of A_k against B_k), bf16 output
+    equal to the RNE rounding of the fp32 output."""
+    wl = inputs.WORKLOADS[name]
+    say(f"full-size {name}: p={wl.p} M={wl.M} R={wl.K} C={wl.N}")
+    inp = inputs.make_inputs(wl, seed=0, device="cuda")
+    A, B = inputs.weight_grad_operands(inp)
+    d32 = tp.weight_grad(A, B, torch.float32)
+    d16 = tp.weight_grad(A, B, torch.bfloat16)
+    torch.cuda.synchronize()
+    R = wl.K
+    rows = sorted({0, 1, 255, 256, R // 2, R - 1} | {int(r) for r in np.random.default_rng(9).integers(0, R, 6)})
+    idx = torch.as_tensor(rows, device="cuda")
+    for k in range(wl.p):
+        a = inputs.bf16_to_bits(A[k].index_select(1, idx))              # [M, rows]
+        ref = O.weight_grad([a], [inputs.bf16_to_bits(B[k])])[0]         # [rows, C]
+        what = f"{name} dW_{k} rows={len(rows)}"
+        assert_f32(d32[k].index_select(0, idx), ref, what)
+        assert_bf16(d16[k].index_select(0, idx), ref, what)
+        assert_bf16_is_rne_of_f32(d16[k], d32[k], what)
 
 
 def test_fullsize_reducescatter_equals_allreduce_rows():

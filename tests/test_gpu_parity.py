@@ -269,6 +269,48 @@ def test_message_bf16_reducescatter_and_dx():
 
 
 # ---------------------------------------------------------------------------
+# Weight gradients
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind,p,M,R,C", [
+    ("row", 3, 200, 264, 328),     # ragged in every dimension (K tail: 200 = 3*64 + 8)
+    ("col", 2, 1000, 520, 136),
+    ("col", 8, 64, 256, 1032),     # one K step
+    ("row", 1, 37, 8, 8),          # a single partial tile
+])
+def test_weight_grad_parity(kind, p, M, R, C):
+    say(f"weight grad {kind} p={p} M={M} R={R} C={C}")
+    if kind == "row":    # A_k = X_k per shard, B = dY shared
+        Ah = shards([(M, R)] * p, ("normal", 1.0), 91)
+        Bh = [inputs.draw((M, C), ("normal", 1.0), 92000)] * p
+    else:                # A = gathered X shared, B_k = dY_k per shard
+        Ah = [inputs.draw((M, R), ("normal", 1.0), 93000)] * p
+        Bh = shards([(M, C)] * p, ("normal", 1.0), 94)
+    refs = O.weight_grad(bits(Ah), bits(Bh))
+    A, B = gpu(Ah), gpu(Bh)
+    d32 = tp.weight_grad(A, B, torch.float32)
+    d16 = tp.weight_grad(A, B, torch.bfloat16)
+    torch.cuda.synchronize()
+    for k in range(p):
+        what = f"dW {kind} shard {k}"
+        assert_f32(d32[k], refs[k], what)
+        assert_bf16(d16[k], refs[k], what)
+        assert_bf16_is_rne_of_f32(d16[k], d32[k], what)
+
+
+def test_weight_grad_integer_exact():
+    p, M, R, C = 2, 300, 136, 264
+    rng = np.random.default_rng(95)
+    Ah = [torch.from_numpy(rng.integers(-2, 3, (M, R)).astype(np.float32)).to(torch.bfloat16) for _ in range(p)]
+    Bh = [torch.from_numpy(rng.integers(-2, 3, (M, C)).astype(np.float32)).to(torch.bfloat16) for _ in range(p)]
+    refs = O.weight_grad(bits(Ah), bits(Bh))
+    d = tp.weight_grad(gpu(Ah), gpu(Bh), torch.float32)
+    torch.cuda.synchronize()
+    for k in range(p):
+        assert np.array_equal(d[k].cpu().double().numpy(), refs[k]), k
+
+
+# ---------------------------------------------------------------------------
 # MatMul -> ReduceScatter
 # ---------------------------------------------------------------------------
 

@@ -304,11 +304,46 @@ def pin_message_bf16_dx(o):
     return np.array_equal(o.matmul_dx_msg_bf16(dY, W), o.matmul_allreduce_msg_bf16(dY, Wt))
 
 
+def pin_weight_grad_golden(o):
+    g = _load("tiny_tp_example.json")["weight_grad"]
+    c = g["column"]
+    got = o.weight_grad([_bits(c["X"])] * 2, [_bits(d) for d in c["dY"]])
+    if not all(np.array_equal(a, e) for a, e in zip(got, c["dW"])):
+        return False
+    r = g["row"]
+    got = o.weight_grad([_bits(x) for x in r["X_shards"]], [_bits(r["dY"])] * 2)
+    return all(np.array_equal(a, e) for a, e in zip(got, r["dW"]))
+
+
+def pin_weight_grad_autograd(o):
+    """torch float64 autograd of the row- and column-parallel forwards."""
+    rng = np.random.default_rng(8)
+    p, M, K, N = 3, 5, 4, 6
+    X = [_bits(rng.standard_normal((M, K))) for _ in range(p)]
+    W = [_bits(rng.standard_normal((K, N))) for _ in range(p)]
+    G = _bits(rng.standard_normal((M, N)))
+    Wt = [torch.tensor(O.bf16_bits_to_f64(w), requires_grad=True) for w in W]
+    Y = sum(torch.tensor(O.bf16_bits_to_f64(x)) @ w for x, w in zip(X, Wt))
+    (Y * torch.tensor(O.bf16_bits_to_f64(G))).sum().backward()
+    row = o.weight_grad(X, [G] * p)
+    if not all(np.allclose(r, w.grad.numpy(), rtol=1e-12, atol=1e-12) for r, w in zip(row, Wt)):
+        return False
+    # column-parallel: Y_k = X W_k, upstream gradient G_k per shard
+    Xg = _bits(rng.standard_normal((M, K)))
+    Gk = [_bits(rng.standard_normal((M, N))) for _ in range(p)]
+    Wt = [torch.tensor(O.bf16_bits_to_f64(w), requires_grad=True) for w in W]
+    loss = sum(((torch.tensor(O.bf16_bits_to_f64(Xg)) @ w) * torch.tensor(O.bf16_bits_to_f64(g))).sum()
+               for w, g in zip(Wt, Gk))
+    loss.backward()
+    col = o.weight_grad([Xg] * p, Gk)
+    return all(np.allclose(c, w.grad.numpy(), rtol=1e-12, atol=1e-12) for c, w in zip(col, Wt))
+
+
 PINS = [pin_tiny_row_parallel, pin_tiny_reducescatter, pin_tiny_column_backward, pin_tiny_allgather,
         pin_worked_example, pin_brute_force_unsharded, pin_brute_force_dx, pin_dx_autograd,
         pin_column_identity, pin_chunked_equals_whole, pin_rs_slices, pin_chunk_bounds,
         pin_round_bf16, pin_message_bf16_golden, pin_message_bf16_integer_exact,
-        pin_message_bf16_error_bound, pin_message_bf16_dx]
+        pin_message_bf16_error_bound, pin_message_bf16_dx, pin_weight_grad_golden, pin_weight_grad_autograd]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -452,9 +487,20 @@ def _m_message_fold_reversed():
     return _msg_mutant(fold=lambda ms: O.sum_messages_f32(list(ms)[::-1]))
 
 
+def _m_weight_grad_swapped():
+    # the operands' roles swapped: B_k^T A_k (the transposed gradient)
+    return _Mutant(weight_grad=lambda A, B: [O.bf16_bits_to_f64(b).T @ O.bf16_bits_to_f64(a) for a, b in zip(A, B)])
+
+
+def _m_weight_grad_shard_shift():
+    # shard k paired with the next shard's B
+    return _Mutant(weight_grad=lambda A, B: O.weight_grad(A, list(B[1:]) + list(B[:1])))
+
+
 MUTANTS = [_m_dropped_shard, _m_sign, _m_dx_untransposed, _m_slices_reversed, _m_gather_reversed,
            _m_round_truncate, _m_round_via_f32, _m_chunk_lastshort, _m_pipeline_serial,
-           _m_message_truncated, _m_message_unrounded, _m_message_fold_f64, _m_message_fold_reversed]
+           _m_message_truncated, _m_message_unrounded, _m_message_fold_f64, _m_message_fold_reversed,
+           _m_weight_grad_swapped, _m_weight_grad_shard_shift]
 
 
 @pytest.mark.parametrize("mut", MUTANTS, ids=[m.__name__ for m in MUTANTS])
