@@ -80,8 +80,10 @@ bool valid_dtype(int d) { return d == TPF_BF16 || d == TPF_F32; }
 
 int out_kind(int dtype) { return dtype == TPF_F32 ? OUT_F32 : OUT_BF16; }
 
-// Tile configuration from the op's total shape only.
-int pick_cfg(int64_t M) { return M <= 64 ? CFG_SMALL : CFG_LARGE; }
+// Tile configuration from the op's total row count only (never from the
+// chunking): every configuration runs the same MFMA sequence per element, so
+// the choice changes speed, not bits.
+int pick_cfg(int64_t M) { return M <= 32 ? CFG_SMALL : M <= 64 ? CFG_MID : CFG_LARGE; }
 
 // Common checks of sizes, chunking, dtype and scheduler.
 int check_common(int p, int64_t M, int64_t N, int64_t K, int n_chunks, int dtype, int sched, bool need_div) {

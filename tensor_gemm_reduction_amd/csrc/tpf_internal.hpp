@@ -122,7 +122,7 @@ static_assert(sizeof(TimelineEvent) == 32, "timeline event layout");
 
 // Tile configurations (chosen from the op's shape only, never from the chunk
 // count, so every chunking runs the same per-element arithmetic).
-enum CfgId : int { CFG_LARGE = 0, CFG_SMALL = 1 };
+enum CfgId : int { CFG_LARGE = 0, CFG_SMALL = 1, CFG_MID = 2 };
 #ifndef TPF_LARGE_STAGES
 #define TPF_LARGE_STAGES 2
 #endif
@@ -162,7 +162,21 @@ using CfgLarge = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN,
                          TPF_LARGE_L2PF, TPF_LARGE_PP, TPF_LARGE_PPMODE>;
 using CfgLargeFused = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN, TPF_LARGE_STAGES,
                               TPF_LARGE_BK, TPF_FUSED_L2PF, TPF_LARGE_PP, TPF_LARGE_PPMODE>;
-using CfgSmall = TileCfg<32, 128, 1, 4, 4, 64, 0>;    // decode-shaped rows, 4 stages of 20 KiB
+#ifndef TPF_SMALL_BM
+#define TPF_SMALL_BM 32
+#endif
+#ifndef TPF_SMALL_BN
+#define TPF_SMALL_BN 128
+#endif
+#ifndef TPF_SMALL_STAGES
+#define TPF_SMALL_STAGES 4
+#endif
+// Decode-shaped row counts (measured on 134 MB of weights, p = 8):
+//   M <= 32:  32 x 128 tiles, 4 stages of 20 KiB, two workgroups per CU;
+//   M <= 64:  64 x 256 tiles, 3 stages of 40 KiB: each weight tile is read by
+//             one workgroup instead of two (47 % -> 61 % of HBM bandwidth at M = 64).
+using CfgSmall = TileCfg<TPF_SMALL_BM, TPF_SMALL_BN, 1, 4, TPF_SMALL_STAGES, 64, 0>;
+using CfgMid = TileCfg<64, 256, 1, 4, 3, 64, 0>;
 
 int cfg_bm(int cfg);
 int cfg_bn(int cfg);

@@ -37,8 +37,8 @@ __device__ __forceinline__ const T& kernarg() {
   return *(const T*)__builtin_amdgcn_kernarg_segment_ptr();
 }
 
-int cfg_bm(int cfg) { return cfg == CFG_SMALL ? CfgSmall::BM : CfgLarge::BM; }
-int cfg_bn(int cfg) { return cfg == CFG_SMALL ? CfgSmall::BN : CfgLarge::BN; }
+int cfg_bm(int cfg) { return cfg == CFG_SMALL ? CfgSmall::BM : cfg == CFG_MID ? CfgMid::BM : CfgLarge::BM; }
+int cfg_bn(int cfg) { return cfg == CFG_SMALL ? CfgSmall::BN : cfg == CFG_MID ? CfgMid::BN : CfgLarge::BN; }
 
 template <class Cfg>
 __device__ __forceinline__ void store_any(const Frag<Cfg>& f, const TileJob& j, const GemmOperands& g, int shard) {
@@ -452,6 +452,7 @@ static int fused_blocks_per_cu() {
 
 int fused_occupancy(int cfg, int bl) {
   if (cfg == CFG_SMALL) return bl == B_KN ? fused_blocks_per_cu<CfgSmall, B_KN>() : fused_blocks_per_cu<CfgSmall, B_NK>();
+  if (cfg == CFG_MID) return bl == B_KN ? fused_blocks_per_cu<CfgMid, B_KN>() : fused_blocks_per_cu<CfgMid, B_NK>();
   return bl == B_KN ? fused_blocks_per_cu<CfgLargeFused, B_KN>() : fused_blocks_per_cu<CfgLargeFused, B_NK>();
 }
 
@@ -461,6 +462,11 @@ hipError_t launch_fused(int cfg, int bl, const FusedArgs& a, int grid, hipStream
       hipLaunchKernelGGL((fused_kernel<CfgSmall, B_KN>), dim3(grid), dim3(CfgSmall::THREADS), 0, s, a);
     else
       hipLaunchKernelGGL((fused_kernel<CfgSmall, B_NK>), dim3(grid), dim3(CfgSmall::THREADS), 0, s, a);
+  } else if (cfg == CFG_MID) {
+    if (bl == B_KN)
+      hipLaunchKernelGGL((fused_kernel<CfgMid, B_KN>), dim3(grid), dim3(CfgMid::THREADS), 0, s, a);
+    else
+      hipLaunchKernelGGL((fused_kernel<CfgMid, B_NK>), dim3(grid), dim3(CfgMid::THREADS), 0, s, a);
   } else {
     if (bl == B_KN)
       hipLaunchKernelGGL((fused_kernel<CfgLargeFused, B_KN>), dim3(grid), dim3(CfgLargeFused::THREADS), 0, s, a);
@@ -490,6 +496,9 @@ hipError_t launch_tiles(int cfg, int bl, int red, const TileArgs& a, hipStream_t
   if (cfg == CFG_SMALL) {
     if (red) launch_tile_cfg<CfgSmall, 1>(bl, a, grid, s);
     else launch_tile_cfg<CfgSmall, 0>(bl, a, grid, s);
+  } else if (cfg == CFG_MID) {
+    if (red) launch_tile_cfg<CfgMid, 1>(bl, a, grid, s);
+    else launch_tile_cfg<CfgMid, 0>(bl, a, grid, s);
   } else {
     if (red) launch_tile_cfg<CfgLarge, 1>(bl, a, grid, s);
     else launch_tile_cfg<CfgLarge, 0>(bl, a, grid, s);
