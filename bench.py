@@ -94,6 +94,7 @@ def main():
     M, N, K, p = wl.M, wl.N, wl.K, wl.p
     flops = wl.flops()
     kbytes = kernel_bytes(wl, 2 if args.message == "bf16" else 4)
+    kflops = flops / 2 if wl.op == "mlp_sp" else flops    # the timed launch of the MLP block is FC2
     msg = args.message
 
     if wl.op in ("allreduce", "reducescatter"):
@@ -121,6 +122,19 @@ def main():
             inp = sets[i % len(sets)]
             tp.matmul_dx(inp.X, inp.W, tp.ALLREDUCE, n_chunks=n, sched=sched, dX=dX, ws=ws, handle=handle,
                          message=msg)
+        ws_bytes = ws.numel()
+    elif wl.op == "mlp_sp":
+        # AllGather -> FC1 + GeLU -> FC2 -> ReduceScatter; N = hidden, K = ffn shard
+        ws = torch.empty(tp.workspace_size(tp.OP_MLP_SP, p, M, N, K, n, message=msg), dtype=torch.uint8,
+                         device=dev)
+        XG = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        Hs = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(p)]
+        Ys = [torch.empty((M // p, N), dtype=torch.bfloat16, device=dev) for _ in range(p)]
+
+        def call(i, sched):
+            inp = sets[i % len(sets)]
+            tp.mlp_sp(inp.X, inp.W[:p], inp.W[p:], n_chunks=n, sched=sched, X_gathered=XG, H=Hs, Y=Ys, ws=ws,
+                      handle=handle, message=msg)
         ws_bytes = ws.numel()
     elif wl.op.startswith("wgrad"):
         # dW_k [K, N] = A_k^T B_k over M rows, fp32 out (the optimizer's input)
@@ -184,11 +198,11 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     # The dominant kernel is priced against MFMA or HBM, whichever bounds it:
     # its algorithmic flops per byte against the ridge point peak_flops / peak_bw.
-    hbm_bound = flops / kbytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    hbm_bound = kflops / kbytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     if hbm_bound:
         achieved, peak, unit = kbytes / (avg_kernel_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
     else:
-        achieved, peak, unit = flops / (avg_kernel_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        achieved, peak, unit = kflops / (avg_kernel_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
 
     # --- the other modes (measurement context) ---
     modes = {}
@@ -239,7 +253,7 @@ def main():
                    "workspace_bytes": ws_bytes, "note": wl.note},
         "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "algorithmic_bytes": kbytes, "algorithmic_flops": flops,
+                     "algorithmic_bytes": kbytes, "algorithmic_flops": kflops,
                      "kernel": kernel_name(args.sched, wl.op),
                      "avg_kernel_ms": round(avg_kernel_ms, 4),
                      "timed_launches": len(kern_ms),
@@ -260,6 +274,8 @@ def kernel_bytes(wl, part_bytes=4):
         return 2.0 * M * K + 2.0 * K * N + 2.0 * M * N
     if wl.op.startswith("wgrad"):   # A_k [M, K], B_k [M, N], dW_k [K, N] fp32
         return p * (2.0 * M * K + 2.0 * M * N + 4.0 * K * N)
+    if wl.op == "mlp_sp":           # FC2 launch: H_k [M, K], W2_k [K, N], partials [M, N]
+        return p * (2.0 * M * K + 2.0 * K * N + part_bytes * M * N)
     if wl.op == "dx":      # dY_k [M, N], W_k [K, N], partials [M, K]
         return p * (2.0 * M * N + 2.0 * K * N + part_bytes * M * K)
     return p * (2.0 * M * K + 2.0 * K * N + part_bytes * M * N)
@@ -269,6 +285,8 @@ def kernel_name(sched, op=""):
     """The kernel that dominates one step of `sched` (what `roofline` prices)."""
     if op.startswith("wgrad"):
         return "tile_kernel A_KM (weight-gradient GEMM tiles, transposed A)"
+    if op == "mlp_sp":
+        return "tile_kernel RED=0 (FC2 shard GEMM tiles; FC1 with GeLU runs before it)"
     if sched == "persistent":
         return "fused_kernel (persistent: shard GEMM tiles + chunk reductions)"
     if sched == "tile":
@@ -304,6 +322,10 @@ def cpu_baseline(wl, inp, seconds):
         elif wl.op.startswith("wgrad"):
             A, B = (Xb * wl.p, Wb) if wl.op == "wgrad_col" else (Xb, Wb * wl.p)
             O.weight_grad([a[:, :rows] for a in A], B)
+        elif wl.op == "mlp_sp":
+            x = O.allgather(Xb)[:rows]
+            hid = [O.round_to_bf16_bits(O.gelu(x @ O.bf16_bits_to_f64(w))) for w in Wb[:wl.p]]
+            O.matmul_allreduce(hid, Wb[wl.p:])
         else:
             xg = O.allgather(Xb)[:rows]
             _ = xg @ O.bf16_bits_to_f64(Wb[0])

@@ -119,6 +119,7 @@ extern "C" {
 #define TPF_OP_MATMUL_REDUCESCATTER 1
 #define TPF_OP_ALLGATHER_MATMUL 2
 #define TPF_OP_MATMUL_DX 3
+#define TPF_OP_MLP_SP 4
 
 typedef struct tpf_context* tpf_handle;
 
@@ -198,6 +199,24 @@ int tpf_matmul_dx(tpf_handle h, int sem, int p, int64_t M, int64_t K_in, int64_t
  *   tpf_debug_set_kernel_timing is this call's only launch. */
 int tpf_weight_grad(tpf_handle h, int p, int64_t M, int64_t R, int64_t C, const void* const* A,
                     const void* const* B, void* const* dW, int dw_dtype, void* stream);
+
+/* The MLP block under sequence parallelism (cnblogs §7.1 and §11.3: the
+ * column-parallel FC1 and row-parallel FC2 need no communication between
+ * them; with sequence parallelism the block's input is all-gathered and its
+ * output reduce-scattered along the sequence).  For k = 0..p-1:
+ *   X_gathered = [X_slices[0]; ...; X_slices[p-1]]           [S, Hd] bf16 (output)
+ *   H[k]       = bf16(GeLU(X_gathered W1[k]))                [S, F] bf16 (output;
+ *                GeLU = 0.5 x (1 + erf(x / sqrt 2)) on the fp32 product, one RNE rounding)
+ *   Y_slices[r] = rows [r*S/p, (r+1)*S/p) of sum_k H[k] W2[k]   [S/p, Hd] y_dtype
+ *   X_slices[r]: [S/p, Hd], W1[k]: [Hd, F] (column shard), W2[k]: [F, Hd] (row shard).
+ * FC2 and its ReduceScatter run exactly as tpf_matmul_reducescatter with the
+ * same `sched` (flags included) and workspace
+ * (tpf_workspace_size(TPF_OP_MLP_SP, p, S, Hd, F, n_chunks, sched)); the gather
+ * and FC1 run first.  S % p == 0; Hd and F multiples of 8. */
+int tpf_mlp_sp(tpf_handle h, int p, int64_t S, int64_t Hd, int64_t F, const void* const* X_slices,
+               const void* const* W1, const void* const* W2, void* X_gathered, void* const* H,
+               void* const* Y_slices, int y_dtype, int n_chunks, int sched, void* ws, size_t ws_bytes,
+               void* stream);
 
 /* Wait for the handle's work on `stream` to finish and report whether a
  * bounded wait inside the persistent kernel gave up since the last query

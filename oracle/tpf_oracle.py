@@ -313,3 +313,45 @@ def weight_grad(A_shards: Sequence, B_shards: Sequence) -> List[np.ndarray]:
     if len(A_shards) != len(B_shards):
         raise ValueError("A and B need one block per shard")
     return [_f64(a).T @ _f64(b) for a, b in zip(A_shards, B_shards)]
+
+
+# --------------------------------------------------------------------------
+# The MLP block under sequence parallelism (cnblogs §7.1 and §11.3):
+# AllGather -> column-parallel FC1 -> GeLU -> row-parallel FC2 -> ReduceScatter
+# --------------------------------------------------------------------------
+
+
+def gelu(x: np.ndarray) -> np.ndarray:
+    """GeLU(x) = x * Phi(x) = 0.5 x (1 + erf(x / sqrt(2))), float64.
+
+    Reading: the exact (erf) form; the pages name the activation without
+    choosing between it and the tanh approximation.
+    """
+    import math
+    x = np.asarray(x, dtype=np.float64)
+    erf = np.vectorize(math.erf, otypes=[np.float64])
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+def mlp_sp_hidden(X_slices: Sequence, W1_shards: Sequence) -> List[np.ndarray]:
+    """H_k = bf16(GeLU(X W1_k)): the column shards' activations.
+
+    X is the AllGather of the sequence slices in rank order (cnblogs §2.6);
+    each rank's FC1 is a column shard (§2.3, §7.1), the activation is applied
+    element-wise to its own columns, and the activation is kept as bfloat16
+    (reading: FC2's input has the inputs' format).  Returns bf16 bit patterns.
+    """
+    x = allgather(X_slices)
+    return [round_to_bf16_bits(gelu(x @ _f64(w))) for w in W1_shards]
+
+
+def mlp_sp(X_slices: Sequence, W1_shards: Sequence, W2_shards: Sequence, H_shards=None) -> List[np.ndarray]:
+    """Output slices of the MLP block: ReduceScatter of sum_k H_k W2_k.
+
+    FC2 is row-parallel (§2.4, §7.1): rank k multiplies its activation shard
+    H_k by its row shard W2_k; the partial sums are reduced and scattered
+    along the sequence (§11.3).  ``H_shards`` (bf16 bit patterns) may be given
+    to evaluate FC2 on a particular set of activations.
+    """
+    H = mlp_sp_hidden(X_slices, W1_shards) if H_shards is None else H_shards
+    return matmul_reducescatter(H, W2_shards)

@@ -418,7 +418,7 @@ int tpf_destroy(tpf_handle h) {
 }
 
 size_t tpf_workspace_size(int op, int p, int64_t M, int64_t N, int64_t K, int n_chunks, int sched) {
-  const bool div = op == TPF_OP_MATMUL_REDUCESCATTER || op == TPF_OP_ALLGATHER_MATMUL;
+  const bool div = op == TPF_OP_MATMUL_REDUCESCATTER || op == TPF_OP_ALLGATHER_MATMUL || op == TPF_OP_MLP_SP;
   std::string saved = g_last_error;
   int st = check_common(p, M, N, K, n_chunks, TPF_BF16, sched, div);
   g_last_error = saved;
@@ -427,6 +427,7 @@ size_t tpf_workspace_size(int op, int p, int64_t M, int64_t N, int64_t K, int n_
     case TPF_OP_MATMUL_ALLREDUCE:
     case TPF_OP_MATMUL_REDUCESCATTER:
     case TPF_OP_MATMUL_DX:
+    case TPF_OP_MLP_SP:          // FC2's partials: N = Hd
       return partial_bytes(p, M, N, sched);
     case TPF_OP_ALLGATHER_MATMUL:
       return 0;
@@ -692,6 +693,69 @@ int tpf_weight_grad(tpf_handle h, int p, int64_t M, int64_t R, int64_t C, const 
   g.nshard = p;
   TPF_TIMED(h, s, launch_gemm_rows(CFG_LARGE, A_KM | B_KN, g, 0, (int)R, s));
   return TPF_OK;
+}
+
+int tpf_mlp_sp(tpf_handle h, int p, int64_t S, int64_t Hd, int64_t F, const void* const* X_slices,
+               const void* const* W1, const void* const* W2, void* X_gathered, void* const* H,
+               void* const* Y_slices, int y_dtype, int n_chunks, int sched, void* ws, size_t ws_bytes,
+               void* stream) {
+  // FC1's shapes ([S, Hd] x [Hd, F]) and FC2's ([S, F] x [F, Hd]) share the checks.
+  int st = check_common(p, S, F, Hd, n_chunks, y_dtype, sched, true);
+  if (st) return st;
+  if ((st = check_common(p, S, Hd, F, n_chunks, y_dtype, sched, true))) return st;
+  if ((st = check_ptrs(X_slices, p, "X_slices"))) return st;
+  if ((st = check_ptrs(W1, p, "W1"))) return st;
+  if ((st = check_ptrs(W2, p, "W2"))) return st;
+  if ((st = check_ptr(X_gathered, "X_gathered"))) return st;
+  if ((st = check_ptrs(const_cast<const void* const*>(H), p, "H"))) return st;
+  if ((st = check_ptrs(const_cast<const void* const*>(Y_slices), p, "Y_slices"))) return st;
+  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, S, Hd, sched)))) return st;
+  if ((st = check_handle(h))) return st;
+  if ((st = set_device(h))) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int Si = (int)S, Hi = (int)Hd, Fi = (int)F;
+  // AllGather of the sequence slices in rank order.
+  const int64_t slice_bytes = (int64_t)(Si / p) * Hi * 2;
+  char* xg = reinterpret_cast<char*>(X_gathered);
+  for (int r = 0; r < p; ++r)
+    TPF_HIP(launch_copy(reinterpret_cast<const char*>(X_slices[r]), xg + r * slice_bytes, slice_bytes, h->num_cus, s));
+  // FC1 on the column shards, GeLU in the epilogue, bf16 activations.
+  GemmOperands g{};
+  for (int k = 0; k < p; ++k) {
+    g.A[k] = reinterpret_cast<const __bf16*>(X_gathered);
+    g.B[k] = reinterpret_cast<const __bf16*>(W1[k]);
+    g.dstv[k] = H[k];
+  }
+  g.lda = Hi;
+  g.a_rows = Si;
+  g.ldb = Fi;
+  g.b_rows = Hi;
+  g.ldd = Fi;
+  g.dst_dtype = OUT_BF16;
+  g.act = 1;
+  g.M = Si;
+  g.N = Fi;
+  g.K = Hi;
+  g.nshard = p;
+  TPF_HIP(launch_gemm_rows(pick_cfg(S), B_KN, g, 0, Si, s));
+  // FC2 on the row shards and the ReduceScatter of the partial sums.
+  ReduceCall rc{};
+  rc.p = p;
+  rc.M = Si;
+  rc.N = Hi;
+  rc.K = Fi;
+  rc.bl = B_KN;
+  rc.A = const_cast<const void* const*>(H);
+  rc.B = W2;
+  for (int r = 0; r < p; ++r) rc.ro.y[r] = Y_slices[r];
+  rc.ro.scatter = 1;
+  rc.ro.rows_per_slice = Si / p;
+  rc.ro.dtype = out_kind(y_dtype);
+  rc.ro.pbf16 = msg_bf16(sched) ? 1 : 0;
+  rc.n_chunks = n_chunks;
+  rc.sched = resolve_sched(sched, n_chunks);
+  rc.P = ws;
+  return run_reduce_call(h, rc, s);
 }
 
 int tpf_sync_status(tpf_handle h, void* stream) {

@@ -608,7 +608,11 @@ __device__ __forceinline__ void gemm_tile(Frag<Cfg>& f, const TileJob& j) {
 // Write the accumulators of one tile.  Element (row, col) of the 32x32 MFMA
 // block held in register v of lane l: col = l % 32,
 // row = 8 * (v / 4) + 4 * (l / 32) + v % 4.
-template <class Cfg, int OUT>
+// GeLU(x) = x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)) in fp32 (the erf form;
+// erff is the device math library's).
+__device__ __forceinline__ float gelu_f32(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+
+template <class Cfg, int OUT, int ACT = 0>
 __device__ __forceinline__ void store_tile(const Frag<Cfg>& f, const TileJob& j, void* out, int64_t ldo) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
@@ -624,10 +628,11 @@ __device__ __forceinline__ void store_tile(const Frag<Cfg>& f, const TileJob& j,
         const int row = wm * Cfg::WM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
         if (row < j.rows) {
           const int64_t off = (int64_t)(j.m0 + row) * ldo + col;
+          const float x = ACT ? gelu_f32(f.acc[i][jn][v]) : f.acc[i][jn][v];
           if constexpr (OUT == OUT_F32)
-            reinterpret_cast<float*>(out)[off] = f.acc[i][jn][v];
+            reinterpret_cast<float*>(out)[off] = x;
           else
-            reinterpret_cast<uint16_t*>(out)[off] = (uint16_t)f32_to_bf16_bits(f.acc[i][jn][v]);
+            reinterpret_cast<uint16_t*>(out)[off] = (uint16_t)f32_to_bf16_bits(x);
         }
       }
     }

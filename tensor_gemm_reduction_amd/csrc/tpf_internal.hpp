@@ -45,6 +45,7 @@ struct GemmOperands {
   int64_t dst_shard_stride;   // elements
   int64_t ldd;
   int dst_dtype;              // OUT_F32 or OUT_BF16
+  int act;                    // 1: GeLU applied to the fp32 result before it is stored
   int M, N, K;                // rows, output width, reduction length per shard
   int b_rows;                 // rows of each B operand (K for KN weights, N for NK)
   int nshard;                 // shard GEMMs (p, or 1 for AllGather->MatMul)

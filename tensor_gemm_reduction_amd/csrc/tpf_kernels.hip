@@ -42,6 +42,12 @@ int cfg_bn(int cfg) { return cfg == CFG_SMALL ? CfgSmall::BN : cfg == CFG_MID ? 
 
 template <class Cfg>
 __device__ __forceinline__ void store_any(const Frag<Cfg>& f, const TileJob& j, const GemmOperands& g, int shard) {
+  if (g.act) {   // activation of the MLP block's FC1: GeLU, then bf16
+    uint16_t* d = g.dstv[0] ? reinterpret_cast<uint16_t*>(g.dstv[shard])
+                            : reinterpret_cast<uint16_t*>(g.dst) + (int64_t)shard * g.dst_shard_stride;
+    store_tile<Cfg, OUT_BF16, 1>(f, j, d, g.ldd);
+    return;
+  }
   if (g.dst_dtype == OUT_F32) {
     float* d = g.dstv[0] ? reinterpret_cast<float*>(g.dstv[shard])
                          : reinterpret_cast<float*>(g.dst) + (int64_t)shard * g.dst_shard_stride;

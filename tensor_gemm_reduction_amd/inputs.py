@@ -22,6 +22,9 @@ tensor-parallel Linear it stands for:
   layer: dY_k [2048,6144] N(0,1), W_k [12288,6144] N(0,0.02), 8 chunks.
 * ``decode16`` / ``decode64`` – decode-shaped row-parallel GEMMs, p=8:
   X_k [M,1024], W_k [1024,8192], both N(0,0.02), chunk counts 1/2/4.
+* ``mlp_sp`` – the MLP block of the same GPT-3 layer under sequence
+  parallelism, p=8: slices [256,12288] N(0,1), W1_k [12288,6144] and
+  W2_k [6144,12288] N(0,0.02).
 * ``dw_col`` – the weight gradient of the ``ag_fwd`` column shard layer,
   dW_k = X^T dY_k: gathered X [2048,12288], dY_k [2048,6144], both N(0,1).
 * ``dw_row`` – the weight gradient of the ``mlp_down`` row-parallel layer,
@@ -76,6 +79,9 @@ class Workload:
         if self.op in ("wgrad_col", "wgrad_row"):
             # p GEMMs dW_k [K, N] = A_k^T B_k over M rows
             return 2.0 * self.M * self.K * self.N * self.p
+        if self.op == "mlp_sp":
+            # FC1 [M, N] x [N, K] and FC2 [M, K] x [K, N] on each of p shards
+            return 4.0 * self.M * self.N * self.K * self.p
         if self.op == "dx":
             # dX [M, K] = sum over p shards of dY_k [M, N] . W_k^T
             return 2.0 * self.M * self.N * self.K * self.p
@@ -109,6 +115,10 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("decode64", "allreduce", 8, 64, 8192, 1024, (1, 2, 4),
                  ("normal", 0.02), ("normal", 0.02), index=6,
                  note="decode step, 64 tokens"),
+        Workload("mlp_sp", "mlp_sp", 8, 2048, 12288, 6144, (8, 1, 4),
+                 ("normal", 1.0), ("normal", 0.02), index=9,
+                 note="GPT-3 MLP block under sequence parallelism: AllGather, FC1 column shard + GeLU, "
+                      "FC2 row shard, ReduceScatter (N = hidden, K = ffn shard)"),
         Workload("dw_col", "wgrad_col", 8, 2048, 6144, 12288, (1,),
                  ("normal", 1.0), ("normal", 1.0), index=7, out_dtypes=("f32",),
                  note="column-parallel weight gradient dW_k = X^T dY_k of the GPT-3 FC1 shard"),
@@ -174,6 +184,7 @@ def make_inputs(wl: Workload, seed: int = 0, mode: str = "random", device: str =
       allreduce / reducescatter: X[k] [M, K], W[k] [K, N]     (k < p)
       allgather:                 X[r] [M/p, K] (slices), W[0] [K, N]
       dx:                        X[k] = dY_k [M, N], W[k] [K, N]  (K = K_in, N = N_shard)
+      mlp_sp:                    X[r] [M/p, N] (slices), W[k] = W1_k [N, K], W[p + k] = W2_k [K, N]
       wgrad_col:                 X[0] = gathered input [M, K], W[k] = dY_k [M, N]
       wgrad_row:                 X[k] = X_k [M, K], W[0] = dY [M, N]
     """
@@ -197,6 +208,15 @@ def make_inputs(wl: Workload, seed: int = 0, mode: str = "random", device: str =
         for k in range(p):
             inp.X.append(draw((M, N), wl.x_dist, tensor_seed(idx, "dY", k, seed), mode, device))
             inp.W.append(draw((K, N), wl.w_dist, tensor_seed(idx, "W", k, seed), mode, device))
+    elif wl.op == "mlp_sp":
+        if M % p:
+            raise ValueError("mlp_sp needs M divisible by p")
+        for r in range(p):
+            inp.X.append(draw((M // p, N), wl.x_dist, tensor_seed(idx, "Xs", r, seed), mode, device))
+        for k in range(p):
+            inp.W.append(draw((N, K), wl.w_dist, tensor_seed(idx, "W", k, seed), mode, device))
+        for k in range(p):
+            inp.W.append(draw((K, N), wl.w_dist, tensor_seed(idx, "W", 100 + k, seed), mode, device))
     elif wl.op == "wgrad_col":
         inp.X.append(draw((M, K), wl.x_dist, tensor_seed(idx, "X", 0, seed), mode, device))
         for k in range(p):

@@ -22,7 +22,7 @@ ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGNMENT, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_H
 BF16, F32 = 0, 1
 SCHED_AUTO, SCHED_PERSISTENT, SCHED_TWO_STREAM, SCHED_UNFUSED, SCHED_GEMM_ONLY, SCHED_REDUCE_ONLY, SCHED_TILE = range(7)
 ALLREDUCE, REDUCESCATTER = 0, 1
-OP_MATMUL_ALLREDUCE, OP_MATMUL_REDUCESCATTER, OP_ALLGATHER_MATMUL, OP_MATMUL_DX = range(4)
+OP_MATMUL_ALLREDUCE, OP_MATMUL_REDUCESCATTER, OP_ALLGATHER_MATMUL, OP_MATMUL_DX, OP_MLP_SP = range(5)
 MAX_SHARDS = 16
 MAX_CHUNKS = 64
 
@@ -46,6 +46,7 @@ SIGNATURES = {
     "tpf_allgather_matmul": (_I, [_VP, _I, _I64, _I64, _I64, _PP, _VP, _VP, _VP, _I, _I, _I, _VP, _SZ, _VP]),
     "tpf_matmul_dx": (_I, [_VP, _I, _I, _I64, _I64, _I64, _PP, _PP, _PP, _I, _I, _I, _VP, _SZ, _VP]),
     "tpf_weight_grad": (_I, [_VP, _I, _I64, _I64, _I64, _PP, _PP, _PP, _I, _VP]),
+    "tpf_mlp_sp": (_I, [_VP, _I, _I64, _I64, _I64, _PP, _PP, _PP, _VP, _PP, _PP, _I, _I, _I, _VP, _SZ, _VP]),
     "tpf_sync_status": (_I, [_VP, _VP]),
     "tpf_debug_set_wait": (_I, [_VP, _I64, _I]),
     "tpf_debug_set_timeline": (_I, [_VP, _VP, _I]),
@@ -302,3 +303,32 @@ def weight_grad(A: List[torch.Tensor], B: List[torch.Tensor], out_dtype=torch.fl
                                  ptr_array([b.data_ptr() for b in B]), ptr_array([d.data_ptr() for d in dW]),
                                  _dtype_code(dW[0].dtype), _stream_ptr(stream)))
     return dW
+
+
+def mlp_sp(X_slices: List[torch.Tensor], W1: List[torch.Tensor], W2: List[torch.Tensor], out_dtype=torch.bfloat16,
+           n_chunks: int = 1, sched="auto", X_gathered: Optional[torch.Tensor] = None,
+           H: Optional[List[torch.Tensor]] = None, Y: Optional[List[torch.Tensor]] = None,
+           ws: Optional[torch.Tensor] = None, handle: Optional[Handle] = None, stream=None,
+           message: str = "fp32"):
+    """MLP block under sequence parallelism: AllGather -> FC1 (column shards) + GeLU
+    -> FC2 (row shards) -> ReduceScatter.  Returns (X_gathered, H, Y_slices)."""
+    p = len(X_slices)
+    Sp, Hd = X_slices[0].shape
+    S = Sp * p
+    F = W1[0].shape[1]
+    dev = X_slices[0].device
+    if X_gathered is None:
+        X_gathered = torch.empty((S, Hd), dtype=torch.bfloat16, device=dev)
+    if H is None:
+        H = [torch.empty((S, F), dtype=torch.bfloat16, device=dev) for _ in range(p)]
+    if Y is None:
+        Y = [torch.empty((Sp, Hd), dtype=out_dtype, device=dev) for _ in range(p)]
+    ws, ws_bytes = _ws(OP_MLP_SP, p, S, Hd, F, n_chunks, sched, ws, dev, message)
+    h = handle or default_handle(dev.index)
+    check(load().tpf_mlp_sp(h.ptr, p, S, Hd, F, ptr_array([x.data_ptr() for x in X_slices]),
+                            ptr_array([w.data_ptr() for w in W1]), ptr_array([w.data_ptr() for w in W2]),
+                            X_gathered.data_ptr(), ptr_array([t.data_ptr() for t in H]),
+                            ptr_array([y.data_ptr() for y in Y]), _dtype_code(Y[0].dtype), n_chunks,
+                            _sched(sched, message), ws.data_ptr() if ws is not None else None, ws_bytes,
+                            _stream_ptr(stream)))
+    return X_gathered, H, Y

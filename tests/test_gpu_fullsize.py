@@ -53,7 +53,7 @@ def oracle_rows(wl, inp, rows):
     return xg @ O.bf16_bits_to_f64(bits(inp.W)[0])
 
 
-REDUCING = [n for n, w in inputs.WORKLOADS.items() if not w.op.startswith("wgrad")]
+REDUCING = [n for n, w in inputs.WORKLOADS.items() if not w.op.startswith("wgrad") and w.op != "mlp_sp"]
 WGRAD = [n for n, w in inputs.WORKLOADS.items() if w.op.startswith("wgrad")]
 
 
@@ -105,6 +105,43 @@ def test_fullsize_weight_grad(name):
         assert_f32(d32[k].index_select(0, idx), ref, what)
         assert_bf16(d16[k].index_select(0, idx), ref, what)
         assert_bf16_is_rne_of_f32(d16[k], d32[k], what)
+
+
+def test_fullsize_mlp_sp():
+    """The MLP block at full size: the gathered input exactly, sampled rows of
+    every activation against the float64 GeLU, sampled output rows against
+    FC2 evaluated on the GPU's own activations, and identical bits for every
+    FC2 scheduler."""
+    wl = inputs.WORKLOADS["mlp_sp"]
+    p, S, Hd, F = wl.p, wl.M, wl.N, wl.K
+    say(f"full-size mlp_sp: p={p} S={S} Hd={Hd} F={F}")
+    inp = inputs.make_inputs(wl, seed=0, device="cuda")
+    W1, W2 = inp.W[:p], inp.W[p:]
+    xg, H, Y = tp.mlp_sp(inp.X, W1, W2, torch.bfloat16, n_chunks=wl.default_chunks)
+    _, _, Y32 = tp.mlp_sp(inp.X, W1, W2, torch.float32, n_chunks=wl.default_chunks)
+    torch.cuda.synchronize()
+    assert torch.equal(xg, torch.cat(inp.X, 0))
+    rows = sample_rows(S, wl.default_chunks, seed=4, extra=12)
+    idx = torch.as_tensor(rows, device="cuda")
+    x = O.bf16_bits_to_f64(inputs.bf16_to_bits(xg.index_select(0, idx)))
+    Hb = []
+    for k in range(p):
+        hk = H[k].index_select(0, idx)
+        g = O.gelu(x @ O.bf16_bits_to_f64(inputs.bf16_to_bits(W1[k])))
+        h = O.bf16_bits_to_f64(inputs.bf16_to_bits(hk))
+        tol = 0.5 * np.ldexp(1.0, np.frexp(np.abs(g))[1] - 8) * (1 + 2.0 ** -7) + 1e-5 * np.sqrt(np.mean(g * g))
+        assert (np.abs(h - g) <= tol).all(), f"activation {k}"
+        Hb.append(inputs.bf16_to_bits(hk))
+    ref = O.matmul_allreduce(Hb, [inputs.bf16_to_bits(w) for w in W2])    # the sampled rows of sum_k H_k W2_k
+    y32 = torch.cat(Y32, 0).index_select(0, idx)
+    y16 = torch.cat(Y, 0).index_select(0, idx)
+    assert_f32(y32, ref, "mlp_sp rows")
+    assert_bf16(y16, ref, "mlp_sp rows")
+    assert_bf16_is_rne_of_f32(torch.cat(Y, 0), torch.cat(Y32, 0), "mlp_sp")
+    for sched in ("persistent", "two_stream", "tile"):
+        _, _, Ys = tp.mlp_sp(inp.X, W1, W2, torch.bfloat16, n_chunks=wl.default_chunks, sched=sched)
+        torch.cuda.synchronize()
+        assert_bitwise(torch.cat(Ys, 0), torch.cat(Y, 0), f"mlp_sp {sched}")
 
 
 def test_fullsize_reducescatter_equals_allreduce_rows():

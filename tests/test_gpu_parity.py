@@ -311,6 +311,53 @@ def test_weight_grad_integer_exact():
 
 
 # ---------------------------------------------------------------------------
+# MLP block under sequence parallelism
+# ---------------------------------------------------------------------------
+
+def assert_activation(Hgpu, x_w1, what):
+    """bf16 GeLU activations against the float64 GeLU of the exact product:
+    within half a bf16 ulp plus a slack for the fp32 accumulation of the
+    product (whose error is relative to the sum of |terms|, not to the result),
+    and equal to the RNE rounding of the exact value almost everywhere."""
+    g = O.gelu(x_w1)
+    h = O.bf16_bits_to_f64(inputs.bf16_to_bits(Hgpu))
+    rms = float(np.sqrt(np.mean(g * g)))
+    tol = 0.5 * np.ldexp(1.0, np.frexp(np.abs(g))[1] - 8) * (1 + 2.0 ** -7) + 1e-5 * rms
+    bad = np.abs(h - g) > tol
+    assert not bad.any(), f"{what}: {bad.sum()} activations off"
+    exact = (inputs.bf16_to_bits(Hgpu) == O.round_to_bf16_bits(g)).mean()
+    assert exact > 0.99, f"{what}: only {exact:.4f} of the activations round like the exact value"
+
+
+@pytest.mark.parametrize("p,S,Hd,F", [(2, 64, 136, 264), (4, 520, 264, 200), (8, 256, 72, 136)])
+def test_mlp_sp_parity(p, S, Hd, F):
+    say(f"mlp_sp p={p} S={S} Hd={Hd} F={F}")
+    Xs = shards([(S // p, Hd)] * p, ("normal", 1.0), 101)
+    W1 = shards([(Hd, F)] * p, ("normal", 0.05), 102)
+    W2 = shards([(F, Hd)] * p, ("normal", 0.05), 103)
+    x = O.allgather(bits(Xs))
+    outs = {}
+    for sched in SCHEDS:
+        xg, H, Y32 = tp.mlp_sp(gpu(Xs), gpu(W1), gpu(W2), torch.float32, n_chunks=4, sched=sched)
+        _, H2, Y16 = tp.mlp_sp(gpu(Xs), gpu(W1), gpu(W2), torch.bfloat16, n_chunks=4, sched=sched)
+        torch.cuda.synchronize()
+        assert torch.equal(xg.cpu(), torch.cat(Xs, 0))
+        for k in range(p):
+            assert torch.equal(H[k], H2[k])
+            if sched == "unfused":
+                assert_activation(H[k], x @ O.bf16_bits_to_f64(bits([W1[k]])[0]), f"H_{k}")
+        ref = O.mlp_sp(bits(Xs), bits(W1), bits(W2), H_shards=bits(H))   # FC2 on the GPU's activations
+        for r in range(p):
+            what = f"mlp_sp {sched} slice {r}"
+            assert_f32(Y32[r], ref[r], what)
+            assert_bf16(Y16[r], ref[r], what)
+            assert_bf16_is_rne_of_f32(Y16[r], Y32[r], what)
+        outs[sched] = torch.cat(Y32, 0)
+    for sched, y in outs.items():
+        assert_bitwise(y, outs["unfused"], f"mlp_sp {sched} vs unfused")
+
+
+# ---------------------------------------------------------------------------
 # MatMul -> ReduceScatter
 # ---------------------------------------------------------------------------
 

@@ -339,11 +339,52 @@ def pin_weight_grad_autograd(o):
     return all(np.allclose(c, w.grad.numpy(), rtol=1e-12, atol=1e-12) for c, w in zip(col, Wt))
 
 
+def pin_gelu(o):
+    """GeLU against the normal distribution's tabulated values (Phi(1) =
+    0.841344746068543, Phi(2) = 0.977249868051821), its symmetry
+    GeLU(x) - GeLU(-x) = x, the limits, and torch's erf-form GeLU."""
+    g = o.gelu(np.array([0.0, 1.0, -1.0, 2.0, -2.0, 40.0, -40.0]))
+    tab = [0.0, 0.841344746068543, -(1 - 0.841344746068543), 2 * 0.977249868051821,
+           -2 * (1 - 0.977249868051821), 40.0, 0.0]
+    if not np.allclose(g, tab, rtol=1e-14, atol=1e-15):
+        return False
+    x = np.random.default_rng(10).standard_normal(1000) * 3
+    if not np.allclose(o.gelu(x) - o.gelu(-x), x, rtol=0, atol=1e-14):
+        return False
+    ref = torch.nn.functional.gelu(torch.from_numpy(x)).numpy()   # float64, erf form
+    return np.allclose(o.gelu(x), ref, rtol=1e-14, atol=1e-15)
+
+
+def pin_mlp_sp_unsharded(o):
+    """The sharded MLP block equals the unsharded one (cnblogs §7.1: FC1 split
+    by columns and FC2 by rows needs no communication in between): with the
+    activation kept in float64, sum_k GeLU(X W1_k) W2_k == GeLU(X [W1_0|..]) [W2_0;..].
+    The oracle's bf16 activation is compared in the same way through the
+    same rounding applied to the unsharded activation."""
+    rng = np.random.default_rng(12)
+    p, s, h, f = 2, 8, 6, 4
+    Xs = [_bits(rng.standard_normal((s // p, h))) for _ in range(p)]
+    W1 = [_bits(rng.standard_normal((h, f)) * 0.5) for _ in range(p)]
+    W2 = [_bits(rng.standard_normal((f, h)) * 0.5) for _ in range(p)]
+    x = np.concatenate([O.bf16_bits_to_f64(a) for a in Xs])
+    w1 = np.concatenate([O.bf16_bits_to_f64(w) for w in W1], axis=1)
+    w2 = np.concatenate([O.bf16_bits_to_f64(w) for w in W2], axis=0)
+    hid = O.bf16_bits_to_f64(O.round_to_bf16_bits(0.5 * (x @ w1) * (1 + np.vectorize(__import__("math").erf)(
+        (x @ w1) / np.sqrt(2.0)))))
+    y = hid @ w2
+    got_h = o.mlp_sp_hidden(Xs, W1)
+    if not np.array_equal(np.concatenate(got_h, axis=1), O.round_to_bf16_bits(hid)):
+        return False
+    sl = o.mlp_sp(Xs, W1, W2)
+    return len(sl) == p and np.allclose(np.concatenate(sl), y, rtol=1e-13, atol=1e-13)
+
+
 PINS = [pin_tiny_row_parallel, pin_tiny_reducescatter, pin_tiny_column_backward, pin_tiny_allgather,
         pin_worked_example, pin_brute_force_unsharded, pin_brute_force_dx, pin_dx_autograd,
         pin_column_identity, pin_chunked_equals_whole, pin_rs_slices, pin_chunk_bounds,
         pin_round_bf16, pin_message_bf16_golden, pin_message_bf16_integer_exact,
-        pin_message_bf16_error_bound, pin_message_bf16_dx, pin_weight_grad_golden, pin_weight_grad_autograd]
+        pin_message_bf16_error_bound, pin_message_bf16_dx, pin_weight_grad_golden, pin_weight_grad_autograd,
+        pin_gelu, pin_mlp_sp_unsharded]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -497,10 +538,28 @@ def _m_weight_grad_shard_shift():
     return _Mutant(weight_grad=lambda A, B: O.weight_grad(A, list(B[1:]) + list(B[:1])))
 
 
+def _m_gelu_tanh():
+    # the tanh approximation instead of the erf form
+    def gelu(x):
+        x = np.asarray(x, np.float64)
+        return 0.5 * x * (1 + np.tanh(np.sqrt(2 / np.pi) * (x + 0.044715 * x ** 3)))
+    m = _Mutant(gelu=gelu)
+    m.mlp_sp_hidden = lambda Xs, W1: [O.round_to_bf16_bits(gelu(O.allgather(Xs) @ O.bf16_bits_to_f64(w))) for w in W1]
+    m.mlp_sp = lambda Xs, W1, W2, H=None: O.matmul_reducescatter(m.mlp_sp_hidden(Xs, W1) if H is None else H, W2)
+    return m
+
+
+def _m_mlp_w2_transposed_shards():
+    # FC2 applied with the shards in reverse order
+    m = _Mutant()
+    m.mlp_sp = lambda Xs, W1, W2, H=None: O.matmul_reducescatter(O.mlp_sp_hidden(Xs, W1), list(W2)[::-1])
+    return m
+
+
 MUTANTS = [_m_dropped_shard, _m_sign, _m_dx_untransposed, _m_slices_reversed, _m_gather_reversed,
            _m_round_truncate, _m_round_via_f32, _m_chunk_lastshort, _m_pipeline_serial,
            _m_message_truncated, _m_message_unrounded, _m_message_fold_f64, _m_message_fold_reversed,
-           _m_weight_grad_swapped, _m_weight_grad_shard_shift]
+           _m_weight_grad_swapped, _m_weight_grad_shard_shift, _m_gelu_tanh, _m_mlp_w2_transposed_shards]
 
 
 @pytest.mark.parametrize("mut", MUTANTS, ids=[m.__name__ for m in MUTANTS])
