@@ -617,6 +617,34 @@ __device__ __forceinline__ void store_tile(const Frag<Cfg>& f, const TileJob& j,
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   const int r32 = lane & 31, half = lane >> 5;
+  constexpr int ES = OUT == OUT_F32 ? 4 : 2;
+  if (j.rows == Cfg::BM && j.n0 + Cfg::BN <= j.N) {
+    // Whole tile in range: buffer stores addressed from the tile's first
+    // element, one per-lane offset per 32x32 block and the block-row offsets
+    // (8 (v / 4) + v % 4) * ldo in scalar registers, so each element costs
+    // one store.  Every offset is below 2^31: each output is < 2 GiB.
+    const int64_t tile0 = (int64_t)j.m0 * ldo + j.n0;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(reinterpret_cast<char*>(out) + tile0 * ES, (int64_t)Cfg::BM * ldo * ES);
+    const int lds = (int)ldo * ES;
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i) {
+#pragma unroll
+      for (int jn = 0; jn < Cfg::TN; ++jn) {
+        const int voff = (wm * Cfg::WM + i * 32 + 4 * half) * lds + (wn * Cfg::WN + jn * 32 + r32) * ES;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int soff = (8 * (v >> 2) + (v & 3)) * lds;
+          const float x = ACT ? gelu_f32(f.acc[i][jn][v]) : f.acc[i][jn][v];
+          if constexpr (OUT == OUT_F32)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, voff, soff, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_bits(x), rs, voff, soff, 0);
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < Cfg::TM; ++i) {
 #pragma unroll
