@@ -74,6 +74,49 @@ def test_allreduce_parity(p, M, N, K):
         assert_bitwise(y16, base16, f"bf16 {key} vs unfused n=1")
 
 
+EDGE_CASES = [
+    # p, M, N, K
+    (16, 48, 136, 72),      # the largest p
+    (2, 1, 8, 8),           # one row, the smallest N and K
+    (3, 32, 264, 200),      # last row count of the 32-row tiles
+    (3, 33, 264, 8),        # first row count of the 64-row tiles, one 8-deep K step
+    (5, 64, 1032, 136),     # last row count of the 64-row tiles
+    (5, 65, 8, 1032),       # first row count of the 256-row tiles, output narrower than a tile
+]
+
+
+@pytest.mark.parametrize("p,M,N,K", EDGE_CASES)
+def test_edge_shapes(p, M, N, K):
+    say(f"edge p={p} M={M} N={N} K={K}")
+    Xh = shards([(M, K)] * p, ("normal", 1.0), 111)
+    Wh = shards([(K, N)] * p, ("normal", 0.05), 112)
+    ref = O.matmul_allreduce(bits(Xh), bits(Wh))
+    X, W = gpu(Xh), gpu(Wh)
+    outs = []
+    for sched in SCHEDS:
+        for n in sorted({1, min(M, 3), min(M, 64)}):
+            y32 = tp.matmul_allreduce(X, W, torch.float32, n_chunks=n, sched=sched)
+            y16 = tp.matmul_allreduce(X, W, torch.bfloat16, n_chunks=n, sched=sched)
+            torch.cuda.synchronize()
+            what = f"edge p={p} M={M} N={N} K={K} {sched} n={n}"
+            assert_f32(y32, ref, what)
+            assert_bf16(y16, ref, what)
+            assert_bf16_is_rne_of_f32(y16, y32, what)
+            outs.append(y32)
+    for y in outs[1:]:
+        assert_bitwise(y, outs[0], f"edge p={p} M={M} N={N} K={K}")
+    if M % p == 0:     # the ReduceScatter and dX layouts at the same shapes
+        sl = tp.matmul_reducescatter(X, W, torch.float32, n_chunks=min(M, 3))
+        torch.cuda.synchronize()
+        assert_bitwise(torch.cat(sl, 0), outs[0], "edge RS")
+    dY = gpu(shards([(M, N)] * p, ("normal", 1.0), 113))
+    Wd = gpu(shards([(K, N)] * p, ("normal", 0.05), 114))
+    dref = O.matmul_dx([inputs.bf16_to_bits(t) for t in dY], [inputs.bf16_to_bits(t) for t in Wd])
+    dx = tp.matmul_dx(dY, Wd, tp.ALLREDUCE, torch.float32, n_chunks=min(M, 3))
+    torch.cuda.synchronize()
+    assert_f32(dx, dref, f"edge dX p={p} M={M}")
+
+
 def test_allreduce_integer_exact():
     p, M, N, K = 4, 272, 264, 520
     say(f"allreduce integer-exact p={p} M={M} N={N} K={K}")
