@@ -56,8 +56,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the simulated ranks share one MI355X); --gpus {args.gpus} "
-              f"is not supported in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (the p simulated ranks all live on one MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs as a single process on one GPU", file=sys.stderr)

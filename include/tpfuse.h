@@ -66,7 +66,7 @@ extern "C" {
 #define TPF_ERR_SHAPE -2         /* non-positive size, p or n_chunks out of range, M % p != 0 where required */
 #define TPF_ERR_ALIGNMENT -3     /* pointer not 16-byte aligned, N or K not a multiple of 8 */
 #define TPF_ERR_WORKSPACE -4     /* workspace missing or smaller than tpf_workspace_size() */
-#define TPF_ERR_UNSUPPORTED -5   /* valid request this build cannot run */
+#define TPF_ERR_UNSUPPORTED -5   /* valid request the library cannot run (size limits) */
 #define TPF_ERR_HIP -6           /* a HIP runtime call failed (message in tpf_last_error) */
 #define TPF_ERR_TIMEOUT -7       /* a bounded wait inside the persistent kernel gave up */
 
