@@ -181,6 +181,37 @@ def test_repeated_persistent_calls_are_deterministic():
     assert tp.default_handle().sync_status() == tp.OK
 
 
+@pytest.mark.parametrize("sched", ["auto", "persistent", "tile"])
+def test_graph_capture_replays_match_eager(sched):
+    """The calls enqueue only kernels (no memset, no allocation) and leave every
+    counter at zero, so a captured call replays correctly: several replays, with
+    eager work and synchronizations between them, each equal to the eager bits."""
+    p, M, N, K = 4, 64, 1032, 136
+    say(f"graph capture {sched}")
+    X = gpu(shards([(M, K)] * p, ("normal", 1.0), 121))
+    W = gpu(shards([(K, N)] * p, ("normal", 0.05), 122))
+    h = tp.Handle(0)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(tp.workspace_size(tp.OP_MATMUL_ALLREDUCE, p, M, N, K, 4, sched), dtype=torch.uint8,
+                     device=DEV)
+    ref = tp.matmul_allreduce(X, W, torch.bfloat16, n_chunks=4, sched=sched, handle=h).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tp.matmul_allreduce(X, W, n_chunks=4, sched=sched, Y=Y, ws=ws, handle=h)
+    for i in range(4):
+        Y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bitwise(Y, ref, f"{sched} replay {i}")
+        # eager work on the same handle between replays
+        other = tp.matmul_allreduce(X, W, torch.bfloat16, n_chunks=2, sched=sched, handle=h)
+        torch.cuda.synchronize()
+        assert_bitwise(other, ref, f"{sched} eager call {i}")
+    assert h.sync_status() == tp.OK
+    h.close()
+
+
 def test_tile_counters_reset_between_calls():
     """The tile scheduler's per-output-tile counters and queue shares return to
     zero at the end of every call: calls of different tile grids in a row
