@@ -7,6 +7,10 @@ HBM-resident inputs.  Default workload: the Llama-style MLP down projection
 (row-parallel, p=4 shards X_k [4096,4096] . W_k [4096,4096], 8 M-chunks,
 AllReduce layout, bf16 out).
 
+Before the W warmup steps, untimed steps run for at least --settle-ms
+(default 300 ms): the clocks take that long under sustained load to reach
+their steady state, and the K timed steps are meant to see it.
+
 Prints ONE JSON line.  `value` is whole-step TFLOP/s of the library call
 (algorithmic 2*M*N*K_total over the wall time per step; the default
 scheduler is AUTO, which on one GPU runs the shard-GEMM kernel followed by
@@ -45,6 +49,11 @@ def parse():
     ap.add_argument("--message", default="fp32", choices=["fp32", "bf16"],
                     help="precision of the shard partials (the 2-byte message variant: bf16)")
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated to defeat the 256 MB last-level cache")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed steps run for at least this long before the warmup steps: the GPU's clocks "
+                         "take ~0.1-0.2 s of sustained load to reach their steady state")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture the timed steps in one HIP graph and report its replay time per step")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--modes", default="gemm_only,reduce_only,unfused,two_stream,persistent,tile,auto")
@@ -173,6 +182,16 @@ def main():
         return {"ms_median": per[len(per) // 2], "ms_min": per[0], "ms_mean": sum(per) / len(per),
                 "wall_ms_per_step": 1e3 * wall / steps}
 
+    # --- settle (untimed, time-bounded), then the warmup steps ---
+    settle_steps, t_settle = 0, time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        call(settle_steps, args.sched)
+        settle_steps += 1
+        if settle_steps % 8 == 0:
+            torch.cuda.synchronize()      # measure GPU progress, not how fast the host can enqueue
+    torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
+
     # --- the timed region: exactly `steps` fused steps ---
     for i in range(args.warmup):
         call(i, args.sched)
@@ -203,6 +222,36 @@ def main():
         achieved, peak, unit = kbytes / (avg_kernel_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
     else:
         achieved, peak, unit = kflops / (avg_kernel_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+
+    # --- the same steps captured in one HIP graph (launch overhead removed) ---
+    graph = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call(0, args.sched)          # warm the side stream before capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(args.steps):
+                call(i, args.sched)
+        g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        g0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        st = handle.sync_status()
+        if st != tp.OK:
+            raise RuntimeError(f"graph replay reported status {st}")
+        gms = g0.elapsed_time(g1) / (reps * args.steps)
+        graph = {"ms_per_step": round(gms, 4), "value": round(flops / (gms * 1e-3) / 1e12, 3),
+                 "steps_per_graph": args.steps, "replays": reps}
+        del g
 
     # --- the other modes (measurement context) ---
     modes = {}
@@ -242,6 +291,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "settle": {"ms": round(settle_ms, 1), "steps": settle_steps},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -259,6 +309,7 @@ def main():
                      "timed_launches": len(kern_ms),
                      "avg_step_event_ms": round(sum(step_ms) / len(step_ms), 4)},
         "cpu_baseline": cpu,
+        "graph": graph,
         "modes": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in modes.items()},
         **{k: round(v, 4) for k, v in extra.items()},
     }

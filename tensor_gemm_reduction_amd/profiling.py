@@ -44,6 +44,21 @@ def _rows(path_or_dir: str, suffix: str):
             yield from csv.DictReader(f)
 
 
+def last_dispatches(trace_path: str, name_sub: str, k: int):
+    """Average duration (us) of the last k dispatches of the kernel whose name
+    contains name_sub and that takes the most total time in the trace."""
+    by_name = {}
+    for r in _rows(trace_path, "kernel_trace.csv"):
+        if name_sub in r["Kernel_Name"]:
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            by_name.setdefault(r["Kernel_Name"], []).append((t0, t1 - t0))
+    if not by_name:
+        return None
+    name = max(by_name, key=lambda n: sum(d for _, d in by_name[n]))
+    last = sorted(by_name[name])[-k:]
+    return name, sum(d for _, d in last) / len(last) / 1e3, len(last)
+
+
 def counter_per_dispatch(path: str, counter: str, kernel_sub: str) -> float:
     vals = [float(r["Counter_Value"]) for r in _rows(path, "counter_collection.csv")
             if r.get("Counter_Name") == counter and kernel_sub in r.get("Kernel_Name", "")]
@@ -67,6 +82,13 @@ def stats(csv_path: str, out_path: str, command: str, bench_json: str = "") -> N
         with open(bench_json) as f:
             rec = json.loads(f.read().strip().splitlines()[-1])
         r = rec["roofline"]
+        k = int(r.get("timed_launches") or 0)
+        last = last_dispatches(csv_path, r["kernel"].split()[0], k) if k else None
+        if last:
+            name, avg_us, n = last
+            lines += ["", f"# rocprofv3, the last {n} dispatches of {name[:70]}",
+                      f"#   (the bench's timed launches; earlier ones are its settle and warmup steps): "
+                      f"average {avg_us:.2f} us"]
         lines += ["", f"# bench.py (same run): dominant kernel = {r['kernel']}",
                   f"#   HIP-event average over {r.get('timed_launches')} timed launches: "
                   f"{1e3 * r['avg_kernel_ms']:.2f} us; roofline {r['achieved']} {r['unit']} of {r['peak']} "
