@@ -56,7 +56,7 @@ def parse():
                     help="also capture the timed steps in one HIP graph and report its replay time per step")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--modes", default="gemm_only,reduce_only,unfused,two_stream,persistent,tile,auto")
+    ap.add_argument("--modes", default="gemm_only,reduce_only,unfused,two_stream,persistent,tile,fold,auto")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -340,6 +340,8 @@ def kernel_name(sched, op=""):
         return "tile_kernel RED=0 (FC2 shard GEMM tiles; FC1 with GeLU runs before it)"
     if sched == "persistent":
         return "fused_kernel (persistent: shard GEMM tiles + chunk reductions)"
+    if sched == "fold":
+        return "tile_kernel pair (shards 0..p-2 into partials, then shard p-1 with the fold epilogue)"
     if sched == "tile":
         return "tile_kernel RED=1 (shard GEMM tiles + last-arriver tile sums)"
     if sched == "two_stream":

@@ -87,14 +87,25 @@ extern "C" {
                                     AllGather->MatMul: only the GEMM over an already gathered X) */
 #define TPF_SCHED_REDUCE_ONLY 5  /* measurement: only the reduction of partials already in the workspace
                                     (for AllGather->MatMul: only the gather copy) */
-#define TPF_SCHED_TILE 6         /* readiness per output tile: one persistent kernel runs the shard GEMM
-                                    tiles of the whole output in an L2-friendly order, and the workgroup
+#define TPF_SCHED_TILE 6         /* readiness per output tile: one kernel (one workgroup per tile) runs the
+                                    shard GEMM tiles of the whole output in an L2-friendly order, and the
+                                    workgroup
                                     that finishes the last shard of an output tile sums that tile at once
                                     (the M027 page's per-chunk readiness at the finest chunking, every
                                     output tile its own chunk; n_chunks is checked but does not change
                                     the schedule).  At most 131072 output tiles (TPF_ERR_UNSUPPORTED
                                     beyond).  For AllGather->MatMul, which has no reduction, it runs as
                                     TPF_SCHED_PERSISTENT. */
+#define TPF_SCHED_FOLD 7         /* the reduction folded into the last shard's GEMM epilogue: one launch
+                                    computes the partials of shards 0..p-2, a second computes shard p-1
+                                    and, per output element, adds those partials in shard order and then
+                                    its own accumulator, writing the result directly (no partial of the
+                                    last shard, no separate reduction pass; the same additions in the
+                                    same order as TPF_SCHED_UNFUSED, so the same bits).  The M027 page's
+                                    pipelining taken to one step: the "communication" of the last shard
+                                    is its epilogue.  n_chunks is checked but does not change the
+                                    schedule.  For M <= 64 (one shard's tiles could not fill the GPU)
+                                    and for AllGather->MatMul it runs as TPF_SCHED_UNFUSED. */
 
 /* Message precision, OR-ed into the `sched` argument of the reducing calls
  * (tpf_matmul_allreduce, tpf_matmul_reducescatter, tpf_matmul_dx, and

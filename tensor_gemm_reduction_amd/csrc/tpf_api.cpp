@@ -73,7 +73,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // A scheduler id in the low byte, optionally OR-ed with TPF_MSG_BF16.
 bool valid_sched(int s) {
   const int base = s & 0xff, flags = s & ~0xff;
-  return base >= TPF_SCHED_AUTO && base <= TPF_SCHED_TILE && (flags & ~TPF_MSG_BF16) == 0;
+  return base >= TPF_SCHED_AUTO && base <= TPF_SCHED_FOLD && (flags & ~TPF_MSG_BF16) == 0;
 }
 bool msg_bf16(int s) { return (s & TPF_MSG_BF16) != 0; }
 bool valid_dtype(int d) { return d == TPF_BF16 || d == TPF_F32; }
@@ -197,6 +197,33 @@ int ktime_stop(tpf_handle h, hipStream_t s) {
     if (st_) return st_;             \
   } while (0)
 
+// The fold scheduler's two launches: shards 0..p-2 into their partials, then
+// shard p-1, whose epilogue adds those partials and its own accumulator.
+static hipError_t launch_fold(int cfg, int bl, const GemmOperands& g, const ReduceOut& ro, void* P, int64_t stride,
+                       int p, int M, int N, hipStream_t s) {
+  if (p > 1) {
+    GemmOperands g0 = g;
+    g0.nshard = p - 1;
+    const hipError_t e = launch_gemm_rows(cfg, bl, g0, 0, M, s);
+    if (e != hipSuccess) return e;
+  }
+  TileArgs a{};
+  a.g = g;
+  a.g.A[0] = g.A[p - 1];
+  a.g.B[0] = g.B[p - 1];
+  a.g.nshard = 1;
+  a.ro = ro;
+  a.P = P;
+  a.p_stride = stride;
+  a.p = p;
+  a.row0 = 0;
+  a.row1 = M;
+  a.tiles_m = (M + cfg_bm(cfg) - 1) / cfg_bm(cfg);
+  a.tiles_n = (N + cfg_bn(cfg) - 1) / cfg_bn(cfg);
+  a.tasks = a.tiles_m * a.tiles_n;
+  return launch_tiles(cfg, bl, 2 + (ro.dtype == OUT_F32 ? 1 : 0) + 2 * ro.pbf16, a, s);
+}
+
 int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
   int st = set_device(h);
   if (st) return st;
@@ -221,7 +248,10 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
   ChunkGeom ch{rc.n_chunks, rc.M / rc.n_chunks, rc.M};
   const int64_t stride = (int64_t)rc.M * rc.N;
 
-  switch (rc.sched) {
+  // One shard's tiles of a small-M problem cannot fill the GPU: the fold
+  // scheduler then runs as UNFUSED (the same bits either way).
+  const int sched = rc.sched == TPF_SCHED_FOLD && cfg != CFG_LARGE ? TPF_SCHED_UNFUSED : rc.sched;
+  switch (sched) {
     case TPF_SCHED_GEMM_ONLY:
       TPF_TIMED(h, stream, launch_gemm_rows(cfg, rc.bl, g, 0, rc.M, stream));
       return TPF_OK;
@@ -254,6 +284,9 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
       TPF_HIP(hipStreamWaitEvent(stream, h->ev_join2, 0));
       return TPF_OK;
     }
+    case TPF_SCHED_FOLD:
+      TPF_TIMED(h, stream, launch_fold(cfg, rc.bl, g, rc.ro, rc.P, stride, rc.p, rc.M, rc.N, stream));
+      return TPF_OK;
     case TPF_SCHED_TILE: {
       TileArgs a{};
       a.g = g;
@@ -562,6 +595,7 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
   ChunkGeom ch{n_chunks, Mi / n_chunks, Mi};
   int s = resolve_sched(sched, n_chunks);
   if (s == TPF_SCHED_TILE) s = TPF_SCHED_PERSISTENT;   // no reduction to fold into the tiles
+  if (s == TPF_SCHED_FOLD) s = TPF_SCHED_UNFUSED;
   switch (s) {
     case TPF_SCHED_GEMM_ONLY:
       TPF_TIMED(h, stream_, launch_gemm_rows(cfg, B_KN, g, 0, Mi, stream_));

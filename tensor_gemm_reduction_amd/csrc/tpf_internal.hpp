@@ -189,8 +189,11 @@ hipError_t launch_reduce_rows(const void* P, int64_t stride, int p, int row0, in
                               const ReduceOut& o, int num_cus, hipStream_t s);
 hipError_t launch_fused(int cfg, int bl, const FusedArgs& a, int grid, hipStream_t s);
 int fused_occupancy(int cfg, int bl);   // resident fused workgroups per CU
-// One workgroup per tile; red = 1 for the tile scheduler (fp32 partials,
-// per-output-tile counters, last arriver sums).
+// One workgroup per tile; red = 1 for the tile scheduler (partials,
+// per-output-tile counters, last arriver sums); red = 2 for the last shard of
+// the fold scheduler (a.g holds that shard alone; its epilogue adds the
+// partials of the p - 1 shards before it, already in a.P): red = 2 + (fp32
+// output) + 2 * (bf16 messages), CFG_LARGE only.
 hipError_t launch_tiles(int cfg, int bl, int red, const TileArgs& a, hipStream_t s);
 hipError_t launch_copy(const char* src, char* dst, int64_t bytes, int num_cus, hipStream_t s);
 hipError_t launch_clear_status(Ctrl* c, hipStream_t s);

@@ -356,8 +356,83 @@ __device__ __forceinline__ void reduce_tile_any(const TileArgs& a, int m0, int r
   }
 }
 
-// One workgroup per GEMM tile, used both for plain shard GEMMs (RED = 0) and
-// for the tile scheduler (RED = 1).  The nshard * tiles_m * tiles_n tiles of
+// Epilogue of the fold scheduler, run by the tiles of the last shard after
+// the partials of shards 0..p-2 are complete (an earlier launch wrote them).
+// For each element: s = P_0 + P_1 + ... + P_{p-2} left to right in fp32, then
+// s + (this tile's fp32 accumulator, rounded to bf16 first for 2-byte
+// messages, exactly the message this shard would have stored), rounded once
+// into the AllReduce or ReduceScatter destination.  These are the reduction
+// kernel's additions in its order, so the bits are the same.  The partials of
+// up to four shards for 8 of the 16 elements a lane holds of one 32x32 block
+// are requested together before they are added.
+template <int PB>
+__device__ __forceinline__ float message_value(float acc) {
+  if constexpr (PB) return __uint_as_float(f32_to_bf16_bits(acc) << 16);
+  else return acc;
+}
+
+template <class Cfg, int OUT, int PB>
+__device__ __forceinline__ void fold_store(const Frag<Cfg>& f, const TileJob& j, const TileArgs& a) {
+  constexpr int G = 4, QB = 8;   // shards and rows per batch of loads
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+  const int r32 = lane & 31, half = lane >> 5;
+  const int np = a.p - 1;
+  const int N = j.N;
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i) {
+#pragma unroll
+    for (int jn = 0; jn < Cfg::TN; ++jn) {
+      const int col = j.n0 + wn * Cfg::WN + jn * 32 + r32;
+      const bool col_ok = col < N;
+      const int rbase = wm * Cfg::WM + i * 32 + 4 * half;
+#pragma unroll
+      for (int q0 = 0; q0 < 16; q0 += QB) {
+        float s[QB];
+#pragma unroll
+        for (int k0 = 0; k0 < kMaxShards - 1; k0 += G) {
+          if (k0 >= np) break;
+          float v[G][QB];
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            if (k0 + g < np) {
+              const int64_t base = (int64_t)(k0 + g) * a.p_stride;
+#pragma unroll
+              for (int qq = 0; qq < QB; ++qq) {
+                const int q = q0 + qq;
+                const int row = rbase + 8 * (q >> 2) + (q & 3);
+                v[g][qq] = row < j.rows && col_ok ? load_partial1<PB>(a.P, base + (int64_t)(j.m0 + row) * N + col)
+                                                  : 0.0f;
+              }
+            }
+          }
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            if (k0 + g < np) {
+#pragma unroll
+              for (int qq = 0; qq < QB; ++qq) s[qq] = (k0 + g == 0) ? v[g][qq] : s[qq] + v[g][qq];
+            }
+          }
+        }
+#pragma unroll
+        for (int qq = 0; qq < QB; ++qq) {
+          const int q = q0 + qq;
+          const int row = rbase + 8 * (q >> 2) + (q & 3);
+          const float own = message_value<PB>(f.acc[i][jn][q]);
+          if (row < j.rows && col_ok)
+            reduce_store1<OUT>(a.ro, (int64_t)(j.m0 + row) * N + col, N, np > 0 ? s[qq] + own : own);
+        }
+      }
+    }
+  }
+}
+
+// The fold variants of tile_kernel: RED = 2 + (fp32 output) + 2 * (bf16 messages).
+constexpr int fold_red(int out, int pbf16) { return 2 + (out == OUT_F32 ? 1 : 0) + 2 * pbf16; }
+
+// One workgroup per GEMM tile, used for plain shard GEMMs (RED = 0), for the
+// tile scheduler (RED = 1) and for the last shard of the fold scheduler
+// (RED = 2..5, see fold_red: a.g holds that one shard's operands).  The nshard * tiles_m * tiles_n tiles of
 // rows [row0, row1) are taken in the order of tile_coords (shard-major,
 // grouped tile rows) through xcd_task, so each XCD works through the operand
 // panels of one shard, and the XCDs of different shards advance through the
@@ -379,6 +454,11 @@ __global__ __launch_bounds__(Cfg::THREADS) void tile_kernel(TileArgs args) {
   if constexpr (RED == 0) {
     gemm_tile<Cfg, BL>(f, j);
     store_any<Cfg>(f, j, a.g, shard);
+  } else if constexpr (RED >= 2) {
+    gemm_tile<Cfg, BL>(f, j);
+    constexpr int FOLD_OUT = ((RED - 2) & 1) ? OUT_F32 : OUT_BF16;
+    constexpr int FOLD_PB = (RED - 2) / 2;
+    fold_store<Cfg, FOLD_OUT, FOLD_PB>(f, j, a);
   } else {
     int& s_word = *reinterpret_cast<int*>(stage_ptr<Cfg, 0>());   // idle once gemm_tile returns
     const uint64_t t_start = a.timeline ? __builtin_amdgcn_s_memrealtime() : 0;
@@ -496,19 +576,27 @@ static void launch_tile_cfg(int bl, const TileArgs& a, int grid, hipStream_t s) 
     hipLaunchKernelGGL((tile_kernel<Cfg, B_NK, RED>), dim3(grid), dim3(Cfg::THREADS), 0, s, a);
 }
 
+template <class Cfg>
+static void launch_tile_red(int bl, int red, const TileArgs& a, int grid, hipStream_t s) {
+  if (red == 1) launch_tile_cfg<Cfg, 1>(bl, a, grid, s);
+  else launch_tile_cfg<Cfg, 0>(bl, a, grid, s);
+}
+
 hipError_t launch_tiles(int cfg, int bl, int red, const TileArgs& a, hipStream_t s) {
   if (a.tasks <= 0) return hipSuccess;
   const int grid = a.tasks;
-  if (cfg == CFG_SMALL) {
-    if (red) launch_tile_cfg<CfgSmall, 1>(bl, a, grid, s);
-    else launch_tile_cfg<CfgSmall, 0>(bl, a, grid, s);
-  } else if (cfg == CFG_MID) {
-    if (red) launch_tile_cfg<CfgMid, 1>(bl, a, grid, s);
-    else launch_tile_cfg<CfgMid, 0>(bl, a, grid, s);
-  } else {
-    if (red) launch_tile_cfg<CfgLarge, 1>(bl, a, grid, s);
-    else launch_tile_cfg<CfgLarge, 0>(bl, a, grid, s);
+  if (red >= 2) {   // fold epilogue: large tiles only
+    if (cfg != CFG_LARGE || red > 5) return hipErrorInvalidValue;
+    const int out = ((red - 2) & 1) ? OUT_F32 : OUT_BF16, pb = (red - 2) >> 1;
+    if (out == OUT_BF16 && !pb) launch_tile_cfg<CfgLarge, fold_red(OUT_BF16, 0)>(bl, a, grid, s);
+    else if (out == OUT_F32 && !pb) launch_tile_cfg<CfgLarge, fold_red(OUT_F32, 0)>(bl, a, grid, s);
+    else if (out == OUT_BF16) launch_tile_cfg<CfgLarge, fold_red(OUT_BF16, 1)>(bl, a, grid, s);
+    else launch_tile_cfg<CfgLarge, fold_red(OUT_F32, 1)>(bl, a, grid, s);
+    return hipGetLastError();
   }
+  if (cfg == CFG_SMALL) launch_tile_red<CfgSmall>(bl, red, a, grid, s);
+  else if (cfg == CFG_MID) launch_tile_red<CfgMid>(bl, red, a, grid, s);
+  else launch_tile_red<CfgLarge>(bl, red, a, grid, s);
   return hipGetLastError();
 }
 

@@ -42,6 +42,7 @@ def test_constants_match_header():
     assert int(defs["TPF_F32"]) == tp.F32 and int(defs["TPF_BF16"]) == tp.BF16
     assert int(defs["TPF_SCHED_REDUCE_ONLY"]) == tp.SCHED_REDUCE_ONLY
     assert int(defs["TPF_SCHED_TILE"]) == tp.SCHED_TILE
+    assert int(defs["TPF_SCHED_FOLD"]) == tp.SCHED_FOLD
     assert int(defs["TPF_REDUCESCATTER"]) == tp.REDUCESCATTER
     assert int(defs["TPF_OP_MATMUL_DX"]) == tp.OP_MATMUL_DX
     assert int(defs["TPF_MAX_SHARDS"]) == tp.MAX_SHARDS and int(defs["TPF_MAX_CHUNKS"]) == tp.MAX_CHUNKS
@@ -72,6 +73,8 @@ def test_workspace_size():
     assert ws(tp.OP_MATMUL_DX, 8, 2048, 12288, 6144, 8, "unfused", "bf16") == 8 * 2048 * 12288 * 2
     assert ws(tp.OP_ALLGATHER_MATMUL, 8, 2048, 6144, 12288, 8, message="bf16") == 0
     assert ws(tp.OP_MATMUL_ALLREDUCE, 4, 64, 64, 64, 1, tp.SCHED_TILE | 0x200) == 0   # unknown flag
+    assert ws(tp.OP_MATMUL_ALLREDUCE, 4, 64, 64, 64, 1, tp.SCHED_FOLD + 1) == 0      # unknown scheduler
+    assert ws(tp.OP_MATMUL_ALLREDUCE, 4, 64, 64, 64, 1, "fold") == 4 * 64 * 64 * 4
 
 
 def _ar(p=2, M=64, N=64, K=64, X=None, W=None, Y=A16, dtype=tp.BF16, n=1, sched=tp.SCHED_AUTO, ws=A16,

@@ -75,7 +75,7 @@ def test_fullsize_parity(name):
     assert_bf16_is_rne_of_f32(y16, y32, what)
     # every other chunk count and scheduler gives the same bits
     for m in wl.chunks:
-        for sched in ("persistent", "two_stream", "unfused", "tile"):
+        for sched in ("persistent", "two_stream", "unfused", "tile", "fold"):
             if m == n and sched == "persistent" and n == 1:
                 continue
             y = run(wl, inp, torch.bfloat16, m, sched)
@@ -138,7 +138,7 @@ def test_fullsize_mlp_sp():
     assert_f32(y32, ref, "mlp_sp rows")
     assert_bf16(y16, ref, "mlp_sp rows")
     assert_bf16_is_rne_of_f32(torch.cat(Y, 0), torch.cat(Y32, 0), "mlp_sp")
-    for sched in ("persistent", "two_stream", "tile"):
+    for sched in ("persistent", "two_stream", "tile", "fold"):
         _, _, Ys = tp.mlp_sp(inp.X, W1, W2, torch.bfloat16, n_chunks=wl.default_chunks, sched=sched)
         torch.cuda.synchronize()
         assert_bitwise(torch.cat(Ys, 0), torch.cat(Y, 0), f"mlp_sp {sched}")

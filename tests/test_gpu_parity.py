@@ -16,7 +16,7 @@ from tests.parity import (assert_bf16, assert_bf16_is_rne_of_f32, assert_bitwise
 
 pytestmark = pytest.mark.gpu
 
-SCHEDS = ["persistent", "two_stream", "unfused", "tile"]
+SCHEDS = ["persistent", "two_stream", "unfused", "tile", "fold"]
 DEV = "cuda"
 
 
@@ -181,7 +181,7 @@ def test_repeated_persistent_calls_are_deterministic():
     assert tp.default_handle().sync_status() == tp.OK
 
 
-@pytest.mark.parametrize("sched", ["auto", "persistent", "tile"])
+@pytest.mark.parametrize("sched", ["auto", "persistent", "tile", "fold"])
 def test_graph_capture_replays_match_eager(sched):
     """The calls enqueue only kernels (no memset, no allocation) and leave every
     counter at zero, so a captured call replays correctly: several replays, with
@@ -239,10 +239,10 @@ def test_kernel_timing_records_one_launch_per_call():
     W = gpu(shards([(K, N)] * p, ("normal", 0.05), 72))
     h = tp.Handle(0)
     h.set_kernel_timing(True)
-    for sched in ("auto", "unfused", "gemm_only", "persistent", "tile", "two_stream"):
+    for sched in ("auto", "unfused", "gemm_only", "persistent", "tile", "fold", "two_stream"):
         tp.matmul_allreduce(X, W, n_chunks=4, sched=sched, handle=h)
     t = h.kernel_times()
-    assert len(t) == 5 and all(0.0 < v < 1000.0 for v in t), t    # two_stream records nothing
+    assert len(t) == 6 and all(0.0 < v < 1000.0 for v in t), t    # two_stream records nothing
     assert h.kernel_times() == []                                    # cleared
     h.set_kernel_timing(False)
     tp.matmul_allreduce(X, W, sched="unfused", handle=h)
