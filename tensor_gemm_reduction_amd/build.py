@@ -36,23 +36,47 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libtpfuse)")
 
 
+# tpf_kernels.hip is compiled as KERNEL_PARTS translation units (-DTPF_PART=n),
+# in parallel; see the part list at the top of that file.
+KERNEL_PARTS = 7
+
+
+def _compile_jobs(cc: str):
+    jobs = []
+    for part in range(KERNEL_PARTS):
+        obj = os.path.join(LIBDIR, f"tpf_kernels_p{part}.o")
+        jobs.append((f"tpf_kernels.hip (part {part})", obj,
+                     [cc, "-x", "hip", "-c", os.path.join(CSRC, "tpf_kernels.hip"), "-o", obj,
+                      f"-DTPF_PART={part}"] + HIPCC_FLAGS))
+    for src in SOURCES:
+        if src == "tpf_kernels.hip":
+            continue
+        obj = os.path.join(LIBDIR, os.path.splitext(src)[0] + ".o")
+        jobs.append((src, obj, [cc, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + HIPCC_FLAGS))
+    return jobs
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source for gfx950 and link libtpfuse.so; returns its path."""
     os.makedirs(LIBDIR, exist_ok=True)
     cc = hipcc()
-    objs = []
     t0 = time.time()
-    for src in SOURCES:
-        obj = os.path.join(LIBDIR, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + HIPCC_FLAGS
+    jobs = _compile_jobs(cc)
+    procs = []
+    for name, obj, cmd in jobs:
         if verbose:
             print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
-        if verbose and r.stderr.strip():
-            print(r.stderr, file=sys.stderr)
-        objs.append(obj)
+        procs.append((name, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    failed = []
+    for name, pr in procs:
+        out, err = pr.communicate()
+        if pr.returncode != 0:
+            failed.append(f"hipcc failed on {name}:\n{out}\n{err}")
+        elif verbose and err.strip():
+            print(err, file=sys.stderr)
+    if failed:
+        raise RuntimeError("\n".join(failed))
+    objs = [obj for _, obj, _ in jobs]
     tmp = LIB + ".tmp"
     cmd = [cc, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

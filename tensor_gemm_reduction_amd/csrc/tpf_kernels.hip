@@ -25,6 +25,19 @@
 
 #include "tpf_internal.hpp"
 
+// The launchers are split into parts so that the build can compile them as
+// separate translation units in parallel (-DTPF_PART=n, n = 0..6); without
+// TPF_PART every part is compiled.
+//   0: reductions, copies, status, dispatch      1: persistent kernel, large tiles
+//   2: large tiles (plain, tile scheduler)        3: fold epilogue, fp32 messages
+//   4: decode-shaped (small and mid) tiles        5: persistent kernel, small and mid tiles
+//   6: fold epilogue, bf16 messages
+#ifdef TPF_PART
+#define TPF_IN_PART(n) (TPF_PART == (n))
+#else
+#define TPF_IN_PART(n) 1
+#endif
+
 namespace tpf {
 
 // Kernel arguments are read in place from the kernarg segment.  Indexing a
@@ -37,8 +50,10 @@ __device__ __forceinline__ const T& kernarg() {
   return *(const T*)__builtin_amdgcn_kernarg_segment_ptr();
 }
 
+#if TPF_IN_PART(0)
 int cfg_bm(int cfg) { return cfg == CFG_SMALL ? CfgSmall::BM : cfg == CFG_MID ? CfgMid::BM : CfgLarge::BM; }
 int cfg_bn(int cfg) { return cfg == CFG_SMALL ? CfgSmall::BN : cfg == CFG_MID ? CfgMid::BN : CfgLarge::BN; }
+#endif
 
 template <class Cfg>
 __device__ __forceinline__ void store_any(const Frag<Cfg>& f, const TileJob& j, const GemmOperands& g, int shard) {
@@ -128,6 +143,7 @@ __device__ __forceinline__ void reduce_any(const void* P, int64_t stride, int p,
   }
 }
 
+#if TPF_IN_PART(0)
 __global__ __launch_bounds__(256) void reduce_rows_kernel(const void* P, int64_t stride, int p, int64_t e0,
                                                           int64_t e1, int N, ReduceOut o) {
   reduce_any(P, stride, p, e0, e1, N, o, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256);
@@ -140,6 +156,7 @@ __global__ __launch_bounds__(256) void copy_kernel(const char* src, char* dst, i
 __global__ void clear_status_kernel(Ctrl* c) {
   if (threadIdx.x == 0) atomic_store_relaxed(&c->status, 0);
 }
+#endif
 
 // The XCD (accelerator die) this wave runs on, from the hardware register
 // XCC_ID.  Used only as a locality hint.
@@ -501,6 +518,37 @@ __global__ __launch_bounds__(Cfg::THREADS) void tile_kernel(TileArgs args) {
 // Launchers
 // ---------------------------------------------------------------------------
 
+// Per-part launchers (defined in parts 1 to 6, dispatched in part 0).
+void launch_tiles_large(int bl, int red, const TileArgs& a, int grid, hipStream_t s);
+void launch_tiles_fold_f32msg(int bl, int out, const TileArgs& a, int grid, hipStream_t s);
+void launch_tiles_fold_bf16msg(int bl, int out, const TileArgs& a, int grid, hipStream_t s);
+int fused_occupancy_large(int bl);
+int fused_occupancy_small(int cfg, int bl);
+void launch_fused_large(int bl, const FusedArgs& a, int grid, hipStream_t s);
+void launch_fused_small(int cfg, int bl, const FusedArgs& a, int grid, hipStream_t s);
+void launch_tiles_small(int cfg, int bl, int red, const TileArgs& a, int grid, hipStream_t s);
+
+template <class Cfg, int RED>
+static void launch_tile_cfg(int bl, const TileArgs& a, int grid, hipStream_t s) {
+  if constexpr (Cfg::KM_OK && RED == 0) {
+    if (bl == (A_KM | B_KN)) {
+      hipLaunchKernelGGL((tile_kernel<Cfg, A_KM | B_KN, 0>), dim3(grid), dim3(Cfg::THREADS), 0, s, a);
+      return;
+    }
+  }
+  if (bl == B_KN)
+    hipLaunchKernelGGL((tile_kernel<Cfg, B_KN, RED>), dim3(grid), dim3(Cfg::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((tile_kernel<Cfg, B_NK, RED>), dim3(grid), dim3(Cfg::THREADS), 0, s, a);
+}
+
+template <class Cfg>
+static void launch_tile_red(int bl, int red, const TileArgs& a, int grid, hipStream_t s) {
+  if (red == 1) launch_tile_cfg<Cfg, 1>(bl, a, grid, s);
+  else launch_tile_cfg<Cfg, 0>(bl, a, grid, s);
+}
+
+#if TPF_IN_PART(0)
 hipError_t launch_reduce_rows(const void* P, int64_t stride, int p, int row0, int row1, int N,
                               const ReduceOut& o, int num_cus, hipStream_t s) {
   const int64_t e0 = (int64_t)row0 * N, e1 = (int64_t)row1 * N;
@@ -523,80 +571,18 @@ hipError_t launch_copy(const char* src, char* dst, int64_t bytes, int num_cus, h
   return hipGetLastError();
 }
 
-template <class Cfg, int BL>
-static int fused_blocks_per_cu() {
-  static int cached = 0;
-  if (!cached) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fused_kernel<Cfg, BL>, Cfg::THREADS, 0) != hipSuccess ||
-        n < 1)
-      n = 1;
-    cached = n;
-  }
-  return cached;
-}
-
-int fused_occupancy(int cfg, int bl) {
-  if (cfg == CFG_SMALL) return bl == B_KN ? fused_blocks_per_cu<CfgSmall, B_KN>() : fused_blocks_per_cu<CfgSmall, B_NK>();
-  if (cfg == CFG_MID) return bl == B_KN ? fused_blocks_per_cu<CfgMid, B_KN>() : fused_blocks_per_cu<CfgMid, B_NK>();
-  return bl == B_KN ? fused_blocks_per_cu<CfgLargeFused, B_KN>() : fused_blocks_per_cu<CfgLargeFused, B_NK>();
-}
-
-hipError_t launch_fused(int cfg, int bl, const FusedArgs& a, int grid, hipStream_t s) {
-  if (cfg == CFG_SMALL) {
-    if (bl == B_KN)
-      hipLaunchKernelGGL((fused_kernel<CfgSmall, B_KN>), dim3(grid), dim3(CfgSmall::THREADS), 0, s, a);
-    else
-      hipLaunchKernelGGL((fused_kernel<CfgSmall, B_NK>), dim3(grid), dim3(CfgSmall::THREADS), 0, s, a);
-  } else if (cfg == CFG_MID) {
-    if (bl == B_KN)
-      hipLaunchKernelGGL((fused_kernel<CfgMid, B_KN>), dim3(grid), dim3(CfgMid::THREADS), 0, s, a);
-    else
-      hipLaunchKernelGGL((fused_kernel<CfgMid, B_NK>), dim3(grid), dim3(CfgMid::THREADS), 0, s, a);
-  } else {
-    if (bl == B_KN)
-      hipLaunchKernelGGL((fused_kernel<CfgLargeFused, B_KN>), dim3(grid), dim3(CfgLargeFused::THREADS), 0, s, a);
-    else
-      hipLaunchKernelGGL((fused_kernel<CfgLargeFused, B_NK>), dim3(grid), dim3(CfgLargeFused::THREADS), 0, s, a);
-  }
-  return hipGetLastError();
-}
-
-template <class Cfg, int RED>
-static void launch_tile_cfg(int bl, const TileArgs& a, int grid, hipStream_t s) {
-  if constexpr (Cfg::KM_OK && RED == 0) {
-    if (bl == (A_KM | B_KN)) {
-      hipLaunchKernelGGL((tile_kernel<Cfg, A_KM | B_KN, 0>), dim3(grid), dim3(Cfg::THREADS), 0, s, a);
-      return;
-    }
-  }
-  if (bl == B_KN)
-    hipLaunchKernelGGL((tile_kernel<Cfg, B_KN, RED>), dim3(grid), dim3(Cfg::THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL((tile_kernel<Cfg, B_NK, RED>), dim3(grid), dim3(Cfg::THREADS), 0, s, a);
-}
-
-template <class Cfg>
-static void launch_tile_red(int bl, int red, const TileArgs& a, int grid, hipStream_t s) {
-  if (red == 1) launch_tile_cfg<Cfg, 1>(bl, a, grid, s);
-  else launch_tile_cfg<Cfg, 0>(bl, a, grid, s);
-}
-
 hipError_t launch_tiles(int cfg, int bl, int red, const TileArgs& a, hipStream_t s) {
   if (a.tasks <= 0) return hipSuccess;
   const int grid = a.tasks;
   if (red >= 2) {   // fold epilogue: large tiles only
     if (cfg != CFG_LARGE || red > 5) return hipErrorInvalidValue;
-    const int out = ((red - 2) & 1) ? OUT_F32 : OUT_BF16, pb = (red - 2) >> 1;
-    if (out == OUT_BF16 && !pb) launch_tile_cfg<CfgLarge, fold_red(OUT_BF16, 0)>(bl, a, grid, s);
-    else if (out == OUT_F32 && !pb) launch_tile_cfg<CfgLarge, fold_red(OUT_F32, 0)>(bl, a, grid, s);
-    else if (out == OUT_BF16) launch_tile_cfg<CfgLarge, fold_red(OUT_BF16, 1)>(bl, a, grid, s);
-    else launch_tile_cfg<CfgLarge, fold_red(OUT_F32, 1)>(bl, a, grid, s);
+    const int out = ((red - 2) & 1) ? OUT_F32 : OUT_BF16;
+    if ((red - 2) >> 1) launch_tiles_fold_bf16msg(bl, out, a, grid, s);
+    else launch_tiles_fold_f32msg(bl, out, a, grid, s);
     return hipGetLastError();
   }
-  if (cfg == CFG_SMALL) launch_tile_red<CfgSmall>(bl, red, a, grid, s);
-  else if (cfg == CFG_MID) launch_tile_red<CfgMid>(bl, red, a, grid, s);
-  else launch_tile_red<CfgLarge>(bl, red, a, grid, s);
+  if (cfg == CFG_SMALL || cfg == CFG_MID) launch_tiles_small(cfg, bl, red, a, grid, s);
+  else launch_tiles_large(bl, red, a, grid, s);
   return hipGetLastError();
 }
 
@@ -615,5 +601,84 @@ hipError_t launch_clear_status(Ctrl* c, hipStream_t s) {
   hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(64), 0, s, c);
   return hipGetLastError();
 }
+
+int fused_occupancy(int cfg, int bl) {
+  return cfg == CFG_LARGE ? fused_occupancy_large(bl) : fused_occupancy_small(cfg, bl);
+}
+
+hipError_t launch_fused(int cfg, int bl, const FusedArgs& a, int grid, hipStream_t s) {
+  if (cfg == CFG_LARGE) launch_fused_large(bl, a, grid, s);
+  else launch_fused_small(cfg, bl, a, grid, s);
+  return hipGetLastError();
+}
+#endif
+
+template <class Cfg, int BL>
+static int fused_blocks_per_cu() {
+  static int cached = 0;
+  if (!cached) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fused_kernel<Cfg, BL>, Cfg::THREADS, 0) != hipSuccess ||
+        n < 1)
+      n = 1;
+    cached = n;
+  }
+  return cached;
+}
+
+template <class Cfg>
+static void launch_fused_cfg(int bl, const FusedArgs& a, int grid, hipStream_t s) {
+  if (bl == B_KN)
+    hipLaunchKernelGGL((fused_kernel<Cfg, B_KN>), dim3(grid), dim3(Cfg::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((fused_kernel<Cfg, B_NK>), dim3(grid), dim3(Cfg::THREADS), 0, s, a);
+}
+
+#if TPF_IN_PART(1)
+int fused_occupancy_large(int bl) {
+  return bl == B_KN ? fused_blocks_per_cu<CfgLargeFused, B_KN>() : fused_blocks_per_cu<CfgLargeFused, B_NK>();
+}
+void launch_fused_large(int bl, const FusedArgs& a, int grid, hipStream_t s) {
+  launch_fused_cfg<CfgLargeFused>(bl, a, grid, s);
+}
+#endif
+
+#if TPF_IN_PART(5)
+int fused_occupancy_small(int cfg, int bl) {
+  if (cfg == CFG_SMALL) return bl == B_KN ? fused_blocks_per_cu<CfgSmall, B_KN>() : fused_blocks_per_cu<CfgSmall, B_NK>();
+  return bl == B_KN ? fused_blocks_per_cu<CfgMid, B_KN>() : fused_blocks_per_cu<CfgMid, B_NK>();
+}
+void launch_fused_small(int cfg, int bl, const FusedArgs& a, int grid, hipStream_t s) {
+  if (cfg == CFG_SMALL) launch_fused_cfg<CfgSmall>(bl, a, grid, s);
+  else launch_fused_cfg<CfgMid>(bl, a, grid, s);
+}
+#endif
+
+#if TPF_IN_PART(2)
+void launch_tiles_large(int bl, int red, const TileArgs& a, int grid, hipStream_t s) {
+  launch_tile_red<CfgLarge>(bl, red, a, grid, s);
+}
+#endif
+
+#if TPF_IN_PART(3)
+void launch_tiles_fold_f32msg(int bl, int out, const TileArgs& a, int grid, hipStream_t s) {
+  if (out == OUT_BF16) launch_tile_cfg<CfgLarge, fold_red(OUT_BF16, 0)>(bl, a, grid, s);
+  else launch_tile_cfg<CfgLarge, fold_red(OUT_F32, 0)>(bl, a, grid, s);
+}
+#endif
+
+#if TPF_IN_PART(6)
+void launch_tiles_fold_bf16msg(int bl, int out, const TileArgs& a, int grid, hipStream_t s) {
+  if (out == OUT_BF16) launch_tile_cfg<CfgLarge, fold_red(OUT_BF16, 1)>(bl, a, grid, s);
+  else launch_tile_cfg<CfgLarge, fold_red(OUT_F32, 1)>(bl, a, grid, s);
+}
+#endif
+
+#if TPF_IN_PART(4)
+void launch_tiles_small(int cfg, int bl, int red, const TileArgs& a, int grid, hipStream_t s) {
+  if (cfg == CFG_SMALL) launch_tile_red<CfgSmall>(bl, red, a, grid, s);
+  else launch_tile_red<CfgMid>(bl, red, a, grid, s);
+}
+#endif
 
 }  // namespace tpf
