@@ -166,7 +166,8 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def time_mode(sched, steps, warmup):
+    def time_slice(sched, steps, warmup):
+        """Per-step event times (ms) and wall seconds of `steps` steps of one mode."""
         for i in range(warmup):
             call(i, sched)
         torch.cuda.synchronize()
@@ -177,10 +178,26 @@ def main():
             call(i, sched)
             evs[i][1].record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        per = sorted(a.elapsed_time(b) for a, b in evs)
-        return {"ms_median": per[len(per) // 2], "ms_min": per[0], "ms_mean": sum(per) / len(per),
-                "wall_ms_per_step": 1e3 * wall / steps}
+        return [a.elapsed_time(b) for a, b in evs], time.perf_counter() - t0
+
+    def time_modes(mode_list, steps):
+        """Median step time of each mode, measured round-robin (a few steps of
+        every mode per round) so that clock and temperature drift over the
+        run affects all modes alike instead of favouring the first ones."""
+        per = {m: [] for m in mode_list}
+        wall = {m: 0.0 for m in mode_list}
+        chunk = 2
+        for r in range((steps + chunk - 1) // chunk):
+            for m in mode_list:
+                t, w = time_slice(m, chunk, 1 if r else 2)
+                per[m] += t
+                wall[m] += w
+        out = {}
+        for m in mode_list:
+            v = sorted(per[m])
+            out[m] = {"ms_median": v[len(v) // 2], "ms_min": v[0], "ms_mean": sum(v) / len(v),
+                      "wall_ms_per_step": 1e3 * wall[m] / len(v)}
+        return out
 
     # --- settle (untimed, time-bounded), then the warmup steps ---
     settle_steps, t_settle = 0, time.perf_counter()
@@ -254,9 +271,8 @@ def main():
         del g
 
     # --- the other modes (measurement context) ---
-    modes = {}
-    for m in [x for x in args.modes.split(",") if x and x != "none"]:
-        modes[m] = time_mode(m, max(5, args.steps // 2), 2)
+    mode_list = [x for x in args.modes.split(",") if x and x != "none"]
+    modes = time_modes(mode_list, max(6, args.steps // 2)) if mode_list else {}
     extra = {}
     if "gemm_only" in modes and args.sched in modes:
         t_f = modes[args.sched]["ms_median"]

@@ -682,7 +682,7 @@ __device__ __forceinline__ void store_tile(const Frag<Cfg>& f, const TileJob& j,
       for (int v = 0; v < 16; ++v) {
         const int ro = 8 * (v >> 2) + (v & 3);
         const int voff = whole ? vbase : (col_ok && rb + ro < j.rows ? vbase + ro * lds : (int)kOOB);
-        const int soff = whole ? ro * lds : 0;
+        const int soff = __builtin_amdgcn_readfirstlane(whole ? ro * lds : 0);
         const float x = ACT ? gelu_f32(f.acc[i][jn][v]) : f.acc[i][jn][v];
         if constexpr (OUT == OUT_F32)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, voff, soff, 0);
