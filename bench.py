@@ -167,10 +167,12 @@ def main():
     stream = torch.cuda.current_stream()
 
     def time_slice(sched, steps, warmup):
-        """Per-step event times (ms) and wall seconds of `steps` steps of one mode."""
+        """Per-step event times (ms) and wall seconds of `steps` steps of one mode.
+        No synchronisation between the warmup and the timed steps: the GPU is
+        still busy with the warmup while the host enqueues them, so the
+        events do not see host launch latency."""
         for i in range(warmup):
             call(i, sched)
-        torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         t0 = time.perf_counter()
         for i in range(steps):
@@ -181,13 +183,13 @@ def main():
         return [a.elapsed_time(b) for a, b in evs], time.perf_counter() - t0
 
     def time_modes(mode_list, steps):
-        """Median step time of each mode, measured round-robin (a few steps of
+        """Median step time of each mode, measured round-robin (four steps of
         every mode per round) so that clock and temperature drift over the
         run affects all modes alike instead of favouring the first ones."""
         per = {m: [] for m in mode_list}
         wall = {m: 0.0 for m in mode_list}
-        chunk = 2
-        for r in range((steps + chunk - 1) // chunk):
+        chunk = 4
+        for r in range(max(2, (steps + chunk - 1) // chunk)):
             for m in mode_list:
                 t, w = time_slice(m, chunk, 1 if r else 2)
                 per[m] += t

@@ -601,14 +601,10 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
       TPF_TIMED(h, stream_, launch_gemm_rows(cfg, B_KN, g, 0, Mi, stream_));
       return TPF_OK;
     case TPF_SCHED_REDUCE_ONLY:
-      for (int r = 0; r < p; ++r)
-        TPF_HIP(launch_copy(reinterpret_cast<const char*>(X_slices[r]), xg + r * slice_bytes, slice_bytes, h->num_cus,
-                            stream_));
+      TPF_HIP(launch_gather(X_slices, p, xg, slice_bytes, h->num_cus, stream_));
       return TPF_OK;
     case TPF_SCHED_UNFUSED:
-      for (int r = 0; r < p; ++r)
-        TPF_HIP(launch_copy(reinterpret_cast<const char*>(X_slices[r]), xg + r * slice_bytes, slice_bytes, h->num_cus,
-                            stream_));
+      TPF_HIP(launch_gather(X_slices, p, xg, slice_bytes, h->num_cus, stream_));
       TPF_TIMED(h, stream_, launch_gemm_rows(cfg, B_KN, g, 0, Mi, stream_));
       return TPF_OK;
     case TPF_SCHED_TWO_STREAM: {
@@ -751,8 +747,7 @@ int tpf_mlp_sp(tpf_handle h, int p, int64_t S, int64_t Hd, int64_t F, const void
   // AllGather of the sequence slices in rank order.
   const int64_t slice_bytes = (int64_t)(Si / p) * Hi * 2;
   char* xg = reinterpret_cast<char*>(X_gathered);
-  for (int r = 0; r < p; ++r)
-    TPF_HIP(launch_copy(reinterpret_cast<const char*>(X_slices[r]), xg + r * slice_bytes, slice_bytes, h->num_cus, s));
+  TPF_HIP(launch_gather(X_slices, p, xg, slice_bytes, h->num_cus, s));
   // FC1 on the column shards, GeLU in the epilogue, bf16 activations.
   GemmOperands g{};
   for (int k = 0; k < p; ++k) {

@@ -51,6 +51,13 @@ struct GemmOperands {
   int nshard;                 // shard GEMMs (p, or 1 for AllGather->MatMul)
 };
 
+// Sources of a one-launch AllGather (read in place from the kernarg segment).
+struct GatherArgs {
+  const char* src[kMaxShards];
+  char* dst;
+  int64_t slice_bytes;
+};
+
 struct ChunkGeom {
   int n;       // number of chunks
   int base;    // rows of every chunk but the last (floor(M / n))
@@ -196,6 +203,9 @@ int fused_occupancy(int cfg, int bl);   // resident fused workgroups per CU
 // output) + 2 * (bf16 messages), CFG_LARGE only.
 hipError_t launch_tiles(int cfg, int bl, int red, const TileArgs& a, hipStream_t s);
 hipError_t launch_copy(const char* src, char* dst, int64_t bytes, int num_cus, hipStream_t s);
+// AllGather in one launch: slice r (slice_bytes, a multiple of 16) is copied
+// from src[r] to dst + r * slice_bytes, r = 0 .. p-1.
+hipError_t launch_gather(const void* const* src, int p, char* dst, int64_t slice_bytes, int num_cus, hipStream_t s);
 hipError_t launch_clear_status(Ctrl* c, hipStream_t s);
 
 }  // namespace tpf

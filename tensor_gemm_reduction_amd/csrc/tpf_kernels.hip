@@ -153,6 +153,15 @@ __global__ __launch_bounds__(256) void copy_kernel(const char* src, char* dst, i
   copy_range(src, dst, 0, bytes, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256);
 }
 
+// One launch for the whole AllGather: block row y copies slice y.
+__global__ __launch_bounds__(256) void gather_kernel(GatherArgs args) {
+  (void)args;
+  const GatherArgs& a = kernarg<GatherArgs>();
+  const int r = blockIdx.y;
+  copy_range(a.src[r], a.dst + (int64_t)r * a.slice_bytes, 0, a.slice_bytes,
+             (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256);
+}
+
 __global__ void clear_status_kernel(Ctrl* c) {
   if (threadIdx.x == 0) atomic_store_relaxed(&c->status, 0);
 }
@@ -568,6 +577,22 @@ hipError_t launch_copy(const char* src, char* dst, int64_t bytes, int num_cus, h
   const int64_t cap = (int64_t)num_cus * 8;
   if (grid > cap) grid = cap;
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(256), 0, s, src, dst, bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const void* const* src, int p, char* dst, int64_t slice_bytes, int num_cus, hipStream_t s) {
+  const int64_t chunks = slice_bytes / 16;
+  if (chunks <= 0 || p <= 0) return hipSuccess;
+  if (p > kMaxShards) return hipErrorInvalidValue;
+  GatherArgs a{};
+  for (int r = 0; r < p; ++r) a.src[r] = reinterpret_cast<const char*>(src[r]);
+  a.dst = dst;
+  a.slice_bytes = slice_bytes;
+  int64_t gx = (chunks + 256 * 4 - 1) / (256 * 4);
+  int64_t cap = (int64_t)num_cus * 8 / p;
+  if (cap < 1) cap = 1;
+  if (gx > cap) gx = cap;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)gx, (unsigned)p), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
