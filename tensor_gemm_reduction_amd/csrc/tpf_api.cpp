@@ -21,7 +21,14 @@ using namespace tpf;
 static_assert(TPF_MAX_SHARDS == kMaxShards, "shard limit mismatch");
 static_assert(TPF_MAX_CHUNKS == kMaxChunks, "chunk limit mismatch");
 
-constexpr int kKernelTimes = 256;   // debug kernel-timing records held per handle
+constexpr int kKernelTimes = 256;
+
+// The two-stream scheduler's chunk reductions run on a grid capped at a
+// quarter of the usual size (2 workgroups per CU): they then trickle beside
+// the next chunks' GEMM tiles instead of taking every CU at once (measured
+// 2-3 % faster for that scheduler on sp_rs and dx_bwd; a half or an eighth
+// were slower).
+constexpr int kSideReduceCuDiv = 4;   // debug kernel-timing records held per handle
 
 struct tpf_context {
   int device = 0;
@@ -276,7 +283,8 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
         TPF_HIP(launch_gemm_rows(cfg, rc.bl, g, ch.row0(c), ch.row1(c), gs));
         TPF_HIP(hipEventRecord(h->ev_chunk[c], gs));
         TPF_HIP(hipStreamWaitEvent(h->side, h->ev_chunk[c], 0));
-        TPF_HIP(launch_reduce_rows(rc.P, stride, rc.p, ch.row0(c), ch.row1(c), rc.N, rc.ro, h->num_cus, h->side));
+        TPF_HIP(launch_reduce_rows(rc.P, stride, rc.p, ch.row0(c), ch.row1(c), rc.N, rc.ro,
+                                   std::max(1, h->num_cus / kSideReduceCuDiv), h->side));
       }
       TPF_HIP(hipEventRecord(h->ev_join, h->side));
       TPF_HIP(hipEventRecord(h->ev_join2, h->gemm2));
