@@ -21,14 +21,14 @@ using namespace tpf;
 static_assert(TPF_MAX_SHARDS == kMaxShards, "shard limit mismatch");
 static_assert(TPF_MAX_CHUNKS == kMaxChunks, "chunk limit mismatch");
 
-constexpr int kKernelTimes = 256;
+constexpr int kKernelTimes = 256;   // debug kernel-timing records held per handle
 
 // The two-stream scheduler's chunk reductions run on a grid capped at a
 // quarter of the usual size (2 workgroups per CU): they then trickle beside
 // the next chunks' GEMM tiles instead of taking every CU at once (measured
 // 2-3 % faster for that scheduler on sp_rs and dx_bwd; a half or an eighth
 // were slower).
-constexpr int kSideReduceCuDiv = 4;   // debug kernel-timing records held per handle
+constexpr int kSideReduceCuDiv = 4;
 
 struct tpf_context {
   int device = 0;
