@@ -102,7 +102,7 @@ def main():
         sets.append(inp)
     M, N, K, p = wl.M, wl.N, wl.K, wl.p
     flops = wl.flops()
-    kbytes = kernel_bytes(wl, 2 if args.message == "bf16" else 4)
+    kbytes = kernel_bytes(wl, 2 if args.message == "bf16" else 4, args.sched)
     kflops = flops / 2 if wl.op == "mlp_sp" else flops    # the timed launch of the MLP block is FC2
     msg = args.message
 
@@ -322,7 +322,7 @@ def main():
         "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
                      "algorithmic_bytes": kbytes, "algorithmic_flops": kflops,
-                     "kernel": kernel_name(args.sched, wl.op),
+                     "kernel": kernel_name(args.sched, wl.op, wl.M),
                      "avg_kernel_ms": round(avg_kernel_ms, 4),
                      "timed_launches": len(kern_ms),
                      "avg_step_event_ms": round(sum(step_ms) / len(step_ms), 4)},
@@ -334,11 +334,16 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def kernel_bytes(wl, part_bytes=4):
+def kernel_bytes(wl, part_bytes=4, sched="unfused"):
     """Algorithmic HBM bytes of one launch of the shard-GEMM kernel: every
     operand read once and every output written once (the partials of the
-    reducing ops, `part_bytes` per element; the bf16 output of AllGather)."""
+    reducing ops, `part_bytes` per element; the bf16 output of AllGather).
+    For the fold scheduler's pair of launches: the operands once, the
+    partials of p - 1 shards written and read back once, the bf16 result
+    written once."""
     p, M, N, K = wl.p, wl.M, wl.N, wl.K
+    if resolved_sched(sched, wl.op, M) == "fold" and wl.op in ("allreduce", "reducescatter", "mlp_sp"):
+        return p * (2.0 * M * K + 2.0 * K * N) + 2.0 * (p - 1) * part_bytes * M * N + 2.0 * M * N
     if wl.op == "allgather":
         return 2.0 * M * K + 2.0 * K * N + 2.0 * M * N
     if wl.op.startswith("wgrad"):   # A_k [M, K], B_k [M, N], dW_k [K, N] fp32
@@ -350,11 +355,25 @@ def kernel_bytes(wl, part_bytes=4):
     return p * (2.0 * M * K + 2.0 * K * N + part_bytes * M * N)
 
 
-def kernel_name(sched, op=""):
-    """The kernel that dominates one step of `sched` (what `roofline` prices)."""
+def resolved_sched(sched, op, M):
+    """The scheduler the library runs for `sched` (AUTO: the fold scheduler
+    for reductions of row-major weights with M > 64, GEMM-then-reduce
+    otherwise; the same rule as the library's)."""
+    if sched != "auto":
+        return sched
+    return "fold" if op in ("allreduce", "reducescatter", "mlp_sp") and M > 64 else "unfused"
+
+
+def kernel_name(sched, op="", M=0):
+    """The kernel (or, for the fold scheduler, the pair of launches) that
+    dominates one step of `sched`: what `roofline` prices."""
+    sched = resolved_sched(sched, op, M)
     if op.startswith("wgrad"):
         return "tile_kernel A_KM (weight-gradient GEMM tiles, transposed A)"
     if op == "mlp_sp":
+        if sched == "fold":
+            return ("tile_kernel pair (FC2: shards 0..p-2 into partials, then shard p-1 with the fold epilogue; "
+                    "FC1 with GeLU runs before it)")
         return "tile_kernel RED=0 (FC2 shard GEMM tiles; FC1 with GeLU runs before it)"
     if sched == "persistent":
         return "fused_kernel (persistent: shard GEMM tiles + chunk reductions)"

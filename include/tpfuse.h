@@ -76,8 +76,12 @@ extern "C" {
 
 /* Schedulers.  Every scheduler computes the same bits. */
 #define TPF_SCHED_AUTO 0         /* library's choice.  With every shard on one GPU the reduction shares HBM
-                                    and L2 with the GEMM, and overlapping it costs more than it hides, so
-                                    AUTO runs UNFUSED; the chunked schedulers are chosen explicitly. */
+                                    and L2 with the GEMM, and overlapping it chunk by chunk costs more
+                                    than it hides; folding it into the last shard's GEMM epilogue does
+                                    pay.  AUTO runs TPF_SCHED_FOLD for the reductions of row-major
+                                    weights (MatMul->AllReduce, MatMul->ReduceScatter, the MLP block's
+                                    FC2) when M > 64, and TPF_SCHED_UNFUSED otherwise (dX, decode-shaped
+                                    M, AllGather->MatMul).  Every scheduler gives the same bits. */
 #define TPF_SCHED_PERSISTENT 1   /* one persistent kernel: work queue + per-chunk ready counters */
 #define TPF_SCHED_TWO_STREAM 2   /* per-chunk GEMM launches (alternating between the caller's stream and a
                                     second handle stream), reductions on a side stream after per-chunk

@@ -152,17 +152,26 @@ int check_handle(tpf_handle h) {
 // the whole collective separately first (§04), and expect chunking to slow
 // the GEMM and decode shapes to lack chunkable work (§03, §05).  Here every
 // shard lives on one GPU, so the "messages" travel through the same HBM and
-// L2 as the GEMM's operands: overlapping the reduction costs per-chunk
-// cross-XCD release/acquire, smaller GEMM launches or weights re-read once
-// per chunk, and on MI355X each of those costs more than the reduction it
-// hides (5-10 % of the GEMM at these shapes).  AUTO therefore runs the GEMM
-// kernel followed by the reduction kernel, a kernel boundary being the
-// cheapest device-wide barrier; the chunked schedulers are selected
-// explicitly.
+// L2 as the GEMM's operands: overlapping a chunk's reduction with later
+// chunks' GEMMs costs per-chunk cross-XCD release/acquire, smaller GEMM
+// launches or weights re-read once per chunk, and on MI355X each of those
+// costs more than the reduction it hides.  What does pay is folding the
+// reduction into the last shard's GEMM epilogue (FOLD): no partial of that
+// shard is written or read back, there is no separate reduction pass, and
+// its epilogue's partial reads overlap other tiles' MFMA work.  AUTO runs
+// FOLD for reductions of row-major (KN) weights on the large tiles (measured
+// 4-6 % faster than GEMM-then-reduce on the Llama down projection and the
+// sequence-parallel ReduceScatter) and UNFUSED elsewhere (the transposed-
+// weight dX measured 2 % slower with FOLD; decode shapes have one shard's
+// tiles too few to fill the GPU).  AllGather->MatMul has no reduction and
+// runs UNFUSED.  The chunked schedulers are chosen explicitly.
 int resolve_sched(int sched, int n_chunks) {
   (void)n_chunks;
-  const int base = sched & 0xff;
-  return base == TPF_SCHED_AUTO ? TPF_SCHED_UNFUSED : base;
+  return sched & 0xff;   // AUTO stays AUTO here; each op resolves it below
+}
+
+int auto_reduce_sched(int bl, int cfg) {
+  return bl == B_KN && cfg == CFG_LARGE ? TPF_SCHED_FOLD : TPF_SCHED_UNFUSED;
 }
 
 // A reducing op (row-parallel AR/RS, or dX with either semantic).
@@ -257,7 +266,8 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
 
   // One shard's tiles of a small-M problem cannot fill the GPU: the fold
   // scheduler then runs as UNFUSED (the same bits either way).
-  const int sched = rc.sched == TPF_SCHED_FOLD && cfg != CFG_LARGE ? TPF_SCHED_UNFUSED : rc.sched;
+  int sched = rc.sched == TPF_SCHED_AUTO ? auto_reduce_sched(rc.bl, cfg) : rc.sched;
+  if (sched == TPF_SCHED_FOLD && cfg != CFG_LARGE) sched = TPF_SCHED_UNFUSED;
   switch (sched) {
     case TPF_SCHED_GEMM_ONLY:
       TPF_TIMED(h, stream, launch_gemm_rows(cfg, rc.bl, g, 0, rc.M, stream));
@@ -603,7 +613,7 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
   ChunkGeom ch{n_chunks, Mi / n_chunks, Mi};
   int s = resolve_sched(sched, n_chunks);
   if (s == TPF_SCHED_TILE) s = TPF_SCHED_PERSISTENT;   // no reduction to fold into the tiles
-  if (s == TPF_SCHED_FOLD) s = TPF_SCHED_UNFUSED;
+  if (s == TPF_SCHED_FOLD || s == TPF_SCHED_AUTO) s = TPF_SCHED_UNFUSED;
   switch (s) {
     case TPF_SCHED_GEMM_ONLY:
       TPF_TIMED(h, stream_, launch_gemm_rows(cfg, B_KN, g, 0, Mi, stream_));

@@ -397,59 +397,96 @@ __device__ __forceinline__ float message_value(float acc) {
   else return acc;
 }
 
-template <class Cfg, int OUT, int PB>
-__device__ __forceinline__ void fold_store(const Frag<Cfg>& f, const TileJob& j, const TileArgs& a) {
-  constexpr int G = 4, QB = 8;   // shards and rows per batch of loads
+// The fold epilogue streams the partials with 16-byte loads: the tile's
+// accumulators are staged through the (idle) LDS stage 0 in bands of
+// FOLD_BAND rows, then every thread takes groups of four consecutive
+// columns of a band row, loads the p-1 partials of those elements, adds them
+// in shard order and then its own value, and stores the four results.
+template <class Cfg>
+struct FoldBand {
+  static constexpr int ROWS = 64;                         // rows per band
+  static_assert(Cfg::BM % ROWS == 0 && Cfg::WM % 32 == 0 && ROWS % 32 == 0, "bands of whole 32-row blocks");
+  static_assert(ROWS * Cfg::BN * 4 <= Cfg::LDS_STAGE, "a band fits one LDS stage");
+};
+
+// Sum of the partials of shards 0 .. np-1 at elements e .. e+3, left to right
+// (PP > 0: np == PP at compile time, all loads issued first).
+template <int PP, int PB>
+__device__ __forceinline__ f32x4_t fold_partials4(const void* P, int64_t stride, int np, int64_t e) {
+  if constexpr (PP > 0) {
+    f32x4_t v[PP];
+#pragma unroll
+    for (int k = 0; k < PP; ++k) v[k] = load_partial4<PB>(P, (int64_t)k * stride + e);
+    f32x4_t s = v[0];
+#pragma unroll
+    for (int k = 1; k < PP; ++k) s = s + v[k];
+    return s;
+  } else {
+    f32x4_t s = load_partial4<PB>(P, e);
+    for (int k = 1; k < np; ++k) s = s + load_partial4<PB>(P, (int64_t)k * stride + e);
+    return s;
+  }
+}
+
+template <class Cfg, int OUT, int PB, int PP>
+__device__ __forceinline__ void fold_store_pp(const Frag<Cfg>& f, const TileJob& j, const TileArgs& a) {
+  constexpr int BR = FoldBand<Cfg>::ROWS;
+  constexpr int GROUPS = BR * Cfg::BN / 4;                 // four-column groups per band
+  constexpr int PER = GROUPS / Cfg::THREADS;
+  static_assert(GROUPS % Cfg::THREADS == 0, "whole groups per thread");
+  float* band = reinterpret_cast<float*>(stage_ptr<Cfg, 0>());   // [BR][BN] fp32
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   const int r32 = lane & 31, half = lane >> 5;
   const int np = a.p - 1;
   const int N = j.N;
+  const int ncols = min(Cfg::BN, N - j.n0);                // a multiple of 8
 #pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i) {
+  for (int b0 = 0; b0 < Cfg::BM; b0 += BR) {
+    if (b0 >= j.rows) break;                               // the same for the whole workgroup
+    // This band's 32-row blocks go to LDS.
 #pragma unroll
-    for (int jn = 0; jn < Cfg::TN; ++jn) {
-      const int col = j.n0 + wn * Cfg::WN + jn * 32 + r32;
-      const bool col_ok = col < N;
-      const int rbase = wm * Cfg::WM + i * 32 + 4 * half;
+    for (int i = 0; i < Cfg::TM; ++i) {
+      const int r0 = wm * Cfg::WM + i * 32;
+      if (r0 >= b0 && r0 < b0 + BR) {
 #pragma unroll
-      for (int q0 = 0; q0 < 16; q0 += QB) {
-        float s[QB];
+        for (int jn = 0; jn < Cfg::TN; ++jn) {
+          const int col = wn * Cfg::WN + jn * 32 + r32;
 #pragma unroll
-        for (int k0 = 0; k0 < kMaxShards - 1; k0 += G) {
-          if (k0 >= np) break;
-          float v[G][QB];
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            if (k0 + g < np) {
-              const int64_t base = (int64_t)(k0 + g) * a.p_stride;
-#pragma unroll
-              for (int qq = 0; qq < QB; ++qq) {
-                const int q = q0 + qq;
-                const int row = rbase + 8 * (q >> 2) + (q & 3);
-                v[g][qq] = row < j.rows && col_ok ? load_partial1<PB>(a.P, base + (int64_t)(j.m0 + row) * N + col)
-                                                  : 0.0f;
-              }
-            }
+          for (int v = 0; v < 16; ++v) {
+            const int row = r0 - b0 + 8 * (v >> 2) + 4 * half + (v & 3);
+            band[row * Cfg::BN + col] = f.acc[i][jn][v];
           }
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            if (k0 + g < np) {
-#pragma unroll
-              for (int qq = 0; qq < QB; ++qq) s[qq] = (k0 + g == 0) ? v[g][qq] : s[qq] + v[g][qq];
-            }
-          }
-        }
-#pragma unroll
-        for (int qq = 0; qq < QB; ++qq) {
-          const int q = q0 + qq;
-          const int row = rbase + 8 * (q >> 2) + (q & 3);
-          const float own = message_value<PB>(f.acc[i][jn][q]);
-          if (row < j.rows && col_ok)
-            reduce_store1<OUT>(a.ro, (int64_t)(j.m0 + row) * N + col, N, np > 0 ? s[qq] + own : own);
         }
       }
     }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int g = q * Cfg::THREADS + threadIdx.x;
+      const int row = g / (Cfg::BN / 4), c = (g % (Cfg::BN / 4)) * 4;
+      if (b0 + row < j.rows && c < ncols) {
+        const int64_t e = (int64_t)(j.m0 + b0 + row) * N + j.n0 + c;
+        // This shard's own values as the message it would have stored
+        // (rounded to bf16 first for 2-byte messages).
+        f32x4_t own = *reinterpret_cast<const f32x4_t*>(band + row * Cfg::BN + c);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) own[t] = message_value<PB>(own[t]);
+        const f32x4_t s = np > 0 ? fold_partials4<PP, PB>(a.P, a.p_stride, np, e) + own : own;
+        reduce_store4<OUT>(a.ro, e, N, s);
+      }
+    }
+    __syncthreads();                                       // the band is free again
+  }
+}
+
+template <class Cfg, int OUT, int PB>
+__device__ __forceinline__ void fold_store(const Frag<Cfg>& f, const TileJob& j, const TileArgs& a) {
+  switch (a.p) {   // the partials of the other shards: p - 1 of them
+    case 2: fold_store_pp<Cfg, OUT, PB, 1>(f, j, a); break;
+    case 4: fold_store_pp<Cfg, OUT, PB, 3>(f, j, a); break;
+    case 8: fold_store_pp<Cfg, OUT, PB, 7>(f, j, a); break;
+    default: fold_store_pp<Cfg, OUT, PB, 0>(f, j, a); break;
   }
 }
 

@@ -45,8 +45,11 @@ def _rows(path_or_dir: str, suffix: str):
 
 
 def last_dispatches(trace_path: str, name_sub: str, k: int):
-    """Average duration (us) of the last k dispatches of the kernel whose name
-    contains name_sub and that takes the most total time in the trace."""
+    """Average duration (us) of the last k dispatches of each kernel whose name
+    contains name_sub, summed over those kernels: one launch per step gives
+    that launch's average; the fold scheduler's two launches per step (the
+    partial GEMMs, then the last shard with the fold epilogue) give the
+    average of the pair."""
     by_name = {}
     for r in _rows(trace_path, "kernel_trace.csv"):
         if name_sub in r["Kernel_Name"]:
@@ -54,17 +57,26 @@ def last_dispatches(trace_path: str, name_sub: str, k: int):
             by_name.setdefault(r["Kernel_Name"], []).append((t0, t1 - t0))
     if not by_name:
         return None
-    name = max(by_name, key=lambda n: sum(d for _, d in by_name[n]))
-    last = sorted(by_name[name])[-k:]
-    return name, sum(d for _, d in last) / len(last) / 1e3, len(last)
+    total, n = 0.0, 0
+    for name in by_name:
+        last = sorted(by_name[name])[-k:]
+        total += sum(d for _, d in last) / len(last) / 1e3
+        n = len(last)
+    names = sorted(by_name, key=lambda m: -sum(d for _, d in by_name[m]))
+    label = names[0] if len(names) == 1 else f"{len(names)} kernels per step ({', '.join(m[:40] for m in names)})"
+    return label, total, n
 
 
 def counter_per_dispatch(path: str, counter: str, kernel_sub: str) -> float:
-    vals = [float(r["Counter_Value"]) for r in _rows(path, "counter_collection.csv")
-            if r.get("Counter_Name") == counter and kernel_sub in r.get("Kernel_Name", "")]
-    if not vals:
+    """Per-dispatch average of `counter` for each kernel whose name contains
+    kernel_sub, summed over those kernels (see last_dispatches)."""
+    by_name = {}
+    for r in _rows(path, "counter_collection.csv"):
+        if r.get("Counter_Name") == counter and kernel_sub in r.get("Kernel_Name", ""):
+            by_name.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    if not by_name:
         raise SystemExit(f"no {counter} samples for kernels matching {kernel_sub!r} in {path}")
-    return sum(vals) / len(vals)
+    return sum(sum(v) / len(v) for v in by_name.values())
 
 
 def stats(csv_path: str, out_path: str, command: str, bench_json: str = "") -> None:
@@ -86,7 +98,7 @@ def stats(csv_path: str, out_path: str, command: str, bench_json: str = "") -> N
         last = last_dispatches(csv_path, r["kernel"].split()[0], k) if k else None
         if last:
             name, avg_us, n = last
-            lines += ["", f"# rocprofv3, the last {n} dispatches of {name[:70]}",
+            lines += ["", f"# rocprofv3, the last {n} dispatches of {name[:150]}",
                       f"#   (the bench's timed launches; earlier ones are its settle and warmup steps): "
                       f"average {avg_us:.2f} us"]
         lines += ["", f"# bench.py (same run): dominant kernel = {r['kernel']}",

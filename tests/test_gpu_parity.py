@@ -16,7 +16,7 @@ from tests.parity import (assert_bf16, assert_bf16_is_rne_of_f32, assert_bitwise
 
 pytestmark = pytest.mark.gpu
 
-SCHEDS = ["persistent", "two_stream", "unfused", "tile", "fold"]
+SCHEDS = ["persistent", "two_stream", "unfused", "tile", "fold", "auto"]
 DEV = "cuda"
 
 
