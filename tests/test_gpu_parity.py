@@ -274,7 +274,9 @@ def assert_message_bf16(y32, parts, ref16, what):
     assert (y == ref16).mean() > 0.9, f"{what}: only {(y == ref16).mean():.3f} exact"
 
 
-@pytest.mark.parametrize("p,M,N,K", [(3, 300, 328, 200), (4, 64, 392, 136), (8, 16, 1024, 256)])
+@pytest.mark.parametrize("p,M,N,K", [(3, 300, 328, 200), (4, 64, 392, 136), (8, 16, 1024, 256),
+                                     # large tiles with the fold epilogue's p = 4 and p = 8 variants
+                                     (4, 300, 264, 136), (8, 264, 136, 72)])
 def test_message_bf16_allreduce(p, M, N, K):
     say(f"message bf16 allreduce p={p} M={M} N={N} K={K}")
     Xh = shards([(M, K)] * p, ("normal", 1.0), 81)
