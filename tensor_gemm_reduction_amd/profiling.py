@@ -11,6 +11,10 @@
       bytes of a plain device copy of known size and what the same counter
       reports for it.  The record carries a hash of the kernel sources; the
       benchmark only reports it while the sources still match.
+
+  python -m tensor_gemm_reduction_amd.profiling mfma <counter dir> <kernel-substring> <out.txt> <command...>
+      Matrix-core busy fraction, the clock the GPU ran at and TFLOP/s per
+      dispatch, from one --pmc pass over MFMA_COUNTERS.
 """
 from __future__ import annotations
 
@@ -141,6 +145,49 @@ def traffic(workload, sched, kernel_sub, fetch_csv, write_csv, cfetch_csv, cwrit
     print(json.dumps(rec, indent=1))
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT "
+                 "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_WAVE_CYCLES GRBM_GUI_ACTIVE GRBM_COUNT")
+
+
+def mfma(counter_dir: str, kernel_sub: str, out_path: str, command: str = "", xcds: int = 8, cus: int = 256,
+         simds_per_cu: int = 4, flop_per_clk_simd: int = 1024) -> None:
+    """Matrix-core utilisation of each dispatch of the kernels matching
+    kernel_sub, from one rocprofv3 --pmc pass over MFMA_COUNTERS:
+      clock      = GRBM_GUI_ACTIVE per XCD / dispatch duration (the clock the
+                   GPU actually ran at, against 2.4 GHz for the published peak)
+      MFMA busy  = SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x SIMDs)
+      TFLOP/s    = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / duration
+      peak@clock = SIMDs x 1024 bf16 flop/clk x clock."""
+    by = {}
+    for r in _rows(counter_dir, "counter_collection.csv"):
+        if kernel_sub not in r.get("Kernel_Name", ""):
+            continue
+        d = by.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"],
+                                             "dur": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    if not by:
+        raise SystemExit(f"no dispatches of {kernel_sub!r} in {counter_dir}")
+    simds = cus * simds_per_cu
+    lines = ["# rocprofv3 hardware counters: matrix-core utilisation per dispatch",
+             f"# command: {command}", f"# counters: {MFMA_COUNTERS}", "",
+             f"{'dispatch':>8s} {'kernel':40s} {'dur_us':>8s} {'clk_GHz':>8s} {'mfma_busy':>9s} "
+             f"{'TFLOP/s':>8s} {'peak@clk':>8s} {'frac@clk':>8s} {'frac@2.4':>8s} {'lds_conf':>8s}"]
+    for k in sorted(by, key=int):
+        d = by[k]
+        dur = d["dur"] * 1e-9
+        active = d["GRBM_GUI_ACTIVE"] / xcds
+        clk = active / dur
+        busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * simds)
+        tf = d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / dur / 1e12
+        peak = simds * flop_per_clk_simd * clk / 1e12
+        lines.append(f"{k:>8s} {d['name'][:40]:40s} {dur * 1e6:8.1f} {clk / 1e9:8.3f} {100 * busy:8.1f}% "
+                     f"{tf:8.0f} {peak:8.0f} {tf / peak:8.3f} {tf / (simds * flop_per_clk_simd * 2.4e9 / 1e12):8.3f} "
+                     f"{int(d['SQ_LDS_BANK_CONFLICT']):8d}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def load_traffic(workload: str, profiles_dir: str):
     """HBM bytes per dispatch recorded for `workload`, or None if absent or stale."""
     path = os.path.join(profiles_dir, f"traffic_{workload}.json")
@@ -160,5 +207,8 @@ if __name__ == "__main__":
         stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[5:]), "" if sys.argv[4] == "-" else sys.argv[4])
     elif cmd == "traffic":
         traffic(*sys.argv[2:11], command=" ".join(sys.argv[11:]))
+    elif cmd == "mfma":
+        # mfma <counter dir> <kernel-substring> <out.txt> <command...>
+        mfma(sys.argv[2], sys.argv[3], sys.argv[4], command=" ".join(sys.argv[5:]))
     else:
         raise SystemExit(__doc__)
