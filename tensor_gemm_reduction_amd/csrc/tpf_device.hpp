@@ -87,36 +87,6 @@ __device__ __forceinline__ void reduce_store4(const ReduceOut& o, int64_t e, int
   }
 }
 
-// One partial at element e, widened to fp32 (PB = 1: bf16, PB = 0: fp32).
-template <int PB>
-__device__ __forceinline__ float load_partial1(const void* P, int64_t e) {
-  if constexpr (PB)
-    return __uint_as_float((uint32_t)__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(P) + e) << 16);
-  else
-    return __builtin_nontemporal_load(reinterpret_cast<const float*>(P) + e);
-}
-
-// Store one reduced element e (row-major index into the [M][N] result) into
-// the AllReduce or ReduceScatter destination, rounded once to OUT.
-template <int OUT>
-__device__ __forceinline__ void reduce_store1(const ReduceOut& o, int64_t e, int N, float s) {
-  void* base;
-  int64_t off;
-  if (o.scatter) {
-    const int64_t row = e / N;
-    const int sl = (int)(row / o.rows_per_slice);
-    base = o.y[sl];
-    off = e - (int64_t)sl * o.rows_per_slice * N;
-  } else {
-    base = o.y[0];
-    off = e;
-  }
-  if constexpr (OUT == OUT_F32)
-    reinterpret_cast<float*>(base)[off] = s;
-  else
-    reinterpret_cast<uint16_t*>(base)[off] = (uint16_t)f32_to_bf16_bits(s);
-}
-
 // Reduce elements [e0, e1) (multiples of 4) with `nthr` cooperating threads
 // numbered `t`.  P is compile-time when PP > 0 (loads of all shards are then
 // issued together), run-time otherwise.

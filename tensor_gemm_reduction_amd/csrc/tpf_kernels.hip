@@ -399,7 +399,7 @@ __device__ __forceinline__ float message_value(float acc) {
 
 // The fold epilogue streams the partials with 16-byte loads: the tile's
 // accumulators are staged through the (idle) LDS stage 0 in bands of
-// FOLD_BAND rows, then every thread takes groups of four consecutive
+// FoldBand::ROWS rows, then every thread takes groups of four consecutive
 // columns of a band row, loads the p-1 partials of those elements, adds them
 // in shard order and then its own value, and stores the four results.
 template <class Cfg>
