@@ -102,7 +102,6 @@ def main():
         sets.append(inp)
     M, N, K, p = wl.M, wl.N, wl.K, wl.p
     flops = wl.flops()
-    kbytes = kernel_bytes(wl, 2 if args.message == "bf16" else 4, args.sched)
     kflops = flops / 2 if wl.op == "mlp_sp" else flops    # the timed launch of the MLP block is FC2
     msg = args.message
 
@@ -229,6 +228,10 @@ def main():
         raise RuntimeError(f"fused path reported status {st}")
     launch_ms = handle.kernel_times(args.steps)
     handle.set_kernel_timing(False)
+    # the scheduler the library ran for args.sched (AUTO resolved): it names
+    # the timed kernels and sets their algorithmic bytes
+    ran = handle.last_sched() or args.sched
+    kbytes = kernel_bytes(wl, 2 if args.message == "bf16" else 4, ran)
     step_ms = [a.elapsed_time(b) for a, b in evs]
     ms_per_step = 1e3 * wall / args.steps
     kern_ms = launch_ms if launch_ms else step_ms    # two_stream records no single dominant launch
@@ -316,13 +319,13 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "op": wl.op, "p": p, "M": M, "N": N, "K_shard": K,
-                   "n_chunks": n, "sched": args.sched, "out": "bf16", "message": args.message,
+                   "n_chunks": n, "sched": args.sched, "sched_ran": ran, "out": "bf16", "message": args.message,
                    "input_sets": args.sets,
                    "workspace_bytes": ws_bytes, "note": wl.note},
         "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
                      "algorithmic_bytes": kbytes, "algorithmic_flops": kflops,
-                     "kernel": kernel_name(args.sched, wl.op, wl.M),
+                     "kernel": kernel_name(ran, wl.op),
                      "avg_kernel_ms": round(avg_kernel_ms, 4),
                      "timed_launches": len(kern_ms),
                      "avg_step_event_ms": round(sum(step_ms) / len(step_ms), 4)},
@@ -342,7 +345,7 @@ def kernel_bytes(wl, part_bytes=4, sched="unfused"):
     partials of p - 1 shards written and read back once, the bf16 result
     written once."""
     p, M, N, K = wl.p, wl.M, wl.N, wl.K
-    if resolved_sched(sched, wl.op, M) == "fold" and wl.op in ("allreduce", "reducescatter", "mlp_sp"):
+    if sched == "fold" and wl.op in ("allreduce", "reducescatter", "mlp_sp"):
         return p * (2.0 * M * K + 2.0 * K * N) + 2.0 * (p - 1) * part_bytes * M * N + 2.0 * M * N
     if wl.op == "allgather":
         return 2.0 * M * K + 2.0 * K * N + 2.0 * M * N
@@ -355,19 +358,10 @@ def kernel_bytes(wl, part_bytes=4, sched="unfused"):
     return p * (2.0 * M * K + 2.0 * K * N + part_bytes * M * N)
 
 
-def resolved_sched(sched, op, M):
-    """The scheduler the library runs for `sched` (AUTO: the fold scheduler
-    for reductions of row-major weights with M > 64, GEMM-then-reduce
-    otherwise; the same rule as the library's)."""
-    if sched != "auto":
-        return sched
-    return "fold" if op in ("allreduce", "reducescatter", "mlp_sp") and M > 64 else "unfused"
-
-
-def kernel_name(sched, op="", M=0):
+def kernel_name(sched, op=""):
     """The kernel (or, for the fold scheduler, the pair of launches) that
-    dominates one step of `sched`: what `roofline` prices."""
-    sched = resolved_sched(sched, op, M)
+    dominates one step of the scheduler the library ran: what `roofline`
+    prices."""
     if op.startswith("wgrad"):
         return "tile_kernel A_KM (weight-gradient GEMM tiles, transposed A)"
     if op == "mlp_sp":

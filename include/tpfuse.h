@@ -78,10 +78,15 @@ extern "C" {
 #define TPF_SCHED_AUTO 0         /* library's choice.  With every shard on one GPU the reduction shares HBM
                                     and L2 with the GEMM, and overlapping it chunk by chunk costs more
                                     than it hides; folding it into the last shard's GEMM epilogue does
-                                    pay.  AUTO runs TPF_SCHED_FOLD for the reductions of row-major
-                                    weights (MatMul->AllReduce, MatMul->ReduceScatter, the MLP block's
-                                    FC2) when M > 64, and TPF_SCHED_UNFUSED otherwise (dX, decode-shaped
-                                    M, AllGather->MatMul).  Every scheduler gives the same bits. */
+                                    pay when the last shard's tiles fill whole waves of the GPU.  AUTO
+                                    runs TPF_SCHED_FOLD for the reductions of row-major weights
+                                    (MatMul->AllReduce, MatMul->ReduceScatter, the MLP block's FC2) on
+                                    the large tiles (M > 64) when the p-1 shards' tiles and the last
+                                    shard's tiles take no more waves of one-tile-per-CU workgroups
+                                    than all p shards' tiles together, and TPF_SCHED_UNFUSED otherwise
+                                    (and for dX, decode-shaped M, AllGather->MatMul);
+                                    tpf_debug_last_sched reports the choice.  Every scheduler gives
+                                    the same bits. */
 #define TPF_SCHED_PERSISTENT 1   /* one persistent kernel: work queue + per-chunk ready counters */
 #define TPF_SCHED_TWO_STREAM 2   /* per-chunk GEMM launches (alternating between the caller's stream and a
                                     second handle stream), reductions on a side stream after per-chunk
@@ -272,6 +277,12 @@ int tpf_debug_set_kernel_timing(tpf_handle h, int enable);
  * durations in milliseconds into `ms` (host array), oldest first.  Returns
  * the number written (>= 0) or a negative status; clears the records. */
 int tpf_debug_kernel_times(tpf_handle h, float* ms, int max);
+
+/* The scheduler (a TPF_SCHED_* value, with TPF_SCHED_AUTO resolved and
+ * any fallback applied) that the last reducing or AllGather->MatMul call on
+ * the handle ran, or -1 before the first; negative status for a NULL handle.
+ * For measurement tools that must name the kernels a call ran. */
+int tpf_debug_last_sched(tpf_handle h);
 
 /* Static text for a status code. */
 const char* tpf_status_string(int code);

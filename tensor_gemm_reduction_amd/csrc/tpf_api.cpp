@@ -50,6 +50,7 @@ struct tpf_context {
   hipEvent_t kt0[kKernelTimes] = {}, kt1[kKernelTimes] = {};
   int kt_next = 0;      // ring slot of the next record
   int kt_count = 0;     // records held (<= kKernelTimes)
+  int last_sched = -1;  // scheduler the last call ran (AUTO resolved), -1 before any
 };
 
 namespace {
@@ -158,20 +159,30 @@ int check_handle(tpf_handle h) {
 // costs more than the reduction it hides.  What does pay is folding the
 // reduction into the last shard's GEMM epilogue (FOLD): no partial of that
 // shard is written or read back, there is no separate reduction pass, and
-// its epilogue's partial reads overlap other tiles' MFMA work.  AUTO runs
-// FOLD for reductions of row-major (KN) weights on the large tiles (measured
-// 4-6 % faster than GEMM-then-reduce on the Llama down projection and the
-// sequence-parallel ReduceScatter) and UNFUSED elsewhere (the transposed-
-// weight dX measured 2 % slower with FOLD; decode shapes have one shard's
-// tiles too few to fill the GPU).  AllGather->MatMul has no reduction and
-// runs UNFUSED.  The chunked schedulers are chosen explicitly.
+// its epilogue's partial reads overlap other tiles' MFMA work.  But its
+// second launch holds only one shard's tiles, so it pays only when splitting
+// the tiles into p-1 shards' and one shard's launches costs no extra wave of
+// workgroups (one resident large tile per CU): AUTO runs FOLD for reductions
+// of row-major (KN) weights on the large tiles when
+//   waves((p-1) T) + waves(T) == waves(p T),  T = one shard's output tiles,
+// and UNFUSED otherwise.  Measured: FOLD 4-7 % faster than GEMM-then-reduce
+// on the Llama down projection (T = 256: 3 + 1 = 4 waves) and the
+// sequence-parallel ReduceScatter (T = 1024: 28 + 4 = 32); 2 % slower on the
+// MLP block's FC2 and on dX (T = 384: 11 + 2 = 13 > 12) and 1.8x slower on
+// the 2-shard worked example (T = 8: 1 + 1 > 1); the transposed-weight dX
+// runs UNFUSED in any case, and so do decode-shaped M (small tiles).
+// AllGather->MatMul has no reduction and runs UNFUSED.  The chunked
+// schedulers are chosen explicitly.
 int resolve_sched(int sched, int n_chunks) {
   (void)n_chunks;
   return sched & 0xff;   // AUTO stays AUTO here; each op resolves it below
 }
 
-int auto_reduce_sched(int bl, int cfg) {
-  return bl == B_KN && cfg == CFG_LARGE ? TPF_SCHED_FOLD : TPF_SCHED_UNFUSED;
+int auto_reduce_sched(int bl, int cfg, int p, int64_t M, int64_t N, int num_cus) {
+  if (bl != B_KN || cfg != CFG_LARGE || num_cus <= 0) return TPF_SCHED_UNFUSED;
+  const int64_t T = ((M + cfg_bm(cfg) - 1) / cfg_bm(cfg)) * ((N + cfg_bn(cfg) - 1) / cfg_bn(cfg));
+  auto waves = [num_cus](int64_t tiles) { return (tiles + num_cus - 1) / num_cus; };
+  return waves((p - 1) * T) + waves(T) == waves(p * T) ? TPF_SCHED_FOLD : TPF_SCHED_UNFUSED;
 }
 
 // A reducing op (row-parallel AR/RS, or dX with either semantic).
@@ -266,8 +277,9 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
 
   // One shard's tiles of a small-M problem cannot fill the GPU: the fold
   // scheduler then runs as UNFUSED (the same bits either way).
-  int sched = rc.sched == TPF_SCHED_AUTO ? auto_reduce_sched(rc.bl, cfg) : rc.sched;
+  int sched = rc.sched == TPF_SCHED_AUTO ? auto_reduce_sched(rc.bl, cfg, rc.p, rc.M, rc.N, h->num_cus) : rc.sched;
   if (sched == TPF_SCHED_FOLD && cfg != CFG_LARGE) sched = TPF_SCHED_UNFUSED;
+  h->last_sched = sched;
   switch (sched) {
     case TPF_SCHED_GEMM_ONLY:
       TPF_TIMED(h, stream, launch_gemm_rows(cfg, rc.bl, g, 0, rc.M, stream));
@@ -614,6 +626,7 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
   int s = resolve_sched(sched, n_chunks);
   if (s == TPF_SCHED_TILE) s = TPF_SCHED_PERSISTENT;   // no reduction to fold into the tiles
   if (s == TPF_SCHED_FOLD || s == TPF_SCHED_AUTO) s = TPF_SCHED_UNFUSED;
+  h->last_sched = s;
   switch (s) {
     case TPF_SCHED_GEMM_ONLY:
       TPF_TIMED(h, stream_, launch_gemm_rows(cfg, B_KN, g, 0, Mi, stream_));
@@ -862,6 +875,12 @@ int tpf_debug_kernel_times(tpf_handle h, float* ms, int max) {
   h->kt_next = 0;
   h->kt_count = 0;
   return n;
+}
+
+int tpf_debug_last_sched(tpf_handle h) {
+  int st = check_handle(h);
+  if (st) return st;
+  return h->last_sched;
 }
 
 int tpf_debug_set_wait(tpf_handle h, int64_t spins, int unreachable) {

@@ -53,6 +53,7 @@ SIGNATURES = {
     "tpf_debug_set_timeline": (_I, [_VP, _VP, _I]),
     "tpf_debug_set_kernel_timing": (_I, [_VP, _I]),
     "tpf_debug_kernel_times": (_I, [_VP, ctypes.POINTER(ctypes.c_float), _I]),
+    "tpf_debug_last_sched": (_I, [_VP]),
     "tpf_status_string": (ctypes.c_char_p, [_I]),
     "tpf_last_error": (ctypes.c_char_p, []),
     "tpf_version": (_I, []),
@@ -159,6 +160,15 @@ class Handle:
     def set_kernel_timing(self, enable: bool) -> None:
         """Record timing events around each later call's dominant kernel launch."""
         check(load().tpf_debug_set_kernel_timing(self._h, 1 if enable else 0))
+
+    def last_sched(self) -> str:
+        """Name of the scheduler the last reducing or AllGather call on this
+        handle ran (AUTO resolved), or "" before the first."""
+        v = load().tpf_debug_last_sched(self._h)
+        if v < -1:
+            check(v)
+        names = {code: name for name, code in SCHEDS.items()}
+        return names.get(v, "")
 
     def kernel_times(self, max_records: int = 256) -> List[float]:
         """Durations (ms) of the recorded launches, oldest first; clears the record."""

@@ -197,5 +197,6 @@ def test_handle_calls_reject_null():
     assert lib.tpf_debug_set_wait(None, 10, 1) == tp.ERR_INVALID_ARG
     assert lib.tpf_debug_set_kernel_timing(None, 1) == tp.ERR_INVALID_ARG
     assert lib.tpf_debug_kernel_times(None, None, 0) == tp.ERR_INVALID_ARG
+    assert lib.tpf_debug_last_sched(None) == tp.ERR_INVALID_ARG
     assert lib.tpf_create(None, 0) == tp.ERR_INVALID_ARG
     assert lib.tpf_destroy(None) == tp.OK

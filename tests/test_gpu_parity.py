@@ -117,6 +117,38 @@ def test_edge_shapes(p, M, N, K):
     assert_f32(dx, dref, f"edge dX p={p} M={M}")
 
 
+def test_auto_scheduler_choice():
+    """AUTO folds the reduction into the last shard's GEMM only when the
+    last shard's tiles fill whole waves of the GPU (see tpfuse.h), and runs
+    GEMM-then-reduce otherwise; both give the bits of every other scheduler."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    h = tp.Handle(0)
+
+    def ran(p, M, N, K, op="ar"):
+        X = [torch.ones((M, K), dtype=torch.bfloat16, device=DEV) for _ in range(p)]
+        W = [torch.ones((K, N), dtype=torch.bfloat16, device=DEV) for _ in range(p)]
+        if op == "ar":
+            y = tp.matmul_allreduce(X, W, torch.float32, handle=h)
+        else:
+            dY = [torch.ones((M, N), dtype=torch.bfloat16, device=DEV) for _ in range(p)]
+            y = tp.matmul_dx(dY, W, tp.ALLREDUCE, torch.float32, handle=h)
+        torch.cuda.synchronize()
+        assert torch.all(y == p * (K if op == "ar" else N)), "ones in, p * depth out"
+        return h.last_sched()
+
+    tiles = lambda M, N: ((M + 255) // 256) * ((N + 255) // 256)
+    waves = lambda t: (t + cus - 1) // cus
+    say(f"auto scheduler choice, {cus} CUs")
+    # 16 x 16 = 256 tiles per shard: whole waves on a 256-CU device
+    for p, M, N in ((4, 4096, 4096), (2, 128, 2048), (3, 2048, 3072)):
+        t = tiles(M, N)
+        expect = "fold" if waves((p - 1) * t) + waves(t) == waves(p * t) else "unfused"
+        assert ran(p, M, N, 64) == expect, (p, M, N)
+    assert ran(2, 128, 2048, 64) == "unfused"          # 8 tiles per shard: one wave either way
+    assert ran(4, 64, 4096, 64) == "unfused"           # decode-shaped rows: small tiles
+    assert ran(2, 512, 512, 64, op="dx") == "unfused"  # weights used transposed
+
+
 def test_allreduce_integer_exact():
     p, M, N, K = 4, 272, 264, 520
     say(f"allreduce integer-exact p={p} M={M} N={N} K={K}")
