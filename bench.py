@@ -347,6 +347,8 @@ def kernel_bytes(wl, part_bytes=4, sched="unfused"):
     p, M, N, K = wl.p, wl.M, wl.N, wl.K
     if sched == "fold" and wl.op in ("allreduce", "reducescatter", "mlp_sp"):
         return p * (2.0 * M * K + 2.0 * K * N) + 2.0 * (p - 1) * part_bytes * M * N + 2.0 * M * N
+    if sched == "fold" and wl.op == "dx":    # dY_k [M, N], W_k [K, N], dX [M, K]
+        return p * (2.0 * M * N + 2.0 * K * N) + 2.0 * (p - 1) * part_bytes * M * K + 2.0 * M * K
     if wl.op == "allgather":
         return 2.0 * M * K + 2.0 * K * N + 2.0 * M * N
     if wl.op.startswith("wgrad"):   # A_k [M, K], B_k [M, N], dW_k [K, N] fp32

@@ -79,14 +79,13 @@ extern "C" {
                                     and L2 with the GEMM, and overlapping it chunk by chunk costs more
                                     than it hides; folding it into the last shard's GEMM epilogue does
                                     pay when the last shard's tiles fill whole waves of the GPU.  AUTO
-                                    runs TPF_SCHED_FOLD for the reductions of row-major weights
-                                    (MatMul->AllReduce, MatMul->ReduceScatter, the MLP block's FC2) on
-                                    the large tiles (M > 64) when the p-1 shards' tiles and the last
-                                    shard's tiles take no more waves of one-tile-per-CU workgroups
-                                    than all p shards' tiles together, and TPF_SCHED_UNFUSED otherwise
-                                    (and for dX, decode-shaped M, AllGather->MatMul);
-                                    tpf_debug_last_sched reports the choice.  Every scheduler gives
-                                    the same bits. */
+                                    runs TPF_SCHED_FOLD for the reducing calls (MatMul->AllReduce,
+                                    MatMul->ReduceScatter, dX, the MLP block's FC2) on the large tiles
+                                    (M > 64) when the p-1 shards' tiles and the last shard's tiles take
+                                    no more waves of one-tile-per-CU workgroups than all p shards'
+                                    tiles together, and TPF_SCHED_UNFUSED otherwise (and for
+                                    decode-shaped M and AllGather->MatMul); tpf_debug_last_sched
+                                    reports the choice.  Every scheduler gives the same bits. */
 #define TPF_SCHED_PERSISTENT 1   /* one persistent kernel: work queue + per-chunk ready counters */
 #define TPF_SCHED_TWO_STREAM 2   /* per-chunk GEMM launches (alternating between the caller's stream and a
                                     second handle stream), reductions on a side stream after per-chunk

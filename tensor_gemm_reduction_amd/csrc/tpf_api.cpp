@@ -163,23 +163,23 @@ int check_handle(tpf_handle h) {
 // second launch holds only one shard's tiles, so it pays only when splitting
 // the tiles into p-1 shards' and one shard's launches costs no extra wave of
 // workgroups (one resident large tile per CU): AUTO runs FOLD for reductions
-// of row-major (KN) weights on the large tiles when
+// on the large tiles when
 //   waves((p-1) T) + waves(T) == waves(p T),  T = one shard's output tiles,
-// and UNFUSED otherwise.  Measured: FOLD 4-7 % faster than GEMM-then-reduce
-// on the Llama down projection (T = 256: 3 + 1 = 4 waves) and the
-// sequence-parallel ReduceScatter (T = 1024: 28 + 4 = 32); 2 % slower on the
-// MLP block's FC2 and on dX (T = 384: 11 + 2 = 13 > 12) and 1.8x slower on
-// the 2-shard worked example (T = 8: 1 + 1 > 1); the transposed-weight dX
-// runs UNFUSED in any case, and so do decode-shaped M (small tiles).
-// AllGather->MatMul has no reduction and runs UNFUSED.  The chunked
-// schedulers are chosen explicitly.
+// and UNFUSED otherwise.  Measured: FOLD 3-7 % faster than GEMM-then-reduce
+// on the Llama down projection (T = 256: 3 + 1 = 4 waves), the
+// sequence-parallel ReduceScatter (T = 1024: 28 + 4 = 32) and dX of the same
+// kind of shapes (T = 256 and 512); 2-3 % slower on the MLP block's FC2 and
+// on the GPT-3-shaped dX (T = 384: 11 + 2 = 13 > 12) and 1.8x slower on the
+// 2-shard worked example (T = 8: 1 + 1 > 1).  Decode-shaped M (small tiles)
+// runs UNFUSED.  AllGather->MatMul has no reduction and runs UNFUSED.  The
+// chunked schedulers are chosen explicitly.
 int resolve_sched(int sched, int n_chunks) {
   (void)n_chunks;
   return sched & 0xff;   // AUTO stays AUTO here; each op resolves it below
 }
 
-int auto_reduce_sched(int bl, int cfg, int p, int64_t M, int64_t N, int num_cus) {
-  if (bl != B_KN || cfg != CFG_LARGE || num_cus <= 0) return TPF_SCHED_UNFUSED;
+int auto_reduce_sched(int cfg, int p, int64_t M, int64_t N, int num_cus) {
+  if (cfg != CFG_LARGE || num_cus <= 0) return TPF_SCHED_UNFUSED;
   const int64_t T = ((M + cfg_bm(cfg) - 1) / cfg_bm(cfg)) * ((N + cfg_bn(cfg) - 1) / cfg_bn(cfg));
   auto waves = [num_cus](int64_t tiles) { return (tiles + num_cus - 1) / num_cus; };
   return waves((p - 1) * T) + waves(T) == waves(p * T) ? TPF_SCHED_FOLD : TPF_SCHED_UNFUSED;
@@ -277,7 +277,7 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
 
   // One shard's tiles of a small-M problem cannot fill the GPU: the fold
   // scheduler then runs as UNFUSED (the same bits either way).
-  int sched = rc.sched == TPF_SCHED_AUTO ? auto_reduce_sched(rc.bl, cfg, rc.p, rc.M, rc.N, h->num_cus) : rc.sched;
+  int sched = rc.sched == TPF_SCHED_AUTO ? auto_reduce_sched(cfg, rc.p, rc.M, rc.N, h->num_cus) : rc.sched;
   if (sched == TPF_SCHED_FOLD && cfg != CFG_LARGE) sched = TPF_SCHED_UNFUSED;
   h->last_sched = sched;
   switch (sched) {

@@ -146,7 +146,10 @@ def test_auto_scheduler_choice():
         assert ran(p, M, N, 64) == expect, (p, M, N)
     assert ran(2, 128, 2048, 64) == "unfused"          # 8 tiles per shard: one wave either way
     assert ran(4, 64, 4096, 64) == "unfused"           # decode-shaped rows: small tiles
-    assert ran(2, 512, 512, 64, op="dx") == "unfused"  # weights used transposed
+    assert ran(2, 512, 512, 64, op="dx") == "unfused"  # dX [512, 64]: 2 tiles per shard
+    t = tiles(4096, 4096)                               # dX [4096, 4096] with p = 4
+    expect = "fold" if waves(3 * t) + waves(t) == waves(4 * t) else "unfused"
+    assert ran(4, 4096, 64, 4096, op="dx") == expect
 
 
 def test_allreduce_integer_exact():
