@@ -93,8 +93,10 @@ __device__ __forceinline__ TileJob make_job(const GemmOperands& g, int shard, in
 
 // Tile u of a row range (shard-major) -> (shard, tm, tn).  Within a shard the
 // tiles go in groups of kGroupM tile-rows, column by column, so that tiles
-// running at the same time share A and B panels.
-constexpr int kGroupM = 4;
+// running at the same time share A and B panels (the 32 tiles an XCD runs
+// at once cover 8 row panels x 4 column panels; measured about 1 % faster
+// than groups of 4 rows, groups of 2 or 16 slower).
+constexpr int kGroupM = 8;
 
 __device__ __forceinline__ void tile_coords(int u, int tiles_m, int tiles_n, int& shard, int& tm, int& tn) {
   const int per_shard = tiles_m * tiles_n;
