@@ -177,10 +177,12 @@ using CfgLargeFused = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARG
 #define TPF_SMALL_BN 128
 #endif
 #ifndef TPF_SMALL_STAGES
-#define TPF_SMALL_STAGES 4
+#define TPF_SMALL_STAGES 2
 #endif
 // Decode-shaped row counts (measured on 134 MB of weights, p = 8):
-//   M <= 32:  32 x 128 tiles, 4 stages of 20 KiB, two workgroups per CU;
+//   M <= 32:  32 x 128 tiles, 2 stages of 20 KiB (measured 4-6 % faster
+//             than 3 or 4 stages; 5 or 6 leave room for one workgroup per CU
+//             and were 25 % slower);
 //   M <= 64:  64 x 256 tiles, 3 stages of 40 KiB: each weight tile is read by
 //             one workgroup instead of two (47 % -> 61 % of HBM bandwidth at M = 64).
 using CfgSmall = TileCfg<TPF_SMALL_BM, TPF_SMALL_BN, 1, 4, TPF_SMALL_STAGES, 64, 0>;
