@@ -1,0 +1,89 @@
+"""Randomized parity (fixed seeds, valid shapes only): ragged M, N and K,
+shard counts from 1 to 16, every reducing op and AllGather->MatMul, every
+scheduler and both output dtypes, each checked against the oracle and
+bit for bit against GEMM-then-reduce.  Complements the hand-picked shapes
+of test_gpu_parity.py."""
+import random
+
+import pytest
+import torch
+
+from oracle import tpf_oracle as O
+from tensor_gemm_reduction_amd import inputs, tpfuse as tp
+from tests.parity import assert_bf16, assert_bitwise, assert_f32
+
+pytestmark = pytest.mark.gpu
+
+SCHEDS = ["auto", "unfused", "fold", "persistent", "two_stream", "tile"]
+DEV = "cuda"
+
+
+def cases(seed, count):
+    rng = random.Random(seed)
+    for i in range(count):
+        op = rng.choice(["ar", "rs", "dx", "ag"])
+        p = rng.choice([1, 2, 3, 4, 5, 8, 11, 16])
+        M = rng.choice([1, 7, 31, 33, 64, 65, 200, 257, 300, 520])
+        if op in ("rs", "ag"):
+            M = max(p, (M // p) * p)
+        N = 8 * rng.randint(1, 70)
+        K = 8 * rng.randint(1, 50)
+        n = rng.randint(1, min(M, 9))
+        yield pytest.param(op, p, M, N, K, n, rng.randint(0, 1 << 30), id=f"{seed}-{i}-{op}-p{p}-M{M}-N{N}-K{K}-n{n}")
+
+
+@pytest.mark.parametrize("op,p,M,N,K,n,seed", list(cases(1, 40)))
+def test_random_shape(op, p, M, N, K, n, seed):
+    print(f"random shape {op} p={p} M={M} N={N} K={K} n={n} seed={seed}", flush=True)
+    g = torch.Generator().manual_seed(seed)
+
+    def draw(shape, s):
+        return (torch.randn(shape, generator=g) * s).to(torch.bfloat16)
+
+    def bits(ts):
+        return [inputs.bf16_to_bits(t) for t in ts]
+
+    outs = {}
+    if op in ("ar", "rs"):
+        Xh = [draw((M, K), 1.0) for _ in range(p)]
+        Wh = [draw((K, N), 0.05) for _ in range(p)]
+        ref = O.matmul_allreduce(bits(Xh), bits(Wh))
+        X, W = [t.to(DEV) for t in Xh], [t.to(DEV) for t in Wh]
+        for sched in SCHEDS:
+            if op == "ar":
+                y32 = tp.matmul_allreduce(X, W, torch.float32, n_chunks=n, sched=sched)
+                y16 = tp.matmul_allreduce(X, W, torch.bfloat16, n_chunks=n, sched=sched)
+            else:
+                y32 = torch.cat(tp.matmul_reducescatter(X, W, torch.float32, n_chunks=n, sched=sched), 0)
+                y16 = torch.cat(tp.matmul_reducescatter(X, W, torch.bfloat16, n_chunks=n, sched=sched), 0)
+            torch.cuda.synchronize()
+            assert_f32(y32, ref, f"{op} {sched}")
+            assert_bf16(y16, ref, f"{op} {sched}")
+            outs[sched] = (y32, y16)
+    elif op == "dx":
+        dYh = [draw((M, N), 1.0) for _ in range(p)]
+        Wh = [draw((K, N), 0.05) for _ in range(p)]
+        ref = O.matmul_dx(bits(dYh), bits(Wh))
+        dY, W = [t.to(DEV) for t in dYh], [t.to(DEV) for t in Wh]
+        for sched in SCHEDS:
+            y32 = tp.matmul_dx(dY, W, tp.ALLREDUCE, torch.float32, n_chunks=n, sched=sched)
+            y16 = tp.matmul_dx(dY, W, tp.ALLREDUCE, torch.bfloat16, n_chunks=n, sched=sched)
+            torch.cuda.synchronize()
+            assert_f32(y32, ref, f"dx {sched}")
+            assert_bf16(y16, ref, f"dx {sched}")
+            outs[sched] = (y32, y16)
+    else:
+        Xh = [draw((M // p, K), 1.0) for _ in range(p)]
+        Wh = draw((K, N), 0.05)
+        _, ref = O.allgather_matmul(bits(Xh), inputs.bf16_to_bits(Wh))
+        X, W = [t.to(DEV) for t in Xh], Wh.to(DEV)
+        for sched in SCHEDS:
+            XG, y32 = tp.allgather_matmul(X, W, torch.float32, n_chunks=n, sched=sched)
+            torch.cuda.synchronize()
+            assert torch.equal(XG.cpu(), torch.cat(Xh, 0)), f"gather {sched}"
+            assert_f32(y32, ref, f"ag {sched}")
+            outs[sched] = (y32, y32)
+    base32, base16 = outs["unfused"]
+    for sched, (a, b) in outs.items():
+        assert_bitwise(a, base32, f"{op} {sched} fp32 vs unfused")
+        assert_bitwise(b, base16, f"{op} {sched} bf16 vs unfused")
