@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--modes", default="gemm_only,reduce_only,unfused,two_stream,persistent,tile,fold,auto")
+    ap.add_argument("--yardstick", action="store_true",
+                    help="only time the vendor GEMM (torch.matmul -> hipBLASLt) on the workload's shard GEMMs, "
+                         "with the weights as given ([K][N]) and K-contiguous, for comparison")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -85,6 +88,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "note": "plain device copy for counter calibration"}), flush=True)
+        return
+
+    if args.yardstick:
+        yardstick(args, inputs.WORKLOADS[args.workload])
         return
 
     tp.load()
@@ -334,6 +341,41 @@ def main():
         "modes": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in modes.items()},
         **{k: round(v, 4) for k, v in extra.items()},
     }
+    print(json.dumps(out), flush=True)
+
+
+def yardstick(args, wl):
+    """The vendor library on the same shard GEMMs (run, not read): p products
+    X_k [M, K] @ W_k per step, bf16 in and out, with W_k as the library's
+    callers store it ([K][N], the "NN" case) and K-contiguous (a transposed
+    copy, the "NT" case).  Context for the roofline, not part of the path."""
+    import torch
+    if wl.op not in ("allreduce", "reducescatter"):
+        raise SystemExit("--yardstick covers the row-parallel workloads (allreduce, reducescatter)")
+    torch.manual_seed(0)
+    p, M, N, K = wl.p, wl.M, wl.N, wl.K
+    X = [torch.randn(M, K, device="cuda").to(torch.bfloat16) for _ in range(p)]
+    W = [(torch.randn(K, N, device="cuda") * 0.02).to(torch.bfloat16) for _ in range(p)]
+    Wt = [w.t().contiguous().t() for w in W]     # same values, K-contiguous storage
+    out = {"yardstick": "torch.matmul (hipBLASLt)", "workload": wl.name, "p": p, "M": M, "N": N, "K": K}
+    flops = 2.0 * p * M * N * K
+    for name, ws in (("nn", W), ("nt", Wt)):
+        def step():
+            for k in range(p):
+                X[k] @ ws[k]
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.settle_ms / 1e3:
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        out[f"{name}_ms_per_step"] = round(ms, 4)
+        out[f"{name}_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
     print(json.dumps(out), flush=True)
 
 

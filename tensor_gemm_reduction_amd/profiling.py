@@ -83,16 +83,21 @@ def counter_per_dispatch(path: str, counter: str, kernel_sub: str) -> float:
     return sum(sum(v) / len(v) for v in by_name.values())
 
 
-def stats(csv_path: str, out_path: str, command: str, bench_json: str = "") -> None:
+def stats(csv_path: str, out_path: str, command: str, bench_json: str = "", name_filter=("tpf::", "copyBuffer"),
+          width: int = 90) -> None:
     lines = [f"# rocprofv3 kernel statistics (durations in microseconds)", f"# command: {command}", ""]
-    lines.append(f"{'kernel':90s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+    lines.append(f"{'kernel':{width}s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
     for r in _rows(csv_path, "kernel_stats.csv"):
         name = r["Name"]
-        if "tpf::" not in name and "copyBuffer" not in name:
+        if not any(f in name for f in name_filter):
             continue
-        lines.append(f"{name[:90]:90s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:10.2f} "
+        lines.append(f"{name[:width]:{width}s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:10.2f} "
                      f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
-    if bench_json and os.path.exists(bench_json):
+    if bench_json and os.path.exists(bench_json) and "yardstick" in open(bench_json).read():
+        with open(bench_json) as f:
+            rec = json.loads(f.read().strip().splitlines()[-1])
+        lines += ["", f"# bench.py --yardstick (same run): " + json.dumps(rec)]
+    elif bench_json and os.path.exists(bench_json):
         # The same command's own JSON line: its HIP-event average of the
         # dominant kernel must agree with the rocprofv3 average above.
         with open(bench_json) as f:
@@ -207,6 +212,9 @@ if __name__ == "__main__":
         stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[5:]), "" if sys.argv[4] == "-" else sys.argv[4])
     elif cmd == "traffic":
         traffic(*sys.argv[2:11], command=" ".join(sys.argv[11:]))
+    elif cmd == "yardstick":
+        # yardstick <csv dir> <out.txt> <bench_json> <command...>: the vendor GEMM kernels, full names
+        stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[5:]), sys.argv[4], name_filter=("Cijk",), width=400)
     elif cmd == "mfma":
         # mfma <counter dir> <kernel-substring> <out.txt> <command...>
         mfma(sys.argv[2], sys.argv[3], sys.argv[4], command=" ".join(sys.argv[5:]))
