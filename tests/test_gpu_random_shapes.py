@@ -2,7 +2,10 @@
 shard counts from 1 to 16, every reducing op and AllGather->MatMul, every
 scheduler and both output dtypes, each checked against the oracle and
 bit for bit against GEMM-then-reduce.  Complements the hand-picked shapes
-of test_gpu_parity.py."""
+of test_gpu_parity.py.  A second, smaller set draws grids of many 256x256
+output tiles (several tile-row groups, more tiles than compute units) so
+the tile order, the ragged last tile row/column and the fold epilogue are
+exercised away from the single-tile corner."""
 import random
 
 import pytest
@@ -32,7 +35,21 @@ def cases(seed, count):
         yield pytest.param(op, p, M, N, K, n, rng.randint(0, 1 << 30), id=f"{seed}-{i}-{op}-p{p}-M{M}-N{N}-K{K}-n{n}")
 
 
-@pytest.mark.parametrize("op,p,M,N,K,n,seed", list(cases(1, 40)))
+def big_cases(seed, count):
+    rng = random.Random(seed)
+    for i in range(count):
+        op = rng.choice(["ar", "rs", "dx", "ag"])
+        p = rng.choice([2, 3, 4, 8])
+        M = rng.choice([700, 1031, 2304, 3000])
+        if op in ("rs", "ag"):
+            M = (M // p) * p
+        N = 8 * rng.randint(64, 320)
+        K = 8 * rng.randint(4, 40)
+        n = rng.randint(1, 9)
+        yield pytest.param(op, p, M, N, K, n, rng.randint(0, 1 << 30), id=f"big{seed}-{i}-{op}-p{p}-M{M}-N{N}-K{K}-n{n}")
+
+
+@pytest.mark.parametrize("op,p,M,N,K,n,seed", list(cases(1, 40)) + list(big_cases(2, 8)))
 def test_random_shape(op, p, M, N, K, n, seed):
     print(f"random shape {op} p={p} M={M} N={N} K={K} n={n} seed={seed}", flush=True)
     g = torch.Generator().manual_seed(seed)
