@@ -13,8 +13,10 @@ their steady state, and the K timed steps are meant to see it.
 
 Prints ONE JSON line.  `value` is whole-step TFLOP/s of the library call
 (algorithmic 2*M*N*K_total over the wall time per step; the default
-scheduler is AUTO, which on one GPU runs the shard-GEMM kernel followed by
-the reduction kernel); `roofline` prices the step's dominant kernel against
+scheduler is AUTO, which at this workload runs the fold scheduler: the GEMMs
+of shards 0..p-2 into fp32 partials, then the last shard's GEMM whose epilogue
+sums them; `config.sched_ran` names what ran); `roofline` prices the step's
+dominant kernel (for the fold scheduler, its pair of launches) against
 the bf16 dense MFMA peak, its average duration measured by HIP events that
 the library records around that launch on the stream it is launched on;
 `modes` gives the GEMM-only, reduce-only, unfused, two-stream, persistent
