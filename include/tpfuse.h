@@ -30,6 +30,11 @@
  *  - All matrices are row-major and contiguous; inputs are bfloat16.
  *  - Every device pointer must be 16-byte aligned; the reduction length and
  *    the output width must be multiples of 8 elements.
+ *  - Pointers are checked for alignment only, not for where they live or
+ *    how large their buffers are: host memory, another device's memory or a
+ *    buffer shorter than the shape arguments imply is undefined behaviour
+ *    (a GPU memory fault).  The Python binding checks the device, shape,
+ *    dtype and layout of every tensor before it calls in.
  *  - Pointer arrays (X[], W[], slices[]) are host arrays read during the call
  *    only; the device buffers they name are owned by the caller.  The library
  *    never allocates or frees caller memory.  Outputs must not alias inputs

@@ -202,6 +202,60 @@ def default_handle(device: Optional[int] = None) -> Handle:
     return h
 
 
+OUT_DTYPES = (torch.bfloat16, torch.float32)
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check(name: str, ts, shape, dtypes=(torch.bfloat16,), device=None) -> torch.device:
+    """Refuse, before any library call, tensors the library cannot be handed.
+
+    The library reads and writes through raw device pointers whose extents it
+    derives from the shape arguments alone, so a tensor on the host, on
+    another device, of another shape or strided would be accessed out of
+    bounds on the GPU.  Every tensor in `ts` must be a contiguous GPU tensor
+    on `device` (default: the first one's), of shape `shape` and one of
+    `dtypes`.  Returns the device."""
+    _need(len(ts) >= 1, f"{name}: no tensors given")
+    dev = device if device is not None else getattr(ts[0], "device", None)
+    shape = tuple(shape)
+    ok = getattr(dev, "type", None) == "cuda"
+    for t in ts:        # one combined test per tensor; the message is built only on failure
+        if not (ok and isinstance(t, torch.Tensor) and t.device == dev and t.dtype in dtypes
+                and t.shape == shape and t.is_contiguous()):
+            ok = False
+            break
+    if not ok:
+        for i, t in enumerate(ts):
+            lab = f"{name}[{i}]" if len(ts) > 1 else name
+            _need(isinstance(t, torch.Tensor), f"{lab} is not a tensor")
+            _need(t.device.type == "cuda", f"{lab} is on {t.device}, not on a GPU")
+            _need(t.device == dev, f"{lab} is on {t.device}, expected {dev}")
+            _need(t.dtype in dtypes, f"{lab} has dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+            _need(tuple(t.shape) == shape, f"{lab} has shape {tuple(t.shape)}, expected {shape}")
+            _need(t.is_contiguous(), f"{lab} is not contiguous")
+        _need(False, f"{name}: the device {dev} is not a GPU")
+    return dev
+
+
+def _check_shards(name: str, ts, p: int) -> None:
+    _need(len(ts) == p, f"{name}: {len(ts)} tensors given, expected one per shard ({p})")
+
+
+def _check_ws(ws, dev) -> None:
+    if ws is not None:
+        _check("ws", [ws], tuple(ws.shape), (ws.dtype,), dev)
+
+
+def _handle(handle, dev) -> "Handle":
+    h = handle or default_handle(dev.index)
+    _need(h.device == dev.index, f"handle is bound to device {h.device}, tensors are on {dev}")
+    return h
+
+
 def workspace_size(op: int, p: int, M: int, N: int, K: int, n_chunks: int = 1, sched=SCHED_AUTO,
                    message: str = "fp32") -> int:
     return int(load().tpf_workspace_size(op, p, M, N, K, n_chunks, _sched(sched, message)))
@@ -221,13 +275,18 @@ def matmul_allreduce(X: List[torch.Tensor], W: List[torch.Tensor], out_dtype=tor
                      handle: Optional[Handle] = None, stream=None, message: str = "fp32") -> torch.Tensor:
     """Y = sum_k X[k] @ W[k] (row-parallel Linear, AllReduce layout)."""
     p = len(X)
+    _need(p >= 1, "X: no shards given")
     M, K = X[0].shape
     N = W[0].shape[1]
-    dev = X[0].device
+    _check_shards("W", W, p)
+    dev = _check("X", X, (M, K))
+    _check("W", W, (K, N), device=dev)
     if Y is None:
         Y = torch.empty((M, N), dtype=out_dtype, device=dev)
+    _check("Y", [Y], (M, N), OUT_DTYPES, dev)
+    _check_ws(ws, dev)
+    h = _handle(handle, dev)
     ws, ws_bytes = _ws(OP_MATMUL_ALLREDUCE, p, M, N, K, n_chunks, sched, ws, dev, message)
-    h = handle or default_handle(dev.index)
     check(load().tpf_matmul_allreduce(h.ptr, p, M, N, K, ptr_array([x.data_ptr() for x in X]),
                                       ptr_array([w.data_ptr() for w in W]), Y.data_ptr(), _dtype_code(Y.dtype),
                                       n_chunks, _sched(sched, message), ws.data_ptr() if ws is not None else None, ws_bytes,
@@ -240,13 +299,20 @@ def matmul_reducescatter(X: List[torch.Tensor], W: List[torch.Tensor], out_dtype
                          handle: Optional[Handle] = None, stream=None, message: str = "fp32") -> List[torch.Tensor]:
     """Slice r = rows [r*M/p, (r+1)*M/p) of sum_k X[k] @ W[k] (ReduceScatter layout)."""
     p = len(X)
+    _need(p >= 1, "X: no shards given")
     M, K = X[0].shape
     N = W[0].shape[1]
-    dev = X[0].device
+    _check_shards("W", W, p)
+    dev = _check("X", X, (M, K))
+    _check("W", W, (K, N), device=dev)
     if Y is None:
         Y = [torch.empty((M // p, N), dtype=out_dtype, device=dev) for _ in range(p)]
+    _check_shards("Y", Y, p)
+    _check("Y", Y, (M // p, N), OUT_DTYPES, dev)
+    _need(len({y.dtype for y in Y}) == 1, "Y: the slices differ in dtype")
+    _check_ws(ws, dev)
+    h = _handle(handle, dev)
     ws, ws_bytes = _ws(OP_MATMUL_REDUCESCATTER, p, M, N, K, n_chunks, sched, ws, dev, message)
-    h = handle or default_handle(dev.index)
     check(load().tpf_matmul_reducescatter(h.ptr, p, M, N, K, ptr_array([x.data_ptr() for x in X]),
                                           ptr_array([w.data_ptr() for w in W]), ptr_array([y.data_ptr() for y in Y]),
                                           _dtype_code(Y[0].dtype), n_chunks, _sched(sched, message),
@@ -259,15 +325,19 @@ def allgather_matmul(X_slices: List[torch.Tensor], W: torch.Tensor, out_dtype=to
                      handle: Optional[Handle] = None, stream=None):
     """(X_gathered, Y): slices concatenated in rank order, then Y = X_gathered @ W."""
     p = len(X_slices)
+    _need(p >= 1, "X_slices: no slices given")
     Ms, K = X_slices[0].shape
     M = Ms * p
     N = W.shape[1]
-    dev = W.device
+    dev = _check("W", [W], (K, N))
+    _check("X_slices", X_slices, (Ms, K), device=dev)
     if X_gathered is None:
         X_gathered = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     if Y is None:
         Y = torch.empty((M, N), dtype=out_dtype, device=dev)
-    h = handle or default_handle(dev.index)
+    _check("X_gathered", [X_gathered], (M, K), device=dev)
+    _check("Y", [Y], (M, N), OUT_DTYPES, dev)
+    h = _handle(handle, dev)
     check(load().tpf_allgather_matmul(h.ptr, p, M, N, K, ptr_array([x.data_ptr() for x in X_slices]), W.data_ptr(),
                                       X_gathered.data_ptr(), Y.data_ptr(), _dtype_code(Y.dtype), n_chunks,
                                       _sched(sched), None, 0, _stream_ptr(stream)))
@@ -279,17 +349,27 @@ def matmul_dx(dY: List[torch.Tensor], W: List[torch.Tensor], semantic: int = ALL
               handle: Optional[Handle] = None, stream=None, message: str = "fp32"):
     """dX = sum_k dY[k] @ W[k]^T; one tensor (ALLREDUCE) or p row slices (REDUCESCATTER)."""
     p = len(dY)
+    _need(p >= 1, "dY: no shards given")
     M, Ns = dY[0].shape
     Kin = W[0].shape[0]
-    dev = dY[0].device
+    _check_shards("W", W, p)
+    dev = _check("dY", dY, (M, Ns))
+    _check("W", W, (Kin, Ns), device=dev)
     if dX is None:
         if semantic == ALLREDUCE:
             dX = torch.empty((M, Kin), dtype=out_dtype, device=dev)
         else:
             dX = [torch.empty((M // p, Kin), dtype=out_dtype, device=dev) for _ in range(p)]
     outs = [dX] if semantic == ALLREDUCE else list(dX)
+    if semantic == ALLREDUCE:
+        _check("dX", outs, (M, Kin), OUT_DTYPES, dev)
+    else:
+        _check_shards("dX", outs, p)
+        _check("dX", outs, (M // p, Kin), OUT_DTYPES, dev)
+        _need(len({o.dtype for o in outs}) == 1, "dX: the slices differ in dtype")
+    _check_ws(ws, dev)
+    h = _handle(handle, dev)
     ws, ws_bytes = _ws(OP_MATMUL_DX, p, M, Kin, Ns, n_chunks, sched, ws, dev, message)
-    h = handle or default_handle(dev.index)
     check(load().tpf_matmul_dx(h.ptr, semantic, p, M, Kin, Ns, ptr_array([d.data_ptr() for d in dY]),
                                ptr_array([w.data_ptr() for w in W]), ptr_array([o.data_ptr() for o in outs]),
                                _dtype_code(outs[0].dtype), n_chunks, _sched(sched, message),
@@ -304,12 +384,18 @@ def weight_grad(A: List[torch.Tensor], B: List[torch.Tensor], out_dtype=torch.fl
     Row-parallel: A = X_k per shard, B = [dY] * p.  Column-parallel:
     A = [X_gathered] * p, B = dY_k per shard."""
     p = len(A)
+    _need(p >= 1, "A: no shards given")
     M, R = A[0].shape
     C = B[0].shape[1]
-    dev = A[0].device
+    _check_shards("B", B, p)
+    dev = _check("A", A, (M, R))
+    _check("B", B, (M, C), device=dev)
     if dW is None:
         dW = [torch.empty((R, C), dtype=out_dtype, device=dev) for _ in range(p)]
-    h = handle or default_handle(dev.index)
+    _check_shards("dW", dW, p)
+    _check("dW", dW, (R, C), OUT_DTYPES, dev)
+    _need(len({d.dtype for d in dW}) == 1, "dW: the shards differ in dtype")
+    h = _handle(handle, dev)
     check(load().tpf_weight_grad(h.ptr, p, M, R, C, ptr_array([a.data_ptr() for a in A]),
                                  ptr_array([b.data_ptr() for b in B]), ptr_array([d.data_ptr() for d in dW]),
                                  _dtype_code(dW[0].dtype), _stream_ptr(stream)))
@@ -324,18 +410,30 @@ def mlp_sp(X_slices: List[torch.Tensor], W1: List[torch.Tensor], W2: List[torch.
     """MLP block under sequence parallelism: AllGather -> FC1 (column shards) + GeLU
     -> FC2 (row shards) -> ReduceScatter.  Returns (X_gathered, H, Y_slices)."""
     p = len(X_slices)
+    _need(p >= 1, "X_slices: no slices given")
     Sp, Hd = X_slices[0].shape
     S = Sp * p
     F = W1[0].shape[1]
-    dev = X_slices[0].device
+    _check_shards("W1", W1, p)
+    _check_shards("W2", W2, p)
+    dev = _check("X_slices", X_slices, (Sp, Hd))
+    _check("W1", W1, (Hd, F), device=dev)
+    _check("W2", W2, (F, Hd), device=dev)
     if X_gathered is None:
         X_gathered = torch.empty((S, Hd), dtype=torch.bfloat16, device=dev)
     if H is None:
         H = [torch.empty((S, F), dtype=torch.bfloat16, device=dev) for _ in range(p)]
     if Y is None:
         Y = [torch.empty((Sp, Hd), dtype=out_dtype, device=dev) for _ in range(p)]
+    _check("X_gathered", [X_gathered], (S, Hd), device=dev)
+    _check_shards("H", H, p)
+    _check("H", H, (S, F), device=dev)
+    _check_shards("Y", Y, p)
+    _check("Y", Y, (Sp, Hd), OUT_DTYPES, dev)
+    _need(len({y.dtype for y in Y}) == 1, "Y: the slices differ in dtype")
+    _check_ws(ws, dev)
+    h = _handle(handle, dev)
     ws, ws_bytes = _ws(OP_MLP_SP, p, S, Hd, F, n_chunks, sched, ws, dev, message)
-    h = handle or default_handle(dev.index)
     check(load().tpf_mlp_sp(h.ptr, p, S, Hd, F, ptr_array([x.data_ptr() for x in X_slices]),
                             ptr_array([w.data_ptr() for w in W1]), ptr_array([w.data_ptr() for w in W2]),
                             X_gathered.data_ptr(), ptr_array([t.data_ptr() for t in H]),

@@ -1,0 +1,76 @@
+"""The Python binding refuses tensors the library cannot be handed (host
+tensors, a wrong shard count, a shard of another shape, dtype or layout)
+with ValueError before any library call: the library derives every extent
+from the shape arguments, so such a tensor would be accessed out of bounds
+on the GPU.  The host-tensor and shard-count cases need no GPU; the rest
+build GPU tensors but launch nothing."""
+import pytest
+import torch
+
+from tensor_gemm_reduction_amd import tpfuse as tp
+
+BF = torch.bfloat16
+
+
+def host(*shape, dtype=BF):
+    return torch.zeros(shape, dtype=dtype)
+
+
+OPS_ON_HOST = {
+    "allreduce": lambda: tp.matmul_allreduce([host(64, 32)] * 2, [host(32, 16)] * 2),
+    "reducescatter": lambda: tp.matmul_reducescatter([host(64, 32)] * 2, [host(32, 16)] * 2),
+    "allgather": lambda: tp.allgather_matmul([host(32, 32)] * 2, host(32, 16)),
+    "dx": lambda: tp.matmul_dx([host(64, 16)] * 2, [host(32, 16)] * 2),
+    "weight_grad": lambda: tp.weight_grad([host(64, 32)] * 2, [host(64, 16)] * 2),
+    "mlp_sp": lambda: tp.mlp_sp([host(32, 16)] * 2, [host(16, 24)] * 2, [host(24, 16)] * 2),
+}
+
+
+@pytest.mark.parametrize("op", sorted(OPS_ON_HOST))
+def test_host_tensors_are_refused(op):
+    with pytest.raises(ValueError, match="not on a GPU"):
+        OPS_ON_HOST[op]()
+
+
+@pytest.mark.parametrize("call", [
+    lambda: tp.matmul_allreduce([host(64, 32)] * 2, [host(32, 16)] * 3),
+    lambda: tp.matmul_reducescatter([host(64, 32)] * 2, [host(32, 16)]),
+    lambda: tp.matmul_dx([host(64, 16)] * 3, [host(32, 16)] * 2),
+    lambda: tp.weight_grad([host(64, 32)] * 2, [host(64, 16)] * 4),
+    lambda: tp.mlp_sp([host(32, 16)] * 2, [host(16, 24)] * 2, [host(24, 16)]),
+])
+def test_shard_count_mismatch_is_refused(call):
+    with pytest.raises(ValueError, match="one per shard"):
+        call()
+
+
+@pytest.mark.gpu
+def test_device_tensor_checks():
+    d = "cuda"
+
+    def dev(*shape, dtype=BF):
+        return torch.zeros(shape, dtype=dtype, device=d)
+
+    X, W = [dev(64, 32)] * 2, [dev(32, 16)] * 2
+    cases = [
+        (lambda: tp.matmul_allreduce([dev(64, 32), dev(48, 32)], W), "X\\[1\\] has shape"),
+        (lambda: tp.matmul_allreduce([dev(64, 32, dtype=torch.float32)] * 2, W), "dtype"),
+        (lambda: tp.matmul_allreduce(X, [dev(16, 32).t()] * 2), "not contiguous"),
+        (lambda: tp.matmul_allreduce(X, W, Y=dev(64, 16, dtype=torch.float16)), "Y has dtype"),
+        (lambda: tp.matmul_allreduce(X, W, Y=dev(64, 8)), "Y has shape"),
+        (lambda: tp.matmul_allreduce(X, W, ws=torch.zeros(1 << 20, dtype=torch.uint8)), "ws is on cpu"),
+        (lambda: tp.matmul_allreduce(X, [host(32, 16)] * 2), "W\\[0\\] is on cpu"),
+        (lambda: tp.matmul_reducescatter(X, W, Y=[dev(32, 16), dev(32, 16, dtype=torch.float32)]),
+         "differ in dtype"),
+        (lambda: tp.allgather_matmul([dev(32, 32)] * 2, W[0], X_gathered=dev(32, 32)), "X_gathered has shape"),
+        (lambda: tp.matmul_dx([dev(64, 16)] * 2, [dev(32, 8)] * 2), "W\\[0\\] has shape"),
+        (lambda: tp.matmul_dx([dev(64, 16)] * 2, [dev(32, 16)] * 2, tp.REDUCESCATTER, dX=[dev(64, 32)] * 2),
+         "dX\\[0\\] has shape"),
+        (lambda: tp.weight_grad([dev(64, 32)] * 2, [dev(60, 16)] * 2), "B\\[0\\] has shape"),
+        (lambda: tp.mlp_sp([dev(32, 16)] * 2, [dev(16, 24)] * 2, [dev(16, 24)] * 2), "W2\\[0\\] has shape"),
+        (lambda: tp.mlp_sp([dev(32, 16)] * 2, [dev(16, 24)] * 2, [dev(24, 16)] * 2,
+                           H=[dev(64, 24, dtype=torch.float32)] * 2), "H\\[0\\] has dtype"),
+    ]
+    for call, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            call()
