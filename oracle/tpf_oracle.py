@@ -92,11 +92,6 @@ def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return np.where(np.isnan(x), np.uint16(0x7FC0), bits).astype(np.uint16)
 
 
-def round_to_f32(x: np.ndarray) -> np.ndarray:
-    """Round float64 values to binary32, round to nearest even (numpy's cast)."""
-    return np.asarray(x, dtype=np.float64).astype(np.float32)
-
-
 # --------------------------------------------------------------------------
 # Chunking and message sizes (M027 page §02-§03)
 # --------------------------------------------------------------------------

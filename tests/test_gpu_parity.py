@@ -532,6 +532,7 @@ def test_dx_parity(p, M, Kin, Ns):
     dYh = shards([(M, Ns)] * p, ("normal", 1.0), 71)
     Wh = shards([(Kin, Ns)] * p, ("normal", 0.05), 72)
     ref = O.matmul_dx(bits(dYh), bits(Wh))
+    ref_rs = O.matmul_dx_reducescatter(bits(dYh), bits(Wh)) if M % p == 0 else None
     dY, W = gpu(dYh), gpu(Wh)
     base = None
     for sched in SCHEDS:
@@ -550,6 +551,7 @@ def test_dx_parity(p, M, Kin, Ns):
                 sl = tp.matmul_dx(dY, W, tp.REDUCESCATTER, torch.bfloat16, n_chunks=n, sched=sched)
                 torch.cuda.synchronize()
                 for r in range(p):
+                    assert_bf16(sl[r], ref_rs[r], what + f" RS slice {r} vs oracle")
                     assert_bitwise(sl[r], d16[r * (M // p):(r + 1) * (M // p)], what + f" RS slice {r}")
 
 

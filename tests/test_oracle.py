@@ -143,6 +143,24 @@ def pin_brute_force_dx(o):
                for i in range(M) for j in range(Kin))
 
 
+def pin_brute_force_dx_reducescatter(o):
+    """dX in the sequence-parallel layout: slice r holds rows [r*M/p, (r+1)*M/p)
+    of sum_k dY_k W_k^T (cnblogs §2.7 ReduceScatter applied to the §6.4
+    backward), checked row by row against the exact rational product."""
+    rng = np.random.default_rng(16)
+    M, Kin, Ns, p = 6, 4, 3, 3
+    dY = [O.round_to_bf16_bits(rng.standard_normal((M, Ns))) for _ in range(p)]
+    W = [O.round_to_bf16_bits(rng.standard_normal((Kin, Ns))) for _ in range(p)]
+    dYc = np.concatenate([O.bf16_bits_to_f64(d) for d in dY], axis=1)    # [M, p*Ns]
+    Wc = np.concatenate([O.bf16_bits_to_f64(w) for w in W], axis=1)      # [Kin, p*Ns]
+    exact = _exact_matmul(dYc, Wc.T)
+    sl = o.matmul_dx_reducescatter(dY, W)
+    if len(sl) != p or any(s.shape != (M // p, Kin) for s in sl):
+        return False
+    return all(abs(sl[r][i, j] - float(exact[r * (M // p) + i][j])) <= 1e-14 * max(1.0, abs(float(exact[r * (M // p) + i][j])))
+               for r in range(p) for i in range(M // p) for j in range(Kin))
+
+
 def pin_dx_autograd(o):
     """The oracle's dX equals autograd's gradient of the column-parallel forward.
 
@@ -380,7 +398,8 @@ def pin_mlp_sp_unsharded(o):
 
 
 PINS = [pin_tiny_row_parallel, pin_tiny_reducescatter, pin_tiny_column_backward, pin_tiny_allgather,
-        pin_worked_example, pin_brute_force_unsharded, pin_brute_force_dx, pin_dx_autograd,
+        pin_worked_example, pin_brute_force_unsharded, pin_brute_force_dx, pin_brute_force_dx_reducescatter,
+        pin_dx_autograd,
         pin_column_identity, pin_chunked_equals_whole, pin_rs_slices, pin_chunk_bounds,
         pin_round_bf16, pin_message_bf16_golden, pin_message_bf16_integer_exact,
         pin_message_bf16_error_bound, pin_message_bf16_dx, pin_weight_grad_golden, pin_weight_grad_autograd,
@@ -459,6 +478,7 @@ def _m_slices_reversed():
         return O.scatter_rows(Y, p)[::-1]
     m = _Mutant(scatter_rows=scatter_rows)
     m.matmul_reducescatter = lambda Xs, Ws: scatter_rows(O.matmul_allreduce(Xs, Ws), len(Xs))
+    m.matmul_dx_reducescatter = lambda dY, W: scatter_rows(O.matmul_dx(dY, W), len(dY))
     return m
 
 
