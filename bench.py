@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
+ROTATION_BYTES = 512 << 20    # inputs streamed per rotation of the input sets: twice the last-level cache
 
 
 def parse():
@@ -50,7 +51,9 @@ def parse():
                     help="auto (= unfused on one GPU), unfused, persistent, two_stream, tile, gemm_only")
     ap.add_argument("--message", default="fp32", choices=["fp32", "bf16"],
                     help="precision of the shard partials (the 2-byte message variant: bf16)")
-    ap.add_argument("--sets", type=int, default=2, help="input sets rotated to defeat the 256 MB last-level cache")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input sets rotated to defeat the 256 MB last-level cache (default: enough that one "
+                         "rotation streams at least 512 MiB, 2 to 8 sets)")
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed steps run for at least this long before the warmup steps: the GPU's clocks "
                          "take ~0.1-0.2 s of sustained load to reach their steady state")
@@ -105,10 +108,12 @@ def main():
     handle = tp.Handle(0)
 
     # --- inputs (generated on the GPU with seeded generators, kept resident) ---
-    sets = []
-    for s in range(args.sets):
-        inp = inputs.make_inputs(wl, seed=s, device=dev)
-        sets.append(inp)
+    sets = [inputs.make_inputs(wl, seed=0, device=dev)]
+    if args.sets <= 0:
+        set_bytes = sum(t.numel() * t.element_size() for t in list(sets[0].X) + list(sets[0].W))
+        args.sets = min(8, max(2, -(-ROTATION_BYTES // set_bytes)))
+    for s in range(1, args.sets):
+        sets.append(inputs.make_inputs(wl, seed=s, device=dev))
     M, N, K, p = wl.M, wl.N, wl.K, wl.p
     flops = wl.flops()
     kflops = flops / 2 if wl.op == "mlp_sp" else flops    # the timed launch of the MLP block is FC2
