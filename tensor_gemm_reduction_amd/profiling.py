@@ -15,6 +15,12 @@
   python -m tensor_gemm_reduction_amd.profiling mfma <counter dir> <kernel-substring> <out.txt> <command...>
       Matrix-core busy fraction, the clock the GPU ran at and TFLOP/s per
       dispatch, from one --pmc pass over MFMA_COUNTERS.
+
+  python -m tensor_gemm_reduction_amd.profiling overlap <trace dir> <dispatches per step> <out.txt> <command...>
+      The last step's dispatches of the library's kernels (queue, start and
+      end relative to the step), and how long GEMM and reduction kernels ran
+      at the same time: the two-stream scheduler's overlap, from a
+      --kernel-trace run.
 """
 from __future__ import annotations
 
@@ -69,6 +75,64 @@ def last_dispatches(trace_path: str, name_sub: str, k: int):
     names = sorted(by_name, key=lambda m: -sum(d for _, d in by_name[m]))
     label = names[0] if len(names) == 1 else f"{len(names)} kernels per step ({', '.join(m[:40] for m in names)})"
     return label, total, n
+
+
+def _union(intervals):
+    """Merge [start, end) intervals; returns the sorted disjoint list."""
+    out = []
+    for a, b in sorted(intervals):
+        if out and a <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], b)
+        else:
+            out.append([a, b])
+    return out
+
+
+def _covered(u):
+    return sum(b - a for a, b in u)
+
+
+def _intersect(u, v):
+    """Length of the intersection of two disjoint sorted interval lists."""
+    i = j = 0
+    total = 0
+    while i < len(u) and j < len(v):
+        lo, hi = max(u[i][0], v[j][0]), min(u[i][1], v[j][1])
+        if hi > lo:
+            total += hi - lo
+        if u[i][1] < v[j][1]:
+            i += 1
+        else:
+            j += 1
+    return total
+
+
+def overlap(trace_path: str, per_step: int, out_path: str, command: str) -> dict:
+    """Summarise the last `per_step` dispatches of the library's kernels."""
+    rows = [r for r in _rows(trace_path, "kernel_trace.csv") if "tpf::" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    step = rows[-per_step:]
+    t0 = min(int(r["Start_Timestamp"]) for r in step)
+    t1 = max(int(r["End_Timestamp"]) for r in step)
+    kind = lambda r: "reduce" if "reduce" in r["Kernel_Name"] else "gemm"
+    spans = {"gemm": [], "reduce": []}
+    lines = [f"# rocprofv3 kernel trace: the last step's {per_step} dispatches (microseconds from the step's first start)",
+             f"# command: {command}", "",
+             f"{'#':>3s} {'kind':6s} {'queue':>5s} {'start_us':>9s} {'end_us':>9s} {'dur_us':>8s}"]
+    for i, r in enumerate(step):
+        a, b = int(r["Start_Timestamp"]) - t0, int(r["End_Timestamp"]) - t0
+        spans[kind(r)].append((a, b))
+        lines.append(f"{i:3d} {kind(r):6s} {r.get('Queue_Id', '?'):>5s} {a / 1e3:9.2f} {b / 1e3:9.2f} {(b - a) / 1e3:8.2f}")
+    g, red = _union(spans["gemm"]), _union(spans["reduce"])
+    res = {"step_us": (t1 - t0) / 1e3, "gemm_busy_us": _covered(g) / 1e3, "reduce_busy_us": _covered(red) / 1e3,
+           "both_us": _intersect(g, red) / 1e3}
+    res["reduce_hidden_frac"] = res["both_us"] / res["reduce_busy_us"] if res["reduce_busy_us"] else 0.0
+    lines += ["", f"step {res['step_us']:.2f} us; a GEMM kernel running {res['gemm_busy_us']:.2f} us; "
+                  f"a reduction kernel running {res['reduce_busy_us']:.2f} us, of which {res['both_us']:.2f} us "
+                  f"({100 * res['reduce_hidden_frac']:.0f} %) beside a GEMM kernel"]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return res
 
 
 def counter_per_dispatch(path: str, counter: str, kernel_sub: str) -> float:
@@ -215,6 +279,9 @@ if __name__ == "__main__":
     elif cmd == "yardstick":
         # yardstick <csv dir> <out.txt> <bench_json> <command...>: the vendor GEMM kernels, full names
         stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[5:]), sys.argv[4], name_filter=("Cijk",), width=400)
+    elif cmd == "overlap":
+        # overlap <trace dir> <dispatches per step> <out.txt> <command...>
+        overlap(sys.argv[2], int(sys.argv[3]), sys.argv[4], command=" ".join(sys.argv[5:]))
     elif cmd == "mfma":
         # mfma <counter dir> <kernel-substring> <out.txt> <command...>
         mfma(sys.argv[2], sys.argv[3], sys.argv[4], command=" ".join(sys.argv[5:]))

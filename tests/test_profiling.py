@@ -7,7 +7,7 @@ import json
 
 from tensor_gemm_reduction_amd import profiling as P
 
-TRACE_COLS = ["Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+TRACE_COLS = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Queue_Id"]
 COUNTER_COLS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
 
 
@@ -24,7 +24,8 @@ def trace(tmp_path, launches):
     d = tmp_path / "trace"
     d.mkdir()
     write_csv(d / "run_kernel_trace.csv", TRACE_COLS,
-              [{"Kernel_Name": n, "Start_Timestamp": t0, "End_Timestamp": t0 + dt} for n, t0, dt in launches])
+              [{"Kernel_Name": n, "Start_Timestamp": t0, "End_Timestamp": t0 + dt, "Queue_Id": 0}
+               for n, t0, dt in launches])
     return str(d)
 
 
@@ -110,3 +111,20 @@ def test_mfma_summary(tmp_path):
     peak = simds * 1024 * clk / 1e12                   # 2097 TFLOP/s at 2.0 GHz
     assert abs(float(line[6]) - peak) < 0.5
     assert abs(float(line[7]) - 1000 / peak) < 5e-4
+
+
+def test_overlap_of_gemm_and_reduction(tmp_path):
+    g, r = "tpf::tile_kernel<A, 0, 0>", "tpf::reduce_rows_kernel"
+    # an earlier step, then the step summarised: GEMMs 0-100, 90-200, 200-300 ns,
+    # reductions 95-120 (inside the GEMMs), 290-330 (10 ns inside) and 340-350 (alone)
+    launches = [(g, 0, 50), (r, 60, 10)]
+    base = 1000
+    launches += [(g, base, 100), (g, base + 90, 110), (g, base + 200, 100),
+                 (r, base + 95, 25), (r, base + 290, 40), (r, base + 340, 10)]
+    out = tmp_path / "o.txt"
+    res = P.overlap(trace(tmp_path, launches), 6, str(out), "test")
+    assert abs(res["step_us"] - 0.350) < 1e-12
+    assert abs(res["gemm_busy_us"] - 0.300) < 1e-12
+    assert abs(res["reduce_busy_us"] - 0.075) < 1e-12
+    assert abs(res["both_us"] - 0.035) < 1e-12        # 25 + 10 ns
+    assert len(out.read_text().splitlines()) == 4 + 6 + 2
