@@ -69,3 +69,16 @@ def test_mlp_sp_bytes():
     assert bench.kernel_bytes(wl, F32, "unfused") == ops + p * nbytes((M, N), F32)
     assert bench.kernel_bytes(wl, F32, "fold") == ops + 2 * (p - 1) * nbytes((M, N), F32) + nbytes((M, N), BF16)
     assert wl.flops() == 2 * (2 * M * N * K * p)     # FC1 and FC2
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: --gpus N > 1 exits with status 2 and says so,
+    before it touches a GPU."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
