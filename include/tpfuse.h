@@ -224,6 +224,18 @@ int tpf_matmul_dx(tpf_handle h, int sem, int p, int64_t M, int64_t K_in, int64_t
 int tpf_weight_grad(tpf_handle h, int p, int64_t M, int64_t R, int64_t C, const void* const* A,
                     const void* const* B, void* const* dW, int dw_dtype, void* stream);
 
+/* Input gradient of a row-parallel Linear (cnblogs §四 backward: with
+ * Y = sum_k X_k W_k the output gradient dY reaches every rank whole, and each
+ * rank's input gradient is a local GEMM, no communication).
+ *   dX[k] = dY W[k]^T, k = 0..p-1, summed over the N columns in fp32 and
+ *   rounded once to dx_dtype (TPF_BF16 or TPF_F32):
+ *   dY: [M, N] bf16 (one tensor, read by every shard), W[k]: [K_shard, N]
+ *   bf16 (the forward weights, used transposed), dX[k]: [M, K_shard].
+ *   K_shard and N must be multiples of 8; no workspace; the kernel timed by
+ *   tpf_debug_set_kernel_timing is this call's only launch. */
+int tpf_rowpar_dx(tpf_handle h, int p, int64_t M, int64_t K_shard, int64_t N, const void* dY,
+                  const void* const* W, void* const* dX, int dx_dtype, void* stream);
+
 /* The MLP block under sequence parallelism (cnblogs §7.1 and §11.3: the
  * column-parallel FC1 and row-parallel FC2 need no communication between
  * them; with sequence parallelism the block's input is all-gathered and its

@@ -310,6 +310,17 @@ def weight_grad(A_shards: Sequence, B_shards: Sequence) -> List[np.ndarray]:
     return [_f64(a).T @ _f64(b) for a, b in zip(A_shards, B_shards)]
 
 
+def rowpar_dx(dY, W_shards: Sequence) -> List[np.ndarray]:
+    """dX_k = dY W_k^T for every shard, float64.
+
+    Row-parallel Linear Y = sum_k X_k W_k (cnblogs §四): the output gradient
+    dY reaches every rank whole, and dL/dX_k = dY W_k^T is each rank's local
+    product; no communication.
+    """
+    d = _f64(dY)
+    return [d @ _f64(w).T for w in W_shards]
+
+
 # --------------------------------------------------------------------------
 # The MLP block under sequence parallelism (cnblogs §7.1 and §11.3):
 # AllGather -> column-parallel FC1 -> GeLU -> row-parallel FC2 -> ReduceScatter

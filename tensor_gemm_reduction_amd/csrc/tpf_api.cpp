@@ -756,6 +756,47 @@ int tpf_weight_grad(tpf_handle h, int p, int64_t M, int64_t R, int64_t C, const 
   return TPF_OK;
 }
 
+int tpf_rowpar_dx(tpf_handle h, int p, int64_t M, int64_t K_shard, int64_t N, const void* dY,
+                  const void* const* W, void* const* dX, int dx_dtype, void* stream) {
+  if (p < 1 || p > kMaxShards) return fail(TPF_ERR_SHAPE, "p must be in [1, " + std::to_string(kMaxShards) + "]");
+  if (M <= 0 || K_shard <= 0 || N <= 0) return fail(TPF_ERR_SHAPE, "M, K_shard and N must be positive");
+  if (M > INT32_MAX || K_shard > INT32_MAX || N > INT32_MAX)
+    return fail(TPF_ERR_SHAPE, "M, K_shard and N must fit in 31 bits");
+  if (K_shard % 8 != 0 || N % 8 != 0) return fail(TPF_ERR_ALIGNMENT, "K_shard and N must be multiples of 8");
+  const int64_t lim = ((int64_t)1 << 31) - 1;
+  if (M * N * 2 > lim || K_shard * N * 2 > lim || M * K_shard * 4 > lim)
+    return fail(TPF_ERR_UNSUPPORTED, "each operand and each output must be smaller than 2 GiB");
+  if (!valid_dtype(dx_dtype)) return fail(TPF_ERR_INVALID_ARG, "unknown output dtype");
+  int st;
+  if ((st = check_ptr(dY, "dY"))) return st;
+  if ((st = check_ptrs(W, p, "W"))) return st;
+  if ((st = check_ptrs(const_cast<const void* const*>(dX), p, "dX"))) return st;
+  if ((st = check_handle(h))) return st;
+  if ((st = set_device(h))) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // dX[k] [M, K_shard] = dY W[k]^T: every shard reads the same dY [M][N]; the
+  // weights stay in their forward layout [K_shard][N] and are used
+  // transposed (NK tiles, as in the column-parallel dX).
+  GemmOperands g{};
+  for (int k = 0; k < p; ++k) {
+    g.A[k] = reinterpret_cast<const __bf16*>(dY);
+    g.B[k] = reinterpret_cast<const __bf16*>(W[k]);
+    g.dstv[k] = dX[k];
+  }
+  g.lda = N;
+  g.a_rows = (int)M;
+  g.ldb = N;
+  g.b_rows = (int)K_shard;
+  g.ldd = K_shard;
+  g.dst_dtype = out_kind(dx_dtype);
+  g.M = (int)M;
+  g.N = (int)K_shard;
+  g.K = (int)N;
+  g.nshard = p;
+  TPF_TIMED(h, s, launch_gemm_rows(pick_cfg(M), B_NK, g, 0, (int)M, s));
+  return TPF_OK;
+}
+
 int tpf_mlp_sp(tpf_handle h, int p, int64_t S, int64_t Hd, int64_t F, const void* const* X_slices,
                const void* const* W1, const void* const* W2, void* X_gathered, void* const* H,
                void* const* Y_slices, int y_dtype, int n_chunks, int sched, void* ws, size_t ws_bytes,

@@ -54,6 +54,7 @@ SIGNATURES = {
     "tpf_debug_set_kernel_timing": (_I, [_VP, _I]),
     "tpf_debug_kernel_times": (_I, [_VP, ctypes.POINTER(ctypes.c_float), _I]),
     "tpf_debug_last_sched": (_I, [_VP]),
+    "tpf_rowpar_dx": (_I, [_VP, _I, _I64, _I64, _I64, _VP, _VP, _VP, _I, _VP]),
     "tpf_status_string": (ctypes.c_char_p, [_I]),
     "tpf_last_error": (ctypes.c_char_p, []),
     "tpf_version": (_I, []),
@@ -400,6 +401,28 @@ def weight_grad(A: List[torch.Tensor], B: List[torch.Tensor], out_dtype=torch.fl
                                  ptr_array([b.data_ptr() for b in B]), ptr_array([d.data_ptr() for d in dW]),
                                  _dtype_code(dW[0].dtype), _stream_ptr(stream)))
     return dW
+
+
+def rowpar_dx(dY: torch.Tensor, W: List[torch.Tensor], out_dtype=torch.bfloat16, dX=None,
+              handle: Optional[Handle] = None, stream=None) -> List[torch.Tensor]:
+    """dX[k] = dY @ W[k]^T for every shard k: the input gradient of a
+    row-parallel Linear (dY [M, N] whole on every rank, W[k] [K_shard, N])."""
+    p = len(W)
+    _need(p >= 1, "W: no shards given")
+    M, N = dY.shape
+    Ks = W[0].shape[0]
+    dev = _check("dY", [dY], (M, N))
+    _check("W", W, (Ks, N), device=dev)
+    if dX is None:
+        dX = [torch.empty((M, Ks), dtype=out_dtype, device=dev) for _ in range(p)]
+    _check_shards("dX", dX, p)
+    _check("dX", dX, (M, Ks), OUT_DTYPES, dev)
+    _need(len({d.dtype for d in dX}) == 1, "dX: the shards differ in dtype")
+    h = _handle(handle, dev)
+    check(load().tpf_rowpar_dx(h.ptr, p, M, Ks, N, dY.data_ptr(), ptr_array([w.data_ptr() for w in W]),
+                               ptr_array([d.data_ptr() for d in dX]), _dtype_code(dX[0].dtype),
+                               _stream_ptr(stream)))
+    return dX
 
 
 def mlp_sp(X_slices: List[torch.Tensor], W1: List[torch.Tensor], W2: List[torch.Tensor], out_dtype=torch.bfloat16,

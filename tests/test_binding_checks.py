@@ -23,6 +23,7 @@ OPS_ON_HOST = {
     "dx": lambda: tp.matmul_dx([host(64, 16)] * 2, [host(32, 16)] * 2),
     "weight_grad": lambda: tp.weight_grad([host(64, 32)] * 2, [host(64, 16)] * 2),
     "mlp_sp": lambda: tp.mlp_sp([host(32, 16)] * 2, [host(16, 24)] * 2, [host(24, 16)] * 2),
+    "rowpar_dx": lambda: tp.rowpar_dx(host(64, 16), [host(32, 16)] * 2),
 }
 
 
@@ -67,6 +68,8 @@ def test_device_tensor_checks():
         (lambda: tp.matmul_dx([dev(64, 16)] * 2, [dev(32, 16)] * 2, tp.REDUCESCATTER, dX=[dev(64, 32)] * 2),
          "dX\\[0\\] has shape"),
         (lambda: tp.weight_grad([dev(64, 32)] * 2, [dev(60, 16)] * 2), "B\\[0\\] has shape"),
+        (lambda: tp.rowpar_dx(dev(64, 16), [dev(32, 16), dev(32, 8)]), "W\\[1\\] has shape"),
+        (lambda: tp.rowpar_dx(dev(64, 16), [dev(32, 16)] * 2, dX=[dev(64, 32)]), "one per shard"),
         (lambda: tp.mlp_sp([dev(32, 16)] * 2, [dev(16, 24)] * 2, [dev(16, 24)] * 2), "W2\\[0\\] has shape"),
         (lambda: tp.mlp_sp([dev(32, 16)] * 2, [dev(16, 24)] * 2, [dev(24, 16)] * 2,
                            H=[dev(64, 24, dtype=torch.float32)] * 2), "H\\[0\\] has dtype"),

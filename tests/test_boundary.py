@@ -191,6 +191,27 @@ def test_weight_grad_checks():
     assert "handle" in _err(None)
 
 
+def test_rowpar_dx_checks():
+    lib = tp.load()
+    P2 = tp.ptr_array([A16] * 2)
+
+    def call(p=2, M=64, K=64, N=64, dY=A16, W=P2, D=P2, dtype=tp.BF16):
+        return lib.tpf_rowpar_dx(None, p, M, K, N, dY, W, D, dtype, None)
+    assert call(p=0) == tp.ERR_SHAPE
+    assert call(p=17) == tp.ERR_SHAPE
+    assert call(M=0) == tp.ERR_SHAPE
+    assert call(K=12) == tp.ERR_ALIGNMENT
+    assert call(N=20) == tp.ERR_ALIGNMENT
+    assert call(dtype=5) == tp.ERR_INVALID_ARG
+    assert call(dY=None) == tp.ERR_INVALID_ARG
+    assert call(dY=MIS) == tp.ERR_ALIGNMENT
+    assert call(W=tp.ptr_array([A16, MIS])) == tp.ERR_ALIGNMENT
+    assert call(D=tp.ptr_array([A16, 0])) == tp.ERR_INVALID_ARG
+    assert call(M=1 << 20, N=1 << 12) == tp.ERR_UNSUPPORTED       # 8 GiB operand
+    assert call() == tp.ERR_INVALID_ARG                             # all valid: the NULL handle
+    assert "handle" in _err(None)
+
+
 def test_handle_calls_reject_null():
     lib = tp.load()
     assert lib.tpf_sync_status(None, None) == tp.ERR_INVALID_ARG

@@ -421,6 +421,37 @@ def test_weight_grad_integer_exact():
         assert np.array_equal(d[k].cpu().double().numpy(), refs[k]), k
 
 
+@pytest.mark.parametrize("p,M,K,N", [(4, 300, 136, 520), (2, 16, 64, 1024), (8, 64, 264, 72), (3, 1, 8, 8)])
+def test_rowpar_dx_parity(p, M, K, N):
+    """Row-parallel input gradients dX_k = dY W_k^T (one dY for every shard)
+    against the oracle, in fp32 and bf16, ragged in every dimension."""
+    say(f"row-parallel dX p={p} M={M} K_shard={K} N={N}")
+    dYh = inputs.draw((M, N), ("normal", 1.0), 96000)
+    Wh = shards([(K, N)] * p, ("normal", 0.05), 97)
+    refs = O.rowpar_dx(inputs.bf16_to_bits(dYh), bits(Wh))
+    dY, W = dYh.to(DEV), gpu(Wh)
+    d32 = tp.rowpar_dx(dY, W, torch.float32)
+    d16 = tp.rowpar_dx(dY, W, torch.bfloat16)
+    torch.cuda.synchronize()
+    for k in range(p):
+        what = f"row-parallel dX shard {k}"
+        assert_f32(d32[k], refs[k], what)
+        assert_bf16(d16[k], refs[k], what)
+        assert_bf16_is_rne_of_f32(d16[k], d32[k], what)
+
+
+def test_rowpar_dx_integer_exact():
+    p, M, K, N = 2, 300, 136, 264
+    rng = np.random.default_rng(98)
+    dYh = torch.from_numpy(rng.integers(-2, 3, (M, N)).astype(np.float32)).to(torch.bfloat16)
+    Wh = [torch.from_numpy(rng.integers(-2, 3, (K, N)).astype(np.float32)).to(torch.bfloat16) for _ in range(p)]
+    refs = O.rowpar_dx(inputs.bf16_to_bits(dYh), bits(Wh))
+    d = tp.rowpar_dx(dYh.to(DEV), gpu(Wh), torch.float32)
+    torch.cuda.synchronize()
+    for k in range(p):
+        assert np.array_equal(d[k].cpu().double().numpy(), refs[k]), k
+
+
 # ---------------------------------------------------------------------------
 # MLP block under sequence parallelism
 # ---------------------------------------------------------------------------

@@ -161,6 +161,36 @@ def pin_brute_force_dx_reducescatter(o):
                for r in range(p) for i in range(M // p) for j in range(Kin))
 
 
+def pin_brute_force_rowpar_dx(o):
+    """Row-parallel input gradients side by side equal dY W^T with the
+    unsharded W = [W_0; ...; W_{p-1}] (cnblogs §四), exact rational brute force."""
+    rng = np.random.default_rng(26)
+    M, Ks, N, p = 3, 2, 5, 3
+    dY = O.round_to_bf16_bits(rng.standard_normal((M, N)))
+    W = [O.round_to_bf16_bits(rng.standard_normal((Ks, N))) for _ in range(p)]
+    Wc = np.concatenate([O.bf16_bits_to_f64(w) for w in W], axis=0)      # [p*Ks, N]
+    exact = _exact_matmul(O.bf16_bits_to_f64(dY), Wc.T)                  # [M, p*Ks]
+    d = o.rowpar_dx(dY, W)
+    if len(d) != p or any(x.shape != (M, Ks) for x in d):
+        return False
+    return all(abs(d[k][i, j] - float(exact[i][k * Ks + j])) <= 1e-14 * max(1.0, abs(float(exact[i][k * Ks + j])))
+               for k in range(p) for i in range(M) for j in range(Ks))
+
+
+def pin_rowpar_dx_autograd(o):
+    """The oracle's dX_k equals autograd's gradient of Y = sum_k X_k W_k with
+    respect to X_k (float64), for loss = <G, Y>."""
+    rng = np.random.default_rng(27)
+    M, Ks, N, p = 4, 3, 6, 2
+    W = [O.round_to_bf16_bits(rng.standard_normal((Ks, N))) for _ in range(p)]
+    G = O.round_to_bf16_bits(rng.standard_normal((M, N)))
+    Xt = [torch.tensor(rng.standard_normal((M, Ks)), requires_grad=True) for _ in range(p)]
+    Y = sum(x @ torch.tensor(O.bf16_bits_to_f64(w)) for x, w in zip(Xt, W))
+    (Y * torch.tensor(O.bf16_bits_to_f64(G))).sum().backward()
+    d = o.rowpar_dx(G, W)
+    return all(np.allclose(dk, x.grad.numpy(), rtol=1e-13, atol=1e-13) for dk, x in zip(d, Xt))
+
+
 def pin_dx_autograd(o):
     """The oracle's dX equals autograd's gradient of the column-parallel forward.
 
@@ -399,7 +429,7 @@ def pin_mlp_sp_unsharded(o):
 
 PINS = [pin_tiny_row_parallel, pin_tiny_reducescatter, pin_tiny_column_backward, pin_tiny_allgather,
         pin_worked_example, pin_brute_force_unsharded, pin_brute_force_dx, pin_brute_force_dx_reducescatter,
-        pin_dx_autograd,
+        pin_dx_autograd, pin_brute_force_rowpar_dx, pin_rowpar_dx_autograd,
         pin_column_identity, pin_chunked_equals_whole, pin_rs_slices, pin_chunk_bounds,
         pin_round_bf16, pin_message_bf16_golden, pin_message_bf16_integer_exact,
         pin_message_bf16_error_bound, pin_message_bf16_dx, pin_weight_grad_golden, pin_weight_grad_autograd,
@@ -471,6 +501,13 @@ def _m_dx_untransposed():
             out = t if out is None else out + t
         return out
     return _Mutant(matmul_dx=matmul_dx)
+
+
+def _m_rowpar_dx_untransposed():
+    def rowpar_dx(dY, W):
+        d = O.bf16_bits_to_f64(dY)
+        return [d @ O.bf16_bits_to_f64(w).reshape(w.shape[1], w.shape[0]) for w in W]
+    return _Mutant(rowpar_dx=rowpar_dx)
 
 
 def _m_slices_reversed():
@@ -576,7 +613,7 @@ def _m_mlp_w2_transposed_shards():
     return m
 
 
-MUTANTS = [_m_dropped_shard, _m_sign, _m_dx_untransposed, _m_slices_reversed, _m_gather_reversed,
+MUTANTS = [_m_dropped_shard, _m_sign, _m_dx_untransposed, _m_rowpar_dx_untransposed, _m_slices_reversed, _m_gather_reversed,
            _m_round_truncate, _m_round_via_f32, _m_chunk_lastshort, _m_pipeline_serial,
            _m_message_truncated, _m_message_unrounded, _m_message_fold_f64, _m_message_fold_reversed,
            _m_weight_grad_swapped, _m_weight_grad_shard_shift, _m_gelu_tanh, _m_mlp_w2_transposed_shards]
