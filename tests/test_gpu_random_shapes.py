@@ -8,6 +8,7 @@ the tile order, the ragged last tile row/column and the fold epilogue are
 exercised away from the single-tile corner."""
 import random
 
+import numpy as np
 import pytest
 import torch
 
@@ -104,3 +105,34 @@ def test_random_shape(op, p, M, N, K, n, seed):
     for sched, (a, b) in outs.items():
         assert_bitwise(a, base32, f"{op} {sched} fp32 vs unfused")
         assert_bitwise(b, base16, f"{op} {sched} bf16 vs unfused")
+
+
+def rowpar_cases(seed, count):
+    rng = random.Random(seed)
+    for i in range(count):
+        p = rng.choice([1, 2, 3, 5, 8, 16])
+        M = rng.choice([1, 7, 31, 33, 64, 65, 300, 520, 1031])
+        K = 8 * rng.randint(1, 50)
+        N = 8 * rng.randint(1, 70)
+        yield pytest.param(p, M, K, N, rng.randint(0, 1 << 30), id=f"rowpar{seed}-{i}-p{p}-M{M}-K{K}-N{N}")
+
+
+@pytest.mark.parametrize("p,M,K,N,seed", list(rowpar_cases(3, 12)))
+def test_random_rowpar_dx(p, M, K, N, seed):
+    """Row-parallel input gradients at random valid shapes: every shard's
+    dX_k = dY W_k^T against the oracle in fp32 and bf16, and the bf16 output
+    equal to the round-to-nearest-even of the fp32 one."""
+    print(f"random rowpar dx p={p} M={M} K_shard={K} N={N} seed={seed}", flush=True)
+    g = torch.Generator().manual_seed(seed)
+    dYh = torch.randn((M, N), generator=g).to(torch.bfloat16)
+    Wh = [(torch.randn((K, N), generator=g) * 0.05).to(torch.bfloat16) for _ in range(p)]
+    refs = O.rowpar_dx(inputs.bf16_to_bits(dYh), [inputs.bf16_to_bits(w) for w in Wh])
+    dY, W = dYh.to(DEV), [w.to(DEV) for w in Wh]
+    d32 = tp.rowpar_dx(dY, W, torch.float32)
+    d16 = tp.rowpar_dx(dY, W, torch.bfloat16)
+    torch.cuda.synchronize()
+    for k in range(p):
+        assert_f32(d32[k], refs[k], f"rowpar shard {k}")
+        assert_bf16(d16[k], refs[k], f"rowpar shard {k}")
+        want = O.round_to_bf16_bits(d32[k].cpu().double().numpy())
+        assert np.array_equal(inputs.bf16_to_bits(d16[k].cpu()), want), f"rowpar shard {k}: bf16 != RNE(fp32)"
