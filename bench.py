@@ -158,6 +158,15 @@ def main():
             tp.mlp_sp(inp.X, inp.W[:p], inp.W[p:], n_chunks=n, sched=sched, X_gathered=XG, H=Hs, Y=Ys, ws=ws,
                       handle=handle, message=msg)
         ws_bytes = ws.numel()
+    elif wl.op == "rowpar_dx":
+        # dX_k [M, K] = dY W_k^T, bf16 out (the gradient handed to the layer below)
+        dXs = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(p)]
+
+        def call(i, sched):
+            inp = sets[i % len(sets)]
+            tp.rowpar_dx(inp.X[0], inp.W, dX=dXs, handle=handle)
+        ws_bytes = 0
+        args.modes = "none"      # no reduction: there are no schedules to compare
     elif wl.op.startswith("wgrad"):
         # dW_k [K, N] = A_k^T B_k over M rows, fp32 out (the optimizer's input)
         dWs = [torch.empty((K, N), dtype=torch.float32, device=dev) for _ in range(p)]
@@ -403,6 +412,8 @@ def kernel_bytes(wl, part_bytes=4, sched="unfused"):
         return p * (2.0 * M * N + 2.0 * K * N) + 2.0 * (p - 1) * part_bytes * M * K + 2.0 * M * K
     if wl.op == "allgather":
         return 2.0 * M * K + 2.0 * K * N + 2.0 * M * N
+    if wl.op == "rowpar_dx":        # dY [M, N] (one, shared), W_k [K, N], dX_k [M, K] bf16
+        return 2.0 * M * N + p * (2.0 * K * N + 2.0 * M * K)
     if wl.op.startswith("wgrad"):   # A_k [M, K], B_k [M, N], dW_k [K, N] fp32
         return p * (2.0 * M * K + 2.0 * M * N + 4.0 * K * N)
     if wl.op == "mlp_sp":           # FC2 launch: H_k [M, K], W2_k [K, N], partials [M, N]
@@ -418,6 +429,8 @@ def kernel_name(sched, op=""):
     prices."""
     if op.startswith("wgrad"):
         return "tile_kernel A_KM (weight-gradient GEMM tiles, transposed A)"
+    if op == "rowpar_dx":
+        return "tile_kernel NK (row-parallel input-gradient tiles, transposed weights, one dY for every shard)"
     if op == "mlp_sp":
         if sched == "fold":
             return ("tile_kernel pair (FC2: shards 0..p-2 into partials, then shard p-1 with the fold epilogue; "
@@ -457,6 +470,8 @@ def cpu_baseline(wl, inp, seconds):
             O.matmul_allreduce(Xb, Wb, rows=r)
         elif wl.op == "dx":
             O.matmul_dx(Xb, Wb, rows=r)
+        elif wl.op == "rowpar_dx":
+            O.rowpar_dx(Xb[0][:rows], Wb)
         elif wl.op.startswith("wgrad"):
             A, B = (Xb * wl.p, Wb) if wl.op == "wgrad_col" else (Xb, Wb * wl.p)
             O.weight_grad([a[:, :rows] for a in A], B)

@@ -125,6 +125,10 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("dw_row", "wgrad_row", 4, 4096, 4096, 4096, (1,),
                  ("normal", 1.0), ("normal", 1.0), index=8, out_dtypes=("f32",),
                  note="row-parallel weight gradient dW_k = X_k^T dY of the MLP down projection"),
+        Workload("dx_row", "rowpar_dx", 4, 4096, 4096, 4096, (1,),
+                 ("normal", 1.0), ("normal", 0.02), index=10,
+                 note="row-parallel input gradient dX_k = dY W_k^T of the MLP down projection "
+                      "(N = the layer's output width, K = the shard's input width)"),
     ]
 }
 
@@ -187,6 +191,7 @@ def make_inputs(wl: Workload, seed: int = 0, mode: str = "random", device: str =
       mlp_sp:                    X[r] [M/p, N] (slices), W[k] = W1_k [N, K], W[p + k] = W2_k [K, N]
       wgrad_col:                 X[0] = gathered input [M, K], W[k] = dY_k [M, N]
       wgrad_row:                 X[k] = X_k [M, K], W[0] = dY [M, N]
+      rowpar_dx:                 X[0] = dY [M, N], W[k] = W_k [K, N]
     """
     M = wl.M if M is None else M
     N = wl.N if N is None else N
@@ -225,6 +230,10 @@ def make_inputs(wl: Workload, seed: int = 0, mode: str = "random", device: str =
         for k in range(p):
             inp.X.append(draw((M, K), wl.x_dist, tensor_seed(idx, "X", k, seed), mode, device))
         inp.W.append(draw((M, N), wl.w_dist, tensor_seed(idx, "dY", 0, seed), mode, device))
+    elif wl.op == "rowpar_dx":
+        inp.X.append(draw((M, N), wl.x_dist, tensor_seed(idx, "dY", 0, seed), mode, device))
+        for k in range(p):
+            inp.W.append(draw((K, N), wl.w_dist, tensor_seed(idx, "W", k, seed), mode, device))
     else:
         raise ValueError(f"unknown op {wl.op!r}")
     return inp

@@ -82,3 +82,10 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_rowpar_dx_bytes():
+    wl = WORKLOADS["dx_row"]        # dY [M, N] read once for every shard, W_k [K, N], dX_k [M, K] bf16
+    p, M, N, K = wl.p, wl.M, wl.N, wl.K
+    assert bench.kernel_bytes(wl) == nbytes((M, N), BF16) + p * (nbytes((K, N), BF16) + nbytes((M, K), BF16))
+    assert wl.flops() == 2 * M * N * K * p
