@@ -107,6 +107,28 @@ def test_fullsize_weight_grad(name):
         assert_bf16_is_rne_of_f32(d16[k], d32[k], what)
 
 
+def test_fullsize_rowpar_dx():
+    """Row-parallel input gradients at the dx_row size (dY [4096,4096] shared
+    by p = 4 shards, W_k [4096,4096]): sampled rows of every dX_k against the
+    oracle (row i of dY W_k^T needs row i of dY only), bf16 output equal to the
+    RNE rounding of the fp32 output."""
+    wl = inputs.WORKLOADS["dx_row"]
+    say(f"full-size dx_row: p={wl.p} M={wl.M} K_shard={wl.K} N={wl.N}")
+    inp = inputs.make_inputs(wl, seed=0, device="cuda")
+    dY = inp.X[0]
+    d32 = tp.rowpar_dx(dY, inp.W, torch.float32)
+    d16 = tp.rowpar_dx(dY, inp.W, torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.M, 16, seed=11)
+    idx = torch.as_tensor(rows, device="cuda")
+    refs = O.rowpar_dx(inputs.bf16_to_bits(dY.index_select(0, idx)), bits(inp.W))
+    for k in range(wl.p):
+        what = f"dx_row dX_{k} rows={len(rows)}"
+        assert_f32(d32[k].index_select(0, idx), refs[k], what)
+        assert_bf16(d16[k].index_select(0, idx), refs[k], what)
+        assert_bf16_is_rne_of_f32(d16[k], d32[k], what)
+
+
 def test_fullsize_mlp_sp():
     """The MLP block at full size: the gathered input exactly, sampled rows of
     every activation against the float64 GeLU, sampled output rows against
