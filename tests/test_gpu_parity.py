@@ -247,6 +247,36 @@ def test_graph_capture_replays_match_eager(sched):
     h.close()
 
 
+def test_graph_capture_rowpar_dx_replays_match_eager():
+    """The row-parallel input-gradient call enqueues one kernel, so it can be
+    captured: several replays, with eager calls between them, each equal to
+    the eager bits."""
+    p, M, K, N = 3, 300, 136, 264
+    say("graph capture rowpar_dx")
+    dYh = inputs.draw((M, N), ("normal", 1.0), 99000)
+    Wh = shards([(K, N)] * p, ("normal", 0.05), 99)
+    dY, W = dYh.to(DEV), gpu(Wh)
+    h = tp.Handle(0)
+    ref = [t.clone() for t in tp.rowpar_dx(dY, W, torch.bfloat16, handle=h)]
+    out = [torch.empty((M, K), dtype=torch.bfloat16, device=DEV) for _ in range(p)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tp.rowpar_dx(dY, W, dX=out, handle=h)
+    for i in range(3):
+        for o in out:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in range(p):
+            assert_bitwise(out[k], ref[k], f"rowpar_dx replay {i} shard {k}")
+        other = tp.rowpar_dx(dY, W, torch.bfloat16, handle=h)
+        torch.cuda.synchronize()
+        assert_bitwise(other[0], ref[0], f"rowpar_dx eager call {i}")
+    assert h.sync_status() == tp.OK
+    h.close()
+
+
 def test_tile_counters_reset_between_calls():
     """The tile scheduler's per-output-tile counters and queue shares return to
     zero at the end of every call: calls of different tile grids in a row
