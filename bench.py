@@ -43,7 +43,8 @@ ROTATION_BYTES = 512 << 20    # inputs streamed per rotation of the input sets: 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 20, or 100 for workloads under 0.1 TFLOP per step)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mlp_down")
     ap.add_argument("--chunks", type=int, default=0, help="0 = the workload's default")
@@ -94,6 +95,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "note": "plain device copy for counter calibration"}), flush=True)
         return
+
+    if args.steps is None:       # short steps need more repetitions for a steady figure
+        args.steps = 100 if inputs.WORKLOADS[args.workload].flops() < 1e11 else 20
 
     if args.yardstick:
         yardstick(args, inputs.WORKLOADS[args.workload])
