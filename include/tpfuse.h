@@ -6,12 +6,18 @@
  * the library computes every shard's local GEMM with bf16 matrix-core tiles,
  * keeps each shard's fp32 local output (the message a rank would send) in a
  * caller-provided workspace, and produces the cross-shard sum in the layout
- * that the collective's semantics require.  The output is split into
- * contiguous row chunks; the reduction of chunk c overlaps the GEMM of later
- * chunks (a persistent kernel with per-chunk ready counters, or two HIP
- * streams with per-chunk events).  The sum over shards is a left fold in
- * shard order k = 0..p-1 in fp32, rounded once to the output type, so results
- * are bit-identical for every chunk count and every scheduler.
+ * that the collective's semantics require.  Several schedulers order that
+ * work: chunked ones that cut the output into contiguous row chunks and
+ * overlap the reduction of chunk c with the GEMM of later chunks (a
+ * persistent kernel with per-chunk ready counters, two HIP streams with
+ * per-chunk events, or readiness per output tile), the unfused
+ * GEMM-then-reduce baseline, a fold of the reduction into the last shard's
+ * GEMM epilogue, and a single-launch path for decode-shaped row counts that
+ * keeps every shard's partial of an output tile on chip.  The default (AUTO)
+ * picks among the unchunked ones by shape (see TPF_SCHED_AUTO).  The sum over
+ * shards is a left fold in shard order k = 0..p-1 in fp32, rounded once to
+ * the output type, so results are bit-identical for every chunk count and
+ * every scheduler.
  *
  * Sources (web pages, cited by title and section):
  *  - ai-infra-kb M027 "compute-communication fusion" page, §01 (row-parallel
@@ -154,8 +160,10 @@ typedef struct tpf_context* tpf_handle;
  * device cannot be used. */
 int tpf_create(tpf_handle* h, int device);
 
-/* Release a handle after all work enqueued with it has finished (the call
- * synchronises the handle's side streams).  NULL is accepted. */
+/* Release a handle.  The caller must first let every call made with it
+ * finish (for instance by synchronising the streams it passed); the call
+ * itself synchronises only the handle's own side streams, never the whole
+ * device.  NULL is accepted. */
 int tpf_destroy(tpf_handle h);
 
 /* Bytes of workspace a call needs (0 if none), a pure function of its

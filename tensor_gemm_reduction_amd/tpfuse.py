@@ -7,6 +7,7 @@ the import of a call fails loudly; there is no fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import List, Optional, Sequence
@@ -120,6 +121,18 @@ def _stream_ptr(stream) -> int:
     return int(stream.cuda_stream)
 
 
+def _on(stream):
+    """Allocation context for buffers the library writes on `stream`.
+
+    torch's caching allocator ties a block to the stream that was current
+    when it was allocated and may hand it out again as soon as the tensor is
+    freed, ordered only against that stream.  Buffers the binding allocates
+    for a call (outputs, workspace) are therefore allocated with the call's
+    stream current, so a freed workspace cannot be reused while the library's
+    kernels on that stream still write it."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 class Handle:
     """A libtpfuse handle bound to one device (owns a side stream, events, counters)."""
 
@@ -194,12 +207,19 @@ def timeline_events(events: torch.Tensor, count: int):
 _default_handles = {}
 
 
-def default_handle(device: Optional[int] = None) -> Handle:
+def default_handle(device: Optional[int] = None, stream=None) -> Handle:
+    """The binding's handle for (device, stream).
+
+    A handle runs one call at a time (its persistent and tile schedulers keep
+    work-queue and readiness counters in the handle), and calls on different
+    streams may run at the same time, so every stream gets its own default
+    handle."""
     dev = torch.cuda.current_device() if device is None else device
-    h = _default_handles.get(dev)
+    key = (int(dev), _stream_ptr(stream) if stream is not None else _stream_ptr(torch.cuda.current_stream(dev)))
+    h = _default_handles.get(key)
     if h is None:
         h = Handle(dev)
-        _default_handles[dev] = h
+        _default_handles[key] = h
     return h
 
 
@@ -251,8 +271,8 @@ def _check_ws(ws, dev) -> None:
         _check("ws", [ws], tuple(ws.shape), (ws.dtype,), dev)
 
 
-def _handle(handle, dev) -> "Handle":
-    h = handle or default_handle(dev.index)
+def _handle(handle, dev, stream=None) -> "Handle":
+    h = handle or default_handle(dev.index, stream)
     _need(h.device == dev.index, f"handle is bound to device {h.device}, tensors are on {dev}")
     return h
 
@@ -262,12 +282,13 @@ def workspace_size(op: int, p: int, M: int, N: int, K: int, n_chunks: int = 1, s
     return int(load().tpf_workspace_size(op, p, M, N, K, n_chunks, _sched(sched, message)))
 
 
-def _ws(op, p, M, N, K, n_chunks, sched, ws, device, message="fp32"):
+def _ws(op, p, M, N, K, n_chunks, sched, ws, device, message="fp32", stream=None):
     need = workspace_size(op, p, M, N, K, n_chunks, sched, message)
     if need == 0:
         return ws, 0 if ws is None else ws.numel() * ws.element_size()
     if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        with _on(stream):
+            ws = torch.empty(need, dtype=torch.uint8, device=device)
     return ws, ws.numel() * ws.element_size()
 
 
@@ -283,11 +304,12 @@ def matmul_allreduce(X: List[torch.Tensor], W: List[torch.Tensor], out_dtype=tor
     dev = _check("X", X, (M, K))
     _check("W", W, (K, N), device=dev)
     if Y is None:
-        Y = torch.empty((M, N), dtype=out_dtype, device=dev)
+        with _on(stream):
+            Y = torch.empty((M, N), dtype=out_dtype, device=dev)
     _check("Y", [Y], (M, N), OUT_DTYPES, dev)
     _check_ws(ws, dev)
-    h = _handle(handle, dev)
-    ws, ws_bytes = _ws(OP_MATMUL_ALLREDUCE, p, M, N, K, n_chunks, sched, ws, dev, message)
+    h = _handle(handle, dev, stream)
+    ws, ws_bytes = _ws(OP_MATMUL_ALLREDUCE, p, M, N, K, n_chunks, sched, ws, dev, message, stream)
     check(load().tpf_matmul_allreduce(h.ptr, p, M, N, K, ptr_array([x.data_ptr() for x in X]),
                                       ptr_array([w.data_ptr() for w in W]), Y.data_ptr(), _dtype_code(Y.dtype),
                                       n_chunks, _sched(sched, message), ws.data_ptr() if ws is not None else None, ws_bytes,
@@ -307,13 +329,14 @@ def matmul_reducescatter(X: List[torch.Tensor], W: List[torch.Tensor], out_dtype
     dev = _check("X", X, (M, K))
     _check("W", W, (K, N), device=dev)
     if Y is None:
-        Y = [torch.empty((M // p, N), dtype=out_dtype, device=dev) for _ in range(p)]
+        with _on(stream):
+            Y = [torch.empty((M // p, N), dtype=out_dtype, device=dev) for _ in range(p)]
     _check_shards("Y", Y, p)
     _check("Y", Y, (M // p, N), OUT_DTYPES, dev)
     _need(len({y.dtype for y in Y}) == 1, "Y: the slices differ in dtype")
     _check_ws(ws, dev)
-    h = _handle(handle, dev)
-    ws, ws_bytes = _ws(OP_MATMUL_REDUCESCATTER, p, M, N, K, n_chunks, sched, ws, dev, message)
+    h = _handle(handle, dev, stream)
+    ws, ws_bytes = _ws(OP_MATMUL_REDUCESCATTER, p, M, N, K, n_chunks, sched, ws, dev, message, stream)
     check(load().tpf_matmul_reducescatter(h.ptr, p, M, N, K, ptr_array([x.data_ptr() for x in X]),
                                           ptr_array([w.data_ptr() for w in W]), ptr_array([y.data_ptr() for y in Y]),
                                           _dtype_code(Y[0].dtype), n_chunks, _sched(sched, message),
@@ -332,13 +355,14 @@ def allgather_matmul(X_slices: List[torch.Tensor], W: torch.Tensor, out_dtype=to
     N = W.shape[1]
     dev = _check("W", [W], (K, N))
     _check("X_slices", X_slices, (Ms, K), device=dev)
-    if X_gathered is None:
-        X_gathered = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    if Y is None:
-        Y = torch.empty((M, N), dtype=out_dtype, device=dev)
+    with _on(stream):
+        if X_gathered is None:
+            X_gathered = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        if Y is None:
+            Y = torch.empty((M, N), dtype=out_dtype, device=dev)
     _check("X_gathered", [X_gathered], (M, K), device=dev)
     _check("Y", [Y], (M, N), OUT_DTYPES, dev)
-    h = _handle(handle, dev)
+    h = _handle(handle, dev, stream)
     check(load().tpf_allgather_matmul(h.ptr, p, M, N, K, ptr_array([x.data_ptr() for x in X_slices]), W.data_ptr(),
                                       X_gathered.data_ptr(), Y.data_ptr(), _dtype_code(Y.dtype), n_chunks,
                                       _sched(sched), None, 0, _stream_ptr(stream)))
@@ -357,10 +381,11 @@ def matmul_dx(dY: List[torch.Tensor], W: List[torch.Tensor], semantic: int = ALL
     dev = _check("dY", dY, (M, Ns))
     _check("W", W, (Kin, Ns), device=dev)
     if dX is None:
-        if semantic == ALLREDUCE:
-            dX = torch.empty((M, Kin), dtype=out_dtype, device=dev)
-        else:
-            dX = [torch.empty((M // p, Kin), dtype=out_dtype, device=dev) for _ in range(p)]
+        with _on(stream):
+            if semantic == ALLREDUCE:
+                dX = torch.empty((M, Kin), dtype=out_dtype, device=dev)
+            else:
+                dX = [torch.empty((M // p, Kin), dtype=out_dtype, device=dev) for _ in range(p)]
     outs = [dX] if semantic == ALLREDUCE else list(dX)
     if semantic == ALLREDUCE:
         _check("dX", outs, (M, Kin), OUT_DTYPES, dev)
@@ -369,8 +394,8 @@ def matmul_dx(dY: List[torch.Tensor], W: List[torch.Tensor], semantic: int = ALL
         _check("dX", outs, (M // p, Kin), OUT_DTYPES, dev)
         _need(len({o.dtype for o in outs}) == 1, "dX: the slices differ in dtype")
     _check_ws(ws, dev)
-    h = _handle(handle, dev)
-    ws, ws_bytes = _ws(OP_MATMUL_DX, p, M, Kin, Ns, n_chunks, sched, ws, dev, message)
+    h = _handle(handle, dev, stream)
+    ws, ws_bytes = _ws(OP_MATMUL_DX, p, M, Kin, Ns, n_chunks, sched, ws, dev, message, stream)
     check(load().tpf_matmul_dx(h.ptr, semantic, p, M, Kin, Ns, ptr_array([d.data_ptr() for d in dY]),
                                ptr_array([w.data_ptr() for w in W]), ptr_array([o.data_ptr() for o in outs]),
                                _dtype_code(outs[0].dtype), n_chunks, _sched(sched, message),
@@ -392,11 +417,12 @@ def weight_grad(A: List[torch.Tensor], B: List[torch.Tensor], out_dtype=torch.fl
     dev = _check("A", A, (M, R))
     _check("B", B, (M, C), device=dev)
     if dW is None:
-        dW = [torch.empty((R, C), dtype=out_dtype, device=dev) for _ in range(p)]
+        with _on(stream):
+            dW = [torch.empty((R, C), dtype=out_dtype, device=dev) for _ in range(p)]
     _check_shards("dW", dW, p)
     _check("dW", dW, (R, C), OUT_DTYPES, dev)
     _need(len({d.dtype for d in dW}) == 1, "dW: the shards differ in dtype")
-    h = _handle(handle, dev)
+    h = _handle(handle, dev, stream)
     check(load().tpf_weight_grad(h.ptr, p, M, R, C, ptr_array([a.data_ptr() for a in A]),
                                  ptr_array([b.data_ptr() for b in B]), ptr_array([d.data_ptr() for d in dW]),
                                  _dtype_code(dW[0].dtype), _stream_ptr(stream)))
@@ -414,11 +440,12 @@ def rowpar_dx(dY: torch.Tensor, W: List[torch.Tensor], out_dtype=torch.bfloat16,
     dev = _check("dY", [dY], (M, N))
     _check("W", W, (Ks, N), device=dev)
     if dX is None:
-        dX = [torch.empty((M, Ks), dtype=out_dtype, device=dev) for _ in range(p)]
+        with _on(stream):
+            dX = [torch.empty((M, Ks), dtype=out_dtype, device=dev) for _ in range(p)]
     _check_shards("dX", dX, p)
     _check("dX", dX, (M, Ks), OUT_DTYPES, dev)
     _need(len({d.dtype for d in dX}) == 1, "dX: the shards differ in dtype")
-    h = _handle(handle, dev)
+    h = _handle(handle, dev, stream)
     check(load().tpf_rowpar_dx(h.ptr, p, M, Ks, N, dY.data_ptr(), ptr_array([w.data_ptr() for w in W]),
                                ptr_array([d.data_ptr() for d in dX]), _dtype_code(dX[0].dtype),
                                _stream_ptr(stream)))
@@ -442,12 +469,13 @@ def mlp_sp(X_slices: List[torch.Tensor], W1: List[torch.Tensor], W2: List[torch.
     dev = _check("X_slices", X_slices, (Sp, Hd))
     _check("W1", W1, (Hd, F), device=dev)
     _check("W2", W2, (F, Hd), device=dev)
-    if X_gathered is None:
-        X_gathered = torch.empty((S, Hd), dtype=torch.bfloat16, device=dev)
-    if H is None:
-        H = [torch.empty((S, F), dtype=torch.bfloat16, device=dev) for _ in range(p)]
-    if Y is None:
-        Y = [torch.empty((Sp, Hd), dtype=out_dtype, device=dev) for _ in range(p)]
+    with _on(stream):
+        if X_gathered is None:
+            X_gathered = torch.empty((S, Hd), dtype=torch.bfloat16, device=dev)
+        if H is None:
+            H = [torch.empty((S, F), dtype=torch.bfloat16, device=dev) for _ in range(p)]
+        if Y is None:
+            Y = [torch.empty((Sp, Hd), dtype=out_dtype, device=dev) for _ in range(p)]
     _check("X_gathered", [X_gathered], (S, Hd), device=dev)
     _check_shards("H", H, p)
     _check("H", H, (S, F), device=dev)
@@ -455,8 +483,8 @@ def mlp_sp(X_slices: List[torch.Tensor], W1: List[torch.Tensor], W2: List[torch.
     _check("Y", Y, (Sp, Hd), OUT_DTYPES, dev)
     _need(len({y.dtype for y in Y}) == 1, "Y: the slices differ in dtype")
     _check_ws(ws, dev)
-    h = _handle(handle, dev)
-    ws, ws_bytes = _ws(OP_MLP_SP, p, S, Hd, F, n_chunks, sched, ws, dev, message)
+    h = _handle(handle, dev, stream)
+    ws, ws_bytes = _ws(OP_MLP_SP, p, S, Hd, F, n_chunks, sched, ws, dev, message, stream)
     check(load().tpf_mlp_sp(h.ptr, p, S, Hd, F, ptr_array([x.data_ptr() for x in X_slices]),
                             ptr_array([w.data_ptr() for w in W1]), ptr_array([w.data_ptr() for w in W2]),
                             X_gathered.data_ptr(), ptr_array([t.data_ptr() for t in H]),

@@ -77,3 +77,51 @@ def test_device_tensor_checks():
     for call, msg in cases:
         with pytest.raises(ValueError, match=msg):
             call()
+
+
+def test_default_handles_are_per_stream(monkeypatch):
+    """A handle runs one call at a time, so the binding keeps one default
+    handle per (device, stream): calls on two streams never share the work
+    queue or readiness counters of one handle.  Host-only (fake handles)."""
+    created = []
+
+    class FakeHandle:
+        def __init__(self, dev):
+            created.append(dev)
+            self.device = dev
+
+    class FakeStream:
+        def __init__(self, ptr):
+            self.cuda_stream = ptr
+
+    monkeypatch.setattr(tp, "Handle", FakeHandle)
+    monkeypatch.setattr(tp, "_default_handles", {})
+    a = tp.default_handle(0, FakeStream(0x10))
+    b = tp.default_handle(0, FakeStream(0x20))
+    c = tp.default_handle(0, FakeStream(0x10))
+    d = tp.default_handle(1, FakeStream(0x10))
+    assert a is c and a is not b and d is not a
+    assert created == [0, 0, 1]
+
+
+@pytest.mark.gpu
+def test_side_stream_call_allocates_on_its_stream():
+    """A call on a side stream with binding-allocated workspace and output
+    gives the same bits as the same call on the current stream (the buffers
+    belong to the side stream's allocator pool, and the call uses that
+    stream's own default handle)."""
+    p, M, N, K = 4, 512, 512, 256
+    g = torch.Generator(device="cuda").manual_seed(5)
+    X = [torch.randn(M, K, device="cuda", generator=g).to(BF) for _ in range(p)]
+    W = [(torch.randn(K, N, device="cuda", generator=g) * 0.02).to(BF) for _ in range(p)]
+    ref = tp.matmul_allreduce(X, W, n_chunks=4, sched="persistent")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for sched in ("persistent", "tile", "unfused", "fold"):
+        outs.append(tp.matmul_allreduce(X, W, n_chunks=4, sched=sched, stream=side))
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert tp.default_handle(0, side) is not tp.default_handle(0)
+    for y in outs:
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
