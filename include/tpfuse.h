@@ -88,15 +88,15 @@ extern "C" {
 /* Schedulers.  Every scheduler computes the same bits. */
 #define TPF_SCHED_AUTO 0         /* library's choice.  With every shard on one GPU the reduction shares HBM
                                     and L2 with the GEMM, and overlapping it chunk by chunk costs more
-                                    than it hides; folding it into the last shard's GEMM epilogue does
-                                    pay when the last shard's tiles fill whole waves of the GPU.  AUTO
-                                    runs TPF_SCHED_FOLD for the reducing calls (MatMul->AllReduce,
-                                    MatMul->ReduceScatter, dX, the MLP block's FC2) on the large tiles
-                                    (M > 64) when the p-1 shards' tiles and the last shard's tiles take
-                                    no more waves of one-tile-per-CU workgroups than all p shards'
-                                    tiles together, and TPF_SCHED_UNFUSED otherwise (and for
-                                    decode-shaped M and AllGather->MatMul); tpf_debug_last_sched
-                                    reports the choice.  Every scheduler gives the same bits. */
+                                    than it hides.  AUTO runs TPF_SCHED_STATIONARY for decode-shaped
+                                    row counts (M <= 64) of the row-parallel calls (MatMul->AllReduce,
+                                    MatMul->ReduceScatter, the MLP block's FC2); TPF_SCHED_FOLD for the
+                                    reducing calls (those, and dX) on the large tiles (M > 64) when the
+                                    p-1 shards' tiles and the last shard's tiles take no more waves of
+                                    one-tile-per-CU workgroups than all p shards' tiles together; and
+                                    TPF_SCHED_UNFUSED otherwise (and for AllGather->MatMul);
+                                    tpf_debug_last_sched reports the choice.  Every scheduler gives the
+                                    same bits. */
 #define TPF_SCHED_PERSISTENT 1   /* one persistent kernel: work queue + per-chunk ready counters */
 #define TPF_SCHED_TWO_STREAM 2   /* per-chunk GEMM launches (alternating between the caller's stream and a
                                     second handle stream), reductions on a side stream after per-chunk
@@ -125,6 +125,16 @@ extern "C" {
                                     is its epilogue.  n_chunks is checked but does not change the
                                     schedule.  For M <= 64 (one shard's tiles could not fill the GPU)
                                     and for AllGather->MatMul it runs as TPF_SCHED_UNFUSED. */
+#define TPF_SCHED_STATIONARY 8   /* one launch, output-stationary: each workgroup owns an output tile of
+                                    32 (M <= 32) or 64 rows and 32 columns, computes every shard's fp32
+                                    partial of it (each the same MFMA chain as the partials the other
+                                    schedulers store), and folds them on chip in shard order, rounding
+                                    once: no partial goes to memory, no workspace, no second launch.
+                                    Built for decode-shaped M, where the weights dominate the traffic and
+                                    the tile's small height costs nothing; correct for any M.  For dX
+                                    (weights used transposed) and AllGather->MatMul it runs as
+                                    TPF_SCHED_UNFUSED.  n_chunks is checked but does not change the
+                                    schedule. */
 
 /* Message precision, OR-ed into the `sched` argument of the reducing calls
  * (tpf_matmul_allreduce, tpf_matmul_reducescatter, tpf_matmul_dx, and
@@ -169,9 +179,12 @@ int tpf_destroy(tpf_handle h);
 /* Bytes of workspace a call needs (0 if none), a pure function of its
  * arguments.  For the reducing operations it is p * M * N * 4 (p * M * N * 2
  * with TPF_MSG_BF16 in `sched`): one local output [M, N] per shard (N = output
- * width: N for the row-parallel ops, K_in for tpf_matmul_dx).  `K` is the
- * per-shard reduction length.  AllGather->MatMul needs none.  Returns 0 for
- * invalid arguments. */
+ * width: N for the row-parallel ops, K_in for tpf_matmul_dx), except that
+ * TPF_SCHED_STATIONARY needs none for the row-parallel calls and the MLP
+ * block (it still needs the full size for tpf_matmul_dx, which it runs
+ * unfused).  AUTO asks for the full size, which covers every scheduler it may
+ * pick.  `K` is the per-shard reduction length.  AllGather->MatMul needs
+ * none.  Returns 0 for invalid arguments. */
 size_t tpf_workspace_size(int op, int p, int64_t M, int64_t N, int64_t K, int n_chunks, int sched);
 
 /* MatMul -> AllReduce (row-parallel Linear, M027 page §01-§03; cnblogs §2.4).

@@ -17,7 +17,7 @@ LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libtpfuse.so")
 
 SOURCES = ["tpf_kernels.hip", "tpf_api.cpp"]
-HEADERS = ["tpf_device.hpp", "tpf_internal.hpp"]
+HEADERS = ["tpf_device.hpp", "tpf_internal.hpp", "tpf_gemm.hpp", "tpf_stationary.hpp"]
 
 # Packed-fp32 instructions are disabled for all device code: the compiler
 # would otherwise form v_pk_* fp32 ops from plain float code.
@@ -38,7 +38,7 @@ def hipcc() -> str:
 
 # tpf_kernels.hip is compiled as KERNEL_PARTS translation units (-DTPF_PART=n),
 # in parallel; see the part list at the top of that file.
-KERNEL_PARTS = 7
+KERNEL_PARTS = 8
 
 
 def _compile_jobs(cc: str):

@@ -15,6 +15,7 @@
 
 #include "../../include/tpfuse.h"
 #include "tpf_internal.hpp"
+#include "tpf_stationary.hpp"
 
 using namespace tpf;
 
@@ -81,7 +82,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // A scheduler id in the low byte, optionally OR-ed with TPF_MSG_BF16.
 bool valid_sched(int s) {
   const int base = s & 0xff, flags = s & ~0xff;
-  return base >= TPF_SCHED_AUTO && base <= TPF_SCHED_FOLD && (flags & ~TPF_MSG_BF16) == 0;
+  return base >= TPF_SCHED_AUTO && base <= TPF_SCHED_STATIONARY && (flags & ~TPF_MSG_BF16) == 0;
 }
 bool msg_bf16(int s) { return (s & TPF_MSG_BF16) != 0; }
 bool valid_dtype(int d) { return d == TPF_BF16 || d == TPF_F32; }
@@ -130,8 +131,12 @@ int check_ptr(const void* ptr, const char* name) {
 }
 
 // Workspace of the reducing ops: one local output ("message") per shard,
-// fp32 or (TPF_MSG_BF16) bf16.
-size_t partial_bytes(int p, int64_t M, int64_t N, int sched) {
+// fp32 or (TPF_MSG_BF16) bf16.  The output-stationary scheduler keeps the
+// partials on chip and needs none for weights stored [K][N] (the
+// row-parallel calls); with weights used transposed (dX) it runs as
+// TPF_SCHED_UNFUSED and needs the full workspace.
+size_t partial_bytes(int p, int64_t M, int64_t N, int sched, bool weights_kn = false) {
+  if ((sched & 0xff) == TPF_SCHED_STATIONARY && weights_kn) return 0;
   return (size_t)p * (size_t)M * (size_t)N * (msg_bf16(sched) ? 2 : 4);
 }
 
@@ -178,8 +183,12 @@ int resolve_sched(int sched, int n_chunks) {
   return sched & 0xff;   // AUTO stays AUTO here; each op resolves it below
 }
 
-int auto_reduce_sched(int cfg, int p, int64_t M, int64_t N, int num_cus) {
-  if (cfg != CFG_LARGE || num_cus <= 0) return TPF_SCHED_UNFUSED;
+int auto_reduce_sched(int cfg, int bl, int p, int64_t M, int64_t N, int num_cus) {
+  // Decode-shaped M with weights stored [K][N]: one launch that keeps every
+  // shard's partial of an output tile on chip (no workspace traffic, no
+  // second launch).
+  if (cfg != CFG_LARGE) return bl == B_KN ? TPF_SCHED_STATIONARY : TPF_SCHED_UNFUSED;
+  if (num_cus <= 0) return TPF_SCHED_UNFUSED;
   const int64_t T = ((M + cfg_bm(cfg) - 1) / cfg_bm(cfg)) * ((N + cfg_bn(cfg) - 1) / cfg_bn(cfg));
   auto waves = [num_cus](int64_t tiles) { return (tiles + num_cus - 1) / num_cus; };
   return waves((p - 1) * T) + waves(T) == waves(p * T) ? TPF_SCHED_FOLD : TPF_SCHED_UNFUSED;
@@ -277,8 +286,11 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
 
   // One shard's tiles of a small-M problem cannot fill the GPU: the fold
   // scheduler then runs as UNFUSED (the same bits either way).
-  int sched = rc.sched == TPF_SCHED_AUTO ? auto_reduce_sched(cfg, rc.p, rc.M, rc.N, h->num_cus) : rc.sched;
+  int sched = rc.sched == TPF_SCHED_AUTO ? auto_reduce_sched(cfg, rc.bl, rc.p, rc.M, rc.N, h->num_cus) : rc.sched;
   if (sched == TPF_SCHED_FOLD && cfg != CFG_LARGE) sched = TPF_SCHED_UNFUSED;
+  // The single launch streams weights stored [K][N]; dX's transposed weights
+  // run GEMM-then-reduce (the same bits).
+  if (sched == TPF_SCHED_STATIONARY && rc.bl != B_KN) sched = TPF_SCHED_UNFUSED;
   h->last_sched = sched;
   switch (sched) {
     case TPF_SCHED_GEMM_ONLY:
@@ -317,6 +329,23 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
     case TPF_SCHED_FOLD:
       TPF_TIMED(h, stream, launch_fold(cfg, rc.bl, g, rc.ro, rc.P, stride, rc.p, rc.M, rc.N, stream));
       return TPF_OK;
+    case TPF_SCHED_STATIONARY: {
+      StationaryArgs a{};
+      for (int k = 0; k < rc.p; ++k) {
+        a.A[k] = g.A[k];
+        a.B[k] = g.B[k];
+      }
+      a.M = rc.M;
+      a.N = rc.N;
+      a.K = rc.K;
+      a.p = rc.p;
+      const int bm = rc.M <= 32 ? 32 : 64;
+      a.tiles_m = (rc.M + bm - 1) / bm;
+      a.tiles_n = (rc.N + kStBN - 1) / kStBN;
+      a.ro = rc.ro;
+      TPF_TIMED(h, stream, launch_stationary(a, rc.ro.pbf16, rc.ro.dtype, stream));
+      return TPF_OK;
+    }
     case TPF_SCHED_TILE: {
       TileArgs a{};
       a.g = g;
@@ -491,9 +520,10 @@ size_t tpf_workspace_size(int op, int p, int64_t M, int64_t N, int64_t K, int n_
   switch (op) {
     case TPF_OP_MATMUL_ALLREDUCE:
     case TPF_OP_MATMUL_REDUCESCATTER:
-    case TPF_OP_MATMUL_DX:
     case TPF_OP_MLP_SP:          // FC2's partials: N = Hd
-      return partial_bytes(p, M, N, sched);
+      return partial_bytes(p, M, N, sched, true);
+    case TPF_OP_MATMUL_DX:
+      return partial_bytes(p, M, N, sched, false);
     case TPF_OP_ALLGATHER_MATMUL:
       return 0;
     default:
@@ -509,7 +539,7 @@ int tpf_matmul_allreduce(tpf_handle h, int p, int64_t M, int64_t N, int64_t K_sh
   if ((st = check_ptrs(X, p, "X"))) return st;
   if ((st = check_ptrs(W, p, "W"))) return st;
   if ((st = check_ptr(Y, "Y"))) return st;
-  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, M, N, sched)))) return st;
+  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, M, N, sched, true)))) return st;
   if ((st = check_handle(h))) return st;
   ReduceCall rc{};
   rc.p = p;
@@ -538,7 +568,7 @@ int tpf_matmul_reducescatter(tpf_handle h, int p, int64_t M, int64_t N, int64_t 
   if ((st = check_ptrs(X, p, "X"))) return st;
   if ((st = check_ptrs(W, p, "W"))) return st;
   if ((st = check_ptrs(Y_slices, p, "Y_slices"))) return st;
-  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, M, N, sched)))) return st;
+  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, M, N, sched, true)))) return st;
   if ((st = check_handle(h))) return st;
   ReduceCall rc{};
   rc.p = p;
@@ -627,7 +657,7 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
   ChunkGeom ch{n_chunks, Mi / n_chunks, Mi};
   int s = resolve_sched(sched, n_chunks);
   if (s == TPF_SCHED_TILE) s = TPF_SCHED_PERSISTENT;   // no reduction to fold into the tiles
-  if (s == TPF_SCHED_FOLD || s == TPF_SCHED_AUTO) s = TPF_SCHED_UNFUSED;
+  if (s == TPF_SCHED_FOLD || s == TPF_SCHED_STATIONARY || s == TPF_SCHED_AUTO) s = TPF_SCHED_UNFUSED;
   h->last_sched = s;
   switch (s) {
     case TPF_SCHED_GEMM_ONLY:
@@ -813,7 +843,7 @@ int tpf_mlp_sp(tpf_handle h, int p, int64_t S, int64_t Hd, int64_t F, const void
   if ((st = check_ptr(X_gathered, "X_gathered"))) return st;
   if ((st = check_ptrs(const_cast<const void* const*>(H), p, "H"))) return st;
   if ((st = check_ptrs(const_cast<const void* const*>(Y_slices), p, "Y_slices"))) return st;
-  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, S, Hd, sched)))) return st;
+  if ((st = check_ws(ws, ws_bytes, partial_bytes(p, S, Hd, sched, true)))) return st;
   if ((st = check_handle(h))) return st;
   if ((st = set_device(h))) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -209,5 +209,9 @@ hipError_t launch_copy(const char* src, char* dst, int64_t bytes, int num_cus, h
 // from src[r] to dst + r * slice_bytes, r = 0 .. p-1.
 hipError_t launch_gather(const void* const* src, int p, char* dst, int64_t slice_bytes, int num_cus, hipStream_t s);
 hipError_t launch_clear_status(Ctrl* c, hipStream_t s);
+// Output-stationary single launch of a reducing call with B stored [K][N]
+// (a.tiles_m x a.tiles_n workgroups; tiles of 32 rows when M <= 32, else 64).
+struct StationaryArgs;
+hipError_t launch_stationary(const StationaryArgs& a, int pbf16, int out, hipStream_t s);
 
 }  // namespace tpf

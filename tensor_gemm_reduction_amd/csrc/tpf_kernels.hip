@@ -24,14 +24,15 @@
 #include <algorithm>
 
 #include "tpf_internal.hpp"
+#include "tpf_stationary.hpp"
 
 // The launchers are split into parts so that the build can compile them as
-// separate translation units in parallel (-DTPF_PART=n, n = 0..6); without
+// separate translation units in parallel (-DTPF_PART=n, n = 0..7); without
 // TPF_PART every part is compiled.
 //   0: reductions, copies, status, dispatch      1: persistent kernel, large tiles
 //   2: large tiles (plain, tile scheduler)        3: fold epilogue, fp32 messages
 //   4: decode-shaped (small and mid) tiles        5: persistent kernel, small and mid tiles
-//   6: fold epilogue, bf16 messages
+//   6: fold epilogue, bf16 messages               7: output-stationary single launch
 #ifdef TPF_PART
 #define TPF_IN_PART(n) (TPF_PART == (n))
 #else
@@ -742,6 +743,49 @@ void launch_tiles_fold_bf16msg(int bl, int out, const TileArgs& a, int grid, hip
 void launch_tiles_small(int cfg, int bl, int red, const TileArgs& a, int grid, hipStream_t s) {
   if (cfg == CFG_SMALL) launch_tile_red<CfgSmall>(bl, red, a, grid, s);
   else launch_tile_red<CfgMid>(bl, red, a, grid, s);
+}
+#endif
+
+#ifndef TPF_ST_STAGES
+#define TPF_ST_STAGES 4
+#endif
+
+// The output-stationary single launch (tpf_stationary.hpp): one workgroup of
+// eight waves per output tile of 32 * RB rows and 32 columns.  The LDS holds
+// the eight waves' weight rings during the K loops and the p partials
+// (p * 32 * RB * 32 fp32, at most 128 KiB) for the fold after them.
+constexpr int kStLdsBytes = 128 * 1024;
+static_assert(kStWaves * TPF_ST_STAGES * kStStageBytes <= kStLdsBytes, "weight rings fit the LDS");
+static_assert(kMaxShards * 64 * kStBN * 4 <= kStLdsBytes, "the partials of every shard fit the LDS");
+
+template <int RB, int PB, int OUT>
+__global__ __launch_bounds__(kStWaves * 64) void stationary_kernel(StationaryArgs args) {
+  (void)args;
+  const StationaryArgs& a = kernarg<StationaryArgs>();
+  __shared__ __attribute__((aligned(1024))) char lds[kStLdsBytes];
+  stationary_tile<RB, TPF_ST_STAGES, PB, OUT>(a, lds, xcd_task(blockIdx.x, a.tiles_m * a.tiles_n));
+}
+
+#if TPF_IN_PART(7)
+template <int RB>
+static void launch_st_rb(const StationaryArgs& a, int pbf16, int out, int grid, hipStream_t s) {
+  const dim3 g(grid), b(kStWaves * 64);
+  if (pbf16) {
+    if (out == OUT_F32) hipLaunchKernelGGL((stationary_kernel<RB, 1, OUT_F32>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((stationary_kernel<RB, 1, OUT_BF16>), g, b, 0, s, a);
+  } else {
+    if (out == OUT_F32) hipLaunchKernelGGL((stationary_kernel<RB, 0, OUT_F32>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((stationary_kernel<RB, 0, OUT_BF16>), g, b, 0, s, a);
+  }
+}
+
+hipError_t launch_stationary(const StationaryArgs& a, int pbf16, int out, hipStream_t s) {
+  const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
+  if (grid <= 0) return hipSuccess;
+  if (grid > INT32_MAX || a.p < 1 || a.p > kMaxShards) return hipErrorInvalidValue;
+  if (a.tiles_m == 1 && a.M <= 32) launch_st_rb<1>(a, pbf16, out, (int)grid, s);
+  else launch_st_rb<2>(a, pbf16, out, (int)grid, s);
+  return hipGetLastError();
 }
 #endif
 

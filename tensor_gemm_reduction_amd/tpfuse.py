@@ -22,7 +22,7 @@ OK = 0
 ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGNMENT, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP, ERR_TIMEOUT = range(-1, -8, -1)
 BF16, F32 = 0, 1
 (SCHED_AUTO, SCHED_PERSISTENT, SCHED_TWO_STREAM, SCHED_UNFUSED, SCHED_GEMM_ONLY, SCHED_REDUCE_ONLY, SCHED_TILE,
- SCHED_FOLD) = range(8)
+ SCHED_FOLD, SCHED_STATIONARY) = range(9)
 ALLREDUCE, REDUCESCATTER = 0, 1
 OP_MATMUL_ALLREDUCE, OP_MATMUL_REDUCESCATTER, OP_ALLGATHER_MATMUL, OP_MATMUL_DX, OP_MLP_SP = range(5)
 MAX_SHARDS = 16
@@ -30,7 +30,7 @@ MAX_CHUNKS = 64
 
 SCHEDS = {"auto": SCHED_AUTO, "persistent": SCHED_PERSISTENT, "two_stream": SCHED_TWO_STREAM,
           "unfused": SCHED_UNFUSED, "gemm_only": SCHED_GEMM_ONLY, "reduce_only": SCHED_REDUCE_ONLY,
-          "tile": SCHED_TILE, "fold": SCHED_FOLD}
+          "tile": SCHED_TILE, "fold": SCHED_FOLD, "stationary": SCHED_STATIONARY}
 
 _VP = ctypes.c_void_p
 _PP = ctypes.POINTER(ctypes.c_void_p)

@@ -43,6 +43,7 @@ def test_constants_match_header():
     assert int(defs["TPF_SCHED_REDUCE_ONLY"]) == tp.SCHED_REDUCE_ONLY
     assert int(defs["TPF_SCHED_TILE"]) == tp.SCHED_TILE
     assert int(defs["TPF_SCHED_FOLD"]) == tp.SCHED_FOLD
+    assert int(defs["TPF_SCHED_STATIONARY"]) == tp.SCHED_STATIONARY
     assert int(defs["TPF_REDUCESCATTER"]) == tp.REDUCESCATTER
     assert int(defs["TPF_OP_MATMUL_DX"]) == tp.OP_MATMUL_DX
     assert int(defs["TPF_MAX_SHARDS"]) == tp.MAX_SHARDS and int(defs["TPF_MAX_CHUNKS"]) == tp.MAX_CHUNKS
@@ -73,7 +74,14 @@ def test_workspace_size():
     assert ws(tp.OP_MATMUL_DX, 8, 2048, 12288, 6144, 8, "unfused", "bf16") == 8 * 2048 * 12288 * 2
     assert ws(tp.OP_ALLGATHER_MATMUL, 8, 2048, 6144, 12288, 8, message="bf16") == 0
     assert ws(tp.OP_MATMUL_ALLREDUCE, 4, 64, 64, 64, 1, tp.SCHED_TILE | 0x200) == 0   # unknown flag
-    assert ws(tp.OP_MATMUL_ALLREDUCE, 4, 64, 64, 64, 1, tp.SCHED_FOLD + 1) == 0      # unknown scheduler
+    assert ws(tp.OP_MATMUL_ALLREDUCE, 4, 64, 64, 64, 1, tp.SCHED_STATIONARY + 1) == 0  # unknown scheduler
+    # the output-stationary single launch keeps the partials on chip (row-parallel
+    # calls and the MLP block); dX runs unfused under it and needs the full size
+    assert ws(tp.OP_MATMUL_ALLREDUCE, 8, 16, 8192, 1024, 1, "stationary") == 0
+    assert ws(tp.OP_MATMUL_REDUCESCATTER, 8, 64, 8192, 1024, 2, "stationary", "bf16") == 0
+    assert ws(tp.OP_MLP_SP, 8, 64, 8192, 1024, 1, "stationary") == 0
+    assert ws(tp.OP_MATMUL_DX, 8, 64, 1024, 512, 1, "stationary") == 8 * 64 * 1024 * 4
+    assert ws(tp.OP_MATMUL_ALLREDUCE, 8, 16, 8192, 1024, 1, "auto") == 8 * 16 * 8192 * 4
     assert ws(tp.OP_MATMUL_ALLREDUCE, 4, 64, 64, 64, 1, "fold") == 4 * 64 * 64 * 4
 
 

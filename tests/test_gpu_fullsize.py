@@ -78,7 +78,7 @@ def test_fullsize_parity(name):
     del ref
     # every other chunk count and scheduler gives the same bits
     for m in wl.chunks:
-        for sched in ("persistent", "two_stream", "unfused", "tile", "fold"):
+        for sched in ("persistent", "two_stream", "unfused", "tile", "fold", "stationary"):
             if m == n and sched == "persistent" and n == 1:
                 continue
             y = run(wl, inp, torch.bfloat16, m, sched)
@@ -159,7 +159,7 @@ def test_fullsize_mlp_sp():
     assert_bf16(torch.cat(Y, 0), ref, f"mlp_sp all {S} rows")
     assert_bf16_is_rne_of_f32(torch.cat(Y, 0), torch.cat(Y32, 0), "mlp_sp")
     del ref
-    for sched in ("persistent", "two_stream", "tile", "fold"):
+    for sched in ("persistent", "two_stream", "tile", "fold", "stationary"):
         _, _, Ys = tp.mlp_sp(inp.X, W1, W2, torch.bfloat16, n_chunks=wl.default_chunks, sched=sched)
         torch.cuda.synchronize()
         assert_bitwise(torch.cat(Ys, 0), torch.cat(Y, 0), f"mlp_sp {sched}")

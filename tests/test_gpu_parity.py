@@ -16,7 +16,7 @@ from tests.parity import (assert_bf16, assert_bf16_is_rne_of_f32, assert_bitwise
 
 pytestmark = pytest.mark.gpu
 
-SCHEDS = ["persistent", "two_stream", "unfused", "tile", "fold", "auto"]
+SCHEDS = ["persistent", "two_stream", "unfused", "tile", "fold", "stationary", "auto"]
 DEV = "cuda"
 
 
@@ -145,7 +145,9 @@ def test_auto_scheduler_choice():
         expect = "fold" if waves((p - 1) * t) + waves(t) == waves(p * t) else "unfused"
         assert ran(p, M, N, 64) == expect, (p, M, N)
     assert ran(2, 128, 2048, 64) == "unfused"          # 8 tiles per shard: one wave either way
-    assert ran(4, 64, 4096, 64) == "unfused"           # decode-shaped rows: small tiles
+    assert ran(4, 64, 4096, 64) == "stationary"        # decode-shaped rows: the single launch
+    assert ran(8, 16, 8192, 1024) == "stationary"
+    assert ran(4, 64, 256, 64, op="dx") == "unfused"   # decode-shaped dX: weights used transposed
     assert ran(2, 512, 512, 64, op="dx") == "unfused"  # dX [512, 64]: 2 tiles per shard
     t = tiles(4096, 4096)                               # dX [4096, 4096] with p = 4
     expect = "fold" if waves(3 * t) + waves(t) == waves(4 * t) else "unfused"
@@ -216,7 +218,7 @@ def test_repeated_persistent_calls_are_deterministic():
     assert tp.default_handle().sync_status() == tp.OK
 
 
-@pytest.mark.parametrize("sched", ["auto", "persistent", "tile", "fold"])
+@pytest.mark.parametrize("sched", ["auto", "persistent", "tile", "fold", "stationary"])
 def test_graph_capture_replays_match_eager(sched):
     """The calls enqueue only kernels (no memset, no allocation) and leave every
     counter at zero, so a captured call replays correctly: several replays, with
@@ -304,10 +306,10 @@ def test_kernel_timing_records_one_launch_per_call():
     W = gpu(shards([(K, N)] * p, ("normal", 0.05), 72))
     h = tp.Handle(0)
     h.set_kernel_timing(True)
-    for sched in ("auto", "unfused", "gemm_only", "persistent", "tile", "fold", "two_stream"):
+    for sched in ("auto", "unfused", "gemm_only", "persistent", "tile", "fold", "stationary", "two_stream"):
         tp.matmul_allreduce(X, W, n_chunks=4, sched=sched, handle=h)
     t = h.kernel_times()
-    assert len(t) == 6 and all(0.0 < v < 1000.0 for v in t), t    # two_stream records nothing
+    assert len(t) == 7 and all(0.0 < v < 1000.0 for v in t), t    # two_stream records nothing
     assert h.kernel_times() == []                                    # cleared
     h.set_kernel_timing(False)
     tp.matmul_allreduce(X, W, sched="unfused", handle=h)

@@ -18,7 +18,7 @@ from tests.parity import assert_bf16, assert_bitwise, assert_f32
 
 pytestmark = pytest.mark.gpu
 
-SCHEDS = ["auto", "unfused", "fold", "persistent", "two_stream", "tile"]
+SCHEDS = ["auto", "unfused", "fold", "persistent", "two_stream", "tile", "stationary"]
 DEV = "cuda"
 
 
