@@ -12,9 +12,9 @@
  * persistent kernel with per-chunk ready counters, two HIP streams with
  * per-chunk events, or readiness per output tile), the unfused
  * GEMM-then-reduce baseline, a fold of the reduction into the last shard's
- * GEMM epilogue, and a single-launch path for decode-shaped row counts that
- * keeps every shard's partial of an output tile on chip.  The default (AUTO)
- * picks among the unchunked ones by shape (see TPF_SCHED_AUTO).  The sum over
+ * GEMM epilogue, and a single launch that keeps every shard's partial of an
+ * output tile on chip.  The default (AUTO) picks between the fold and the
+ * unfused baseline by shape (see TPF_SCHED_AUTO).  The sum over
  * shards is a left fold in shard order k = 0..p-1 in fp32, rounded once to
  * the output type, so results are bit-identical for every chunk count and
  * every scheduler.
@@ -88,15 +88,15 @@ extern "C" {
 /* Schedulers.  Every scheduler computes the same bits. */
 #define TPF_SCHED_AUTO 0         /* library's choice.  With every shard on one GPU the reduction shares HBM
                                     and L2 with the GEMM, and overlapping it chunk by chunk costs more
-                                    than it hides.  AUTO runs TPF_SCHED_STATIONARY for decode-shaped
-                                    row counts (M <= 64) of the row-parallel calls (MatMul->AllReduce,
-                                    MatMul->ReduceScatter, the MLP block's FC2); TPF_SCHED_FOLD for the
-                                    reducing calls (those, and dX) on the large tiles (M > 64) when the
-                                    p-1 shards' tiles and the last shard's tiles take no more waves of
-                                    one-tile-per-CU workgroups than all p shards' tiles together; and
-                                    TPF_SCHED_UNFUSED otherwise (and for AllGather->MatMul);
-                                    tpf_debug_last_sched reports the choice.  Every scheduler gives the
-                                    same bits. */
+                                    than it hides; folding it into the last shard's GEMM epilogue does
+                                    pay when the last shard's tiles fill whole waves of the GPU.  AUTO
+                                    runs TPF_SCHED_FOLD for the reducing calls (MatMul->AllReduce,
+                                    MatMul->ReduceScatter, dX, the MLP block's FC2) on the large tiles
+                                    (M > 64) when the p-1 shards' tiles and the last shard's tiles take
+                                    no more waves of one-tile-per-CU workgroups than all p shards'
+                                    tiles together, and TPF_SCHED_UNFUSED otherwise (and for
+                                    decode-shaped M and AllGather->MatMul); tpf_debug_last_sched
+                                    reports the choice.  Every scheduler gives the same bits. */
 #define TPF_SCHED_PERSISTENT 1   /* one persistent kernel: work queue + per-chunk ready counters */
 #define TPF_SCHED_TWO_STREAM 2   /* per-chunk GEMM launches (alternating between the caller's stream and a
                                     second handle stream), reductions on a side stream after per-chunk
@@ -131,7 +131,9 @@ extern "C" {
                                     schedulers store), and folds them on chip in shard order, rounding
                                     once: no partial goes to memory, no workspace, no second launch.
                                     Built for decode-shaped M, where the weights dominate the traffic and
-                                    the tile's small height costs nothing; correct for any M.  For dX
+                                    the tile's small height costs nothing; correct for any M, but slower
+                                    than TPF_SCHED_UNFUSED on the measured shapes (so AUTO does not
+                                    pick it).  For dX
                                     (weights used transposed) and AllGather->MatMul it runs as
                                     TPF_SCHED_UNFUSED.  n_chunks is checked but does not change the
                                     schedule. */

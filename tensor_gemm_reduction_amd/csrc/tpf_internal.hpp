@@ -210,7 +210,7 @@ hipError_t launch_copy(const char* src, char* dst, int64_t bytes, int num_cus, h
 hipError_t launch_gather(const void* const* src, int p, char* dst, int64_t slice_bytes, int num_cus, hipStream_t s);
 hipError_t launch_clear_status(Ctrl* c, hipStream_t s);
 // Output-stationary single launch of a reducing call with B stored [K][N]
-// (a.tiles_m x a.tiles_n workgroups; tiles of 32 rows when M <= 32, else 64).
+// (the launcher sets the tile grid from the tile shape it picks for M and p).
 struct StationaryArgs;
 hipError_t launch_stationary(const StationaryArgs& a, int pbf16, int out, hipStream_t s);
 

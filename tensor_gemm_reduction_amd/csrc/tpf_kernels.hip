@@ -746,46 +746,61 @@ void launch_tiles_small(int cfg, int bl, int red, const TileArgs& a, int grid, h
 }
 #endif
 
-#ifndef TPF_ST_STAGES
-#define TPF_ST_STAGES 4
-#endif
-
 // The output-stationary single launch (tpf_stationary.hpp): one workgroup of
-// eight waves per output tile of 32 * RB rows and 32 columns.  The LDS holds
-// the eight waves' weight rings during the K loops and the p partials
-// (p * 32 * RB * 32 fp32, at most 128 KiB) for the fold after them.
-constexpr int kStLdsBytes = 128 * 1024;
-static_assert(kStWaves * TPF_ST_STAGES * kStStageBytes <= kStLdsBytes, "weight rings fit the LDS");
-static_assert(kMaxShards * 64 * kStBN * 4 <= kStLdsBytes, "the partials of every shard fit the LDS");
+// eight waves per output tile of 32 columns and 32 (M <= 32) or 64 rows.  The
+// LDS holds the eight waves' weight rings during the K loops and the p
+// partials of the tile (at most 16 x 64 x 32 fp32 = 128 KiB) for the fold
+// after them.  Measured on the decode shapes (p = 8, K = 1024, N = 8192):
+// 2, 3 and 4 ring slots within 3 %; 64-column tiles (half the workgroups,
+// 128-byte weight rows) 8-15 % slower; tiles dealt round-robin over the XCDs
+// instead of in contiguous shares 17 % slower.
+#ifndef TPF_ST_SMALL
+#define TPF_ST_SMALL StCfg<1, 1, 64, 2>
+#endif
+#ifndef TPF_ST_MID
+#define TPF_ST_MID StCfg<2, 1, 64, 2>
+#endif
+using StSmall = TPF_ST_SMALL;
+using StMid = TPF_ST_MID;
+using StSmallAnyP = StCfg<1, 1, 64, 2>;
+using StMidAnyP = StCfg<2, 1, 64, 2>;
+static_assert(st_max_shards<StSmallAnyP>() >= kMaxShards && st_max_shards<StMidAnyP>() >= kMaxShards,
+              "the fallback shapes hold every shard's partials");
 
-template <int RB, int PB, int OUT>
+template <class C, int PB, int OUT>
 __global__ __launch_bounds__(kStWaves * 64) void stationary_kernel(StationaryArgs args) {
   (void)args;
   const StationaryArgs& a = kernarg<StationaryArgs>();
   __shared__ __attribute__((aligned(1024))) char lds[kStLdsBytes];
-  stationary_tile<RB, TPF_ST_STAGES, PB, OUT>(a, lds, xcd_task(blockIdx.x, a.tiles_m * a.tiles_n));
+  stationary_tile<C, PB, OUT>(a, lds, xcd_task(blockIdx.x, a.tiles_m * a.tiles_n));
 }
 
 #if TPF_IN_PART(7)
-template <int RB>
-static void launch_st_rb(const StationaryArgs& a, int pbf16, int out, int grid, hipStream_t s) {
-  const dim3 g(grid), b(kStWaves * 64);
+template <class C>
+static hipError_t launch_st_cfg(StationaryArgs a, int pbf16, int out, hipStream_t s) {
+  a.tiles_m = (a.M + C::BM - 1) / C::BM;
+  a.tiles_n = (a.N + C::BN - 1) / C::BN;
+  const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
+  if (grid <= 0) return hipSuccess;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 g((unsigned)grid), b(kStWaves * 64);
   if (pbf16) {
-    if (out == OUT_F32) hipLaunchKernelGGL((stationary_kernel<RB, 1, OUT_F32>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((stationary_kernel<RB, 1, OUT_BF16>), g, b, 0, s, a);
+    if (out == OUT_F32) hipLaunchKernelGGL((stationary_kernel<C, 1, OUT_F32>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((stationary_kernel<C, 1, OUT_BF16>), g, b, 0, s, a);
   } else {
-    if (out == OUT_F32) hipLaunchKernelGGL((stationary_kernel<RB, 0, OUT_F32>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((stationary_kernel<RB, 0, OUT_BF16>), g, b, 0, s, a);
+    if (out == OUT_F32) hipLaunchKernelGGL((stationary_kernel<C, 0, OUT_F32>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((stationary_kernel<C, 0, OUT_BF16>), g, b, 0, s, a);
   }
+  return hipGetLastError();
 }
 
 hipError_t launch_stationary(const StationaryArgs& a, int pbf16, int out, hipStream_t s) {
-  const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
-  if (grid <= 0) return hipSuccess;
-  if (grid > INT32_MAX || a.p < 1 || a.p > kMaxShards) return hipErrorInvalidValue;
-  if (a.tiles_m == 1 && a.M <= 32) launch_st_rb<1>(a, pbf16, out, (int)grid, s);
-  else launch_st_rb<2>(a, pbf16, out, (int)grid, s);
-  return hipGetLastError();
+  if (a.p < 1 || a.p > kMaxShards || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
+  if (a.M <= 32)
+    return a.p <= st_max_shards<StSmall>() ? launch_st_cfg<StSmall>(a, pbf16, out, s)
+                                           : launch_st_cfg<StSmallAnyP>(a, pbf16, out, s);
+  return a.p <= st_max_shards<StMid>() ? launch_st_cfg<StMid>(a, pbf16, out, s)
+                                       : launch_st_cfg<StMidAnyP>(a, pbf16, out, s);
 }
 #endif
 

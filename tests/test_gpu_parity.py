@@ -145,9 +145,9 @@ def test_auto_scheduler_choice():
         expect = "fold" if waves((p - 1) * t) + waves(t) == waves(p * t) else "unfused"
         assert ran(p, M, N, 64) == expect, (p, M, N)
     assert ran(2, 128, 2048, 64) == "unfused"          # 8 tiles per shard: one wave either way
-    assert ran(4, 64, 4096, 64) == "stationary"        # decode-shaped rows: the single launch
-    assert ran(8, 16, 8192, 1024) == "stationary"
-    assert ran(4, 64, 256, 64, op="dx") == "unfused"   # decode-shaped dX: weights used transposed
+    assert ran(4, 64, 4096, 64) == "unfused"           # decode-shaped rows: GEMM-then-reduce
+    assert ran(8, 16, 8192, 1024) == "unfused"
+    assert ran(4, 64, 256, 64, op="dx") == "unfused"
     assert ran(2, 512, 512, 64, op="dx") == "unfused"  # dX [512, 64]: 2 tiles per shard
     t = tiles(4096, 4096)                               # dX [4096, 4096] with p = 4
     expect = "fold" if waves(3 * t) + waves(t) == waves(4 * t) else "unfused"
