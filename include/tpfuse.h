@@ -200,6 +200,27 @@ int tpf_matmul_allreduce(tpf_handle h, int p, int64_t M, int64_t N, int64_t K_sh
                          const void* const* X, const void* const* W, void* Y, int y_dtype,
                          int n_chunks, int sched, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the static workspace behind tpf_matmul_allreduce_noalloc (64 MiB
+ * per device). */
+#define TPF_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* MatMul -> AllReduce that allocates nothing, for callers that cannot call
+ * hipMalloc: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same operands, result, schedulers and errors as
+ * tpf_matmul_allreduce, without the workspace arguments: the shard partials
+ * go to a library-owned static device array of TPF_NOALLOC_SCRATCH_BYTES per
+ * device (each GPU the library runs on holds it until the process ends; its
+ * address is looked up when the first handle on that device is created).
+ * A call whose scheduler needs more than that (tpf_workspace_size of the same
+ * arguments) fails with TPF_ERR_UNSUPPORTED before anything is enqueued.  The
+ * call makes no allocation of any kind.  Every call on one device shares that
+ * device's array, which keeps the last call's partials: calls that overlap on
+ * one device (other streams, other handles, other threads) race and must be
+ * serialised by the caller. */
+int tpf_matmul_allreduce_noalloc(tpf_handle h, int p, int64_t M, int64_t N, int64_t K_shard,
+                                 const void* const* X, const void* const* W, void* Y, int y_dtype,
+                                 int n_chunks, int sched, void* stream);
+
 /* MatMul -> ReduceScatter (M027 page §01; cnblogs §2.7).
  *   Same operands as tpf_matmul_allreduce; M % p == 0.
  *   Y_slices[r] ([M/p, N], y_dtype), r = 0..p-1, receives rows

@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -23,6 +24,21 @@ static_assert(TPF_MAX_SHARDS == kMaxShards, "shard limit mismatch");
 static_assert(TPF_MAX_CHUNKS == kMaxChunks, "chunk limit mismatch");
 
 constexpr int kKernelTimes = 256;   // debug kernel-timing records held per handle
+
+// Partial workspace of tpf_matmul_allreduce_noalloc: a file-scope device
+// array, one copy per GPU the library runs on, held until the process ends.
+// Host code never uses the array's name as an address (in host code it is a
+// host-side stand-in); it uses the device address that hipGetSymbolAddress
+// returns for the current device, fetched once per device when a handle is
+// created on it (noalloc_scratch()).
+static_assert(TPF_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) char scratch[TPF_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
 
 // The two-stream scheduler's chunk reductions run on a grid capped at a
 // quarter of the usual size (2 workgroups per CU): they then trickle beside
@@ -52,6 +68,7 @@ struct tpf_context {
   int kt_next = 0;      // ring slot of the next record
   int kt_count = 0;     // records held (<= kKernelTimes)
   int last_sched = -1;  // scheduler the last call ran (AUTO resolved), -1 before any
+  void* scratch = nullptr;  // this device's copy of the no-allocation workspace
 };
 
 namespace {
@@ -462,6 +479,18 @@ int tpf_create(tpf_handle* out, int device) {
   e = hipGetDeviceProperties(&prop, device);
   if (e != hipSuccess) return cleanup(hip_fail(e, "hipGetDeviceProperties"));
   h->num_cus = prop.multiProcessorCount;
+  // The no-allocation entry point's workspace: this device's copy of the
+  // static array, looked up once per device with the device current.
+  if (device < kMaxDevices) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+      void* ptr = nullptr;
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return cleanup(hip_fail(e, "hipGetSymbolAddress(scratch)"));
+      g_scratch_ptr[device] = ptr;
+    }
+    h->scratch = g_scratch_ptr[device];
+  }
   e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->gemm2, hipStreamNonBlocking);
   if (e != hipSuccess) return cleanup(hip_fail(e, "hipStreamCreateWithFlags"));
@@ -556,6 +585,38 @@ int tpf_matmul_allreduce(tpf_handle h, int p, int64_t M, int64_t N, int64_t K_sh
   rc.sched = resolve_sched(sched, n_chunks);
   rc.ro.pbf16 = msg_bf16(sched) ? 1 : 0;
   rc.P = ws;
+  return run_reduce_call(h, rc, reinterpret_cast<hipStream_t>(stream));
+}
+
+int tpf_matmul_allreduce_noalloc(tpf_handle h, int p, int64_t M, int64_t N, int64_t K_shard, const void* const* X,
+                                 const void* const* W, void* Y, int y_dtype, int n_chunks, int sched, void* stream) {
+  int st = check_common(p, M, N, K_shard, n_chunks, y_dtype, sched, false);
+  if (st) return st;
+  if ((st = check_ptrs(X, p, "X"))) return st;
+  if ((st = check_ptrs(W, p, "W"))) return st;
+  if ((st = check_ptr(Y, "Y"))) return st;
+  const size_t need = partial_bytes(p, M, N, sched, true);
+  if (need > (size_t)TPF_NOALLOC_SCRATCH_BYTES)
+    return fail(TPF_ERR_UNSUPPORTED, "the partials need " + std::to_string(need) + " bytes; the no-allocation entry "
+                                     "point holds at most " + std::to_string((size_t)TPF_NOALLOC_SCRATCH_BYTES));
+  if ((st = check_handle(h))) return st;
+  if (!h->scratch) return fail(TPF_ERR_UNSUPPORTED, "no static workspace on this device");
+  ReduceCall rc{};
+  rc.p = p;
+  rc.M = (int)M;
+  rc.N = (int)N;
+  rc.K = (int)K_shard;
+  rc.bl = B_KN;
+  rc.A = X;
+  rc.B = W;
+  rc.ro.y[0] = Y;
+  rc.ro.scatter = 0;
+  rc.ro.rows_per_slice = (int)M;
+  rc.ro.dtype = out_kind(y_dtype);
+  rc.n_chunks = n_chunks;
+  rc.sched = resolve_sched(sched, n_chunks);
+  rc.ro.pbf16 = msg_bf16(sched) ? 1 : 0;
+  rc.P = h->scratch;
   return run_reduce_call(h, rc, reinterpret_cast<hipStream_t>(stream));
 }
 

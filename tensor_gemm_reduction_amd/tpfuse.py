@@ -27,6 +27,7 @@ ALLREDUCE, REDUCESCATTER = 0, 1
 OP_MATMUL_ALLREDUCE, OP_MATMUL_REDUCESCATTER, OP_ALLGATHER_MATMUL, OP_MATMUL_DX, OP_MLP_SP = range(5)
 MAX_SHARDS = 16
 MAX_CHUNKS = 64
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 SCHEDS = {"auto": SCHED_AUTO, "persistent": SCHED_PERSISTENT, "two_stream": SCHED_TWO_STREAM,
           "unfused": SCHED_UNFUSED, "gemm_only": SCHED_GEMM_ONLY, "reduce_only": SCHED_REDUCE_ONLY,
@@ -44,6 +45,7 @@ SIGNATURES = {
     "tpf_destroy": (_I, [_VP]),
     "tpf_workspace_size": (_SZ, [_I, _I, _I64, _I64, _I64, _I, _I]),
     "tpf_matmul_allreduce": (_I, [_VP, _I, _I64, _I64, _I64, _PP, _PP, _VP, _I, _I, _I, _VP, _SZ, _VP]),
+    "tpf_matmul_allreduce_noalloc": (_I, [_VP, _I, _I64, _I64, _I64, _PP, _PP, _VP, _I, _I, _I, _VP]),
     "tpf_matmul_reducescatter": (_I, [_VP, _I, _I64, _I64, _I64, _PP, _PP, _PP, _I, _I, _I, _VP, _SZ, _VP]),
     "tpf_allgather_matmul": (_I, [_VP, _I, _I64, _I64, _I64, _PP, _VP, _VP, _VP, _I, _I, _I, _VP, _SZ, _VP]),
     "tpf_matmul_dx": (_I, [_VP, _I, _I, _I64, _I64, _I64, _PP, _PP, _PP, _I, _I, _I, _VP, _SZ, _VP]),
@@ -314,6 +316,28 @@ def matmul_allreduce(X: List[torch.Tensor], W: List[torch.Tensor], out_dtype=tor
                                       ptr_array([w.data_ptr() for w in W]), Y.data_ptr(), _dtype_code(Y.dtype),
                                       n_chunks, _sched(sched, message), ws.data_ptr() if ws is not None else None, ws_bytes,
                                       _stream_ptr(stream)))
+    return Y
+
+
+def matmul_allreduce_noalloc(X: List[torch.Tensor], W: List[torch.Tensor], Y: torch.Tensor, n_chunks: int = 1,
+                             sched="auto", handle: Optional[Handle] = None, stream=None,
+                             message: str = "fp32") -> torch.Tensor:
+    """Y = sum_k X[k] @ W[k] into the caller's Y with no allocation anywhere:
+    the library keeps the partials in its static per-device workspace
+    (NOALLOC_SCRATCH_BYTES); calls that overlap on one device race."""
+    p = len(X)
+    _need(p >= 1, "X: no shards given")
+    M, K = X[0].shape
+    N = W[0].shape[1]
+    _check_shards("W", W, p)
+    dev = _check("X", X, (M, K))
+    _check("W", W, (K, N), device=dev)
+    _check("Y", [Y], (M, N), OUT_DTYPES, dev)
+    h = _handle(handle, dev, stream)
+    check(load().tpf_matmul_allreduce_noalloc(h.ptr, p, M, N, K, ptr_array([x.data_ptr() for x in X]),
+                                              ptr_array([w.data_ptr() for w in W]), Y.data_ptr(),
+                                              _dtype_code(Y.dtype), n_chunks, _sched(sched, message),
+                                              _stream_ptr(stream)))
     return Y
 
 

@@ -229,3 +229,29 @@ def test_handle_calls_reject_null():
     assert lib.tpf_debug_last_sched(None) == tp.ERR_INVALID_ARG
     assert lib.tpf_create(None, 0) == tp.ERR_INVALID_ARG
     assert lib.tpf_destroy(None) == tp.OK
+
+
+def test_noalloc_entry_point_checks_on_host():
+    """The no-allocation MatMul->AllReduce refuses, before touching a device,
+    a request whose partials exceed its static workspace, and otherwise
+    reaches the (NULL) handle check; it takes no workspace arguments."""
+    lib = tp.load()
+    X = tp.ptr_array([A16] * 4)
+    W = tp.ptr_array([A16] * 4)
+    # 4 x 4096 x 4096 fp32 partials = 256 MiB > 64 MiB
+    st = lib.tpf_matmul_allreduce_noalloc(None, 4, 4096, 4096, 4096, X, W, A16, tp.BF16, 1, tp.SCHED_AUTO, None)
+    assert st == tp.ERR_UNSUPPORTED
+    assert "64" in lib.tpf_last_error().decode() or "67108864" in lib.tpf_last_error().decode()
+    # 2-byte messages halve the need: 4 x 1024 x 4096 x 2 = 32 MiB fits, so the
+    # next check (the NULL handle) is the one that fails
+    st = lib.tpf_matmul_allreduce_noalloc(None, 4, 1024, 4096, 4096, X, W, A16, tp.BF16, 1,
+                                          tp.SCHED_AUTO | tp.MSG_BF16, None)
+    assert st == tp.ERR_INVALID_ARG and "handle" in lib.tpf_last_error().decode()
+    # the stationary scheduler needs no workspace at all
+    st = lib.tpf_matmul_allreduce_noalloc(None, 4, 4096, 4096, 4096, X, W, A16, tp.BF16, 1, tp.SCHED_STATIONARY, None)
+    assert st == tp.ERR_INVALID_ARG
+    # ordinary argument checks still apply
+    assert lib.tpf_matmul_allreduce_noalloc(None, 4, 64, 60, 64, X, W, A16, tp.BF16, 1, 0, None) == tp.ERR_ALIGNMENT
+    assert lib.tpf_matmul_allreduce_noalloc(None, 4, 64, 64, 64, X, W, MIS, tp.BF16, 1, 0, None) == tp.ERR_ALIGNMENT
+    text = open(HEADER).read()
+    assert "#define TPF_NOALLOC_SCRATCH_BYTES (64u << 20)" in text and tp.NOALLOC_SCRATCH_BYTES == 64 << 20
