@@ -98,9 +98,13 @@ extern "C" {
                                     decode-shaped M and AllGather->MatMul); tpf_debug_last_sched
                                     reports the choice.  Every scheduler gives the same bits. */
 #define TPF_SCHED_PERSISTENT 1   /* one persistent kernel: work queue + per-chunk ready counters */
-#define TPF_SCHED_TWO_STREAM 2   /* per-chunk GEMM launches (alternating between the caller's stream and a
-                                    second handle stream), reductions on a side stream after per-chunk
-                                    events */
+#define TPF_SCHED_TWO_STREAM 2   /* per-chunk launches alternating between the caller's stream and a second
+                                    handle stream, so that chunk c's reduction runs beside chunk c+1's
+                                    GEMM: for the large tiles (M > 64) each chunk runs as TPF_SCHED_FOLD
+                                    over its rows (the first p-1 shards' tiles, then the last shard's
+                                    tiles with the chunk's reduction folded into their epilogue); for
+                                    decode-shaped M each chunk's GEMM is followed, on a side stream after a
+                                    per-chunk event, by that chunk's reduction kernel */
 #define TPF_SCHED_UNFUSED 3      /* whole GEMM, then the whole reduction (the serial baseline) */
 #define TPF_SCHED_GEMM_ONLY 4    /* measurement: only the shard GEMMs (partials into the workspace; for
                                     AllGather->MatMul: only the GEMM over an already gathered X) */
@@ -309,6 +313,21 @@ int tpf_sync_status(tpf_handle h, void* stream);
  * never reached, so each wait ends by its bound: used to test the timeout
  * path without any kernel hanging. */
 int tpf_debug_set_wait(tpf_handle h, int64_t spins, int unreachable);
+
+/* Debug: perturb the timing of the producers that the readiness protocols
+ * wait for, to stress them (the M027 page §04 asks for the ready events to be
+ * checked).  With period > 0 (and sleeps > 0), every later call on this handle
+ * makes each producer task whose index i satisfies mix(seed, i) % period == 0
+ * (a fixed integer hash) sleep sleeps x 64 x 127 clock cycles (bounded; about
+ * 4 us per unit at 2 GHz) before it stores or publishes its results: the GEMM
+ * tiles of the persistent kernel (before they bump a chunk's ready counter),
+ * its AllGather copy tasks (before they bump a slice's landed counter), the
+ * tile scheduler's tiles (before they bump an output tile's counter) and the
+ * plain shard-GEMM tiles (before they store their partials; the two-stream
+ * and fold schedulers' producers).  Results must not change.  period = 0
+ * turns it off.  Returns TPF_ERR_INVALID_ARG for period < 0 or sleeps outside
+ * [0, 1024]. */
+int tpf_debug_set_delay(tpf_handle h, uint32_t seed, int period, int sleeps);
 
 /* Debug: record the persistent kernel's task timeline.  `events` is a
  * caller-owned device buffer of `max_events` 32-byte records

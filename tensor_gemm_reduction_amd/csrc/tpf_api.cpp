@@ -69,6 +69,7 @@ struct tpf_context {
   int kt_count = 0;     // records held (<= kKernelTimes)
   int last_sched = -1;  // scheduler the last call ran (AUTO resolved), -1 before any
   void* scratch = nullptr;  // this device's copy of the no-allocation workspace
+  DelayArgs delay{};        // debug: timing perturbation of the producers (tpf_debug_set_delay)
 };
 
 namespace {
@@ -252,14 +253,15 @@ int ktime_stop(tpf_handle h, hipStream_t s) {
     if (st_) return st_;             \
   } while (0)
 
-// The fold scheduler's two launches: shards 0..p-2 into their partials, then
-// shard p-1, whose epilogue adds those partials and its own accumulator.
+// The fold scheduler's two launches over output rows [row0, row1): shards
+// 0..p-2 into their partials, then shard p-1, whose epilogue adds those
+// partials and its own accumulator.
 static hipError_t launch_fold(int cfg, int bl, const GemmOperands& g, const ReduceOut& ro, void* P, int64_t stride,
-                       int p, int M, int N, hipStream_t s) {
+                              int p, int row0, int row1, int N, hipStream_t s) {
   if (p > 1) {
     GemmOperands g0 = g;
     g0.nshard = p - 1;
-    const hipError_t e = launch_gemm_rows(cfg, bl, g0, 0, M, s);
+    const hipError_t e = launch_gemm_rows(cfg, bl, g0, row0, row1, s);
     if (e != hipSuccess) return e;
   }
   TileArgs a{};
@@ -271,9 +273,9 @@ static hipError_t launch_fold(int cfg, int bl, const GemmOperands& g, const Redu
   a.P = P;
   a.p_stride = stride;
   a.p = p;
-  a.row0 = 0;
-  a.row1 = M;
-  a.tiles_m = (M + cfg_bm(cfg) - 1) / cfg_bm(cfg);
+  a.row0 = row0;
+  a.row1 = row1;
+  a.tiles_m = (row1 - row0 + cfg_bm(cfg) - 1) / cfg_bm(cfg);
   a.tiles_n = (N + cfg_bn(cfg) - 1) / cfg_bn(cfg);
   a.tasks = a.tiles_m * a.tiles_n;
   return launch_tiles(cfg, bl, 2 + (ro.dtype == OUT_F32 ? 1 : 0) + 2 * ro.pbf16, a, s);
@@ -300,6 +302,7 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
   g.K = rc.K;
   g.b_rows = rc.bl == B_KN ? rc.K : rc.N;
   g.nshard = rc.p;
+  g.delay = h->delay;
   ChunkGeom ch{rc.n_chunks, rc.M / rc.n_chunks, rc.M};
   const int64_t stride = (int64_t)rc.M * rc.N;
 
@@ -323,11 +326,28 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
       TPF_HIP(launch_reduce_rows(rc.P, stride, rc.p, 0, rc.M, rc.N, rc.ro, h->num_cus, stream));
       return TPF_OK;
     case TPF_SCHED_TWO_STREAM: {
-      // Chunk c's GEMM goes to the caller's stream (even c) or the handle's
-      // second GEMM stream (odd c), so the next chunk's tiles fill CUs while
-      // the current chunk's last tiles finish; chunk c's reduction runs on
-      // the side stream after chunk c's event, concurrently with the GEMMs of
-      // later chunks.
+      if (cfg == CFG_LARGE) {
+        // Large tiles: chunk c runs as the fold scheduler over its rows -- the
+        // first p-1 shards' tiles into their partials, then the last shard's
+        // tiles, whose epilogue folds the chunk's reduction -- on the
+        // caller's stream (even c) or the handle's second GEMM stream (odd c).
+        // Chunk c's reduction (the partial reads of its fold epilogue) thus
+        // runs beside chunk c+1's GEMM tiles instead of after all of them.
+        TPF_HIP(hipEventRecord(h->ev_fork, stream));
+        TPF_HIP(hipStreamWaitEvent(h->gemm2, h->ev_fork, 0));
+        for (int c = 0; c < ch.n; ++c) {
+          hipStream_t gs = (c & 1) ? h->gemm2 : stream;
+          TPF_HIP(launch_fold(cfg, rc.bl, g, rc.ro, rc.P, stride, rc.p, ch.row0(c), ch.row1(c), rc.N, gs));
+        }
+        TPF_HIP(hipEventRecord(h->ev_join2, h->gemm2));
+        TPF_HIP(hipStreamWaitEvent(stream, h->ev_join2, 0));
+        return TPF_OK;
+      }
+      // Decode-shaped tiles: chunk c's GEMM goes to the caller's stream (even
+      // c) or the handle's second GEMM stream (odd c), so the next chunk's
+      // tiles fill CUs while the current chunk's last tiles finish; chunk c's
+      // reduction runs on the side stream after chunk c's event, concurrently
+      // with the GEMMs of later chunks.
       TPF_HIP(hipEventRecord(h->ev_fork, stream));
       TPF_HIP(hipStreamWaitEvent(h->side, h->ev_fork, 0));
       TPF_HIP(hipStreamWaitEvent(h->gemm2, h->ev_fork, 0));
@@ -346,7 +366,7 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
       return TPF_OK;
     }
     case TPF_SCHED_FOLD:
-      TPF_TIMED(h, stream, launch_fold(cfg, rc.bl, g, rc.ro, rc.P, stride, rc.p, rc.M, rc.N, stream));
+      TPF_TIMED(h, stream, launch_fold(cfg, rc.bl, g, rc.ro, rc.P, stride, rc.p, 0, rc.M, rc.N, stream));
       return TPF_OK;
     case TPF_SCHED_STATIONARY: {
       StationaryArgs a{};
@@ -711,6 +731,7 @@ int tpf_allgather_matmul(tpf_handle h, int p, int64_t M, int64_t N_shard, int64_
   g.K = Ki;
   g.b_rows = Ki;
   g.nshard = 1;
+  g.delay = h->delay;
   const int slice_rows = Mi / p;
   const int64_t slice_bytes = (int64_t)slice_rows * Ki * 2;
   char* xg = reinterpret_cast<char*>(X_gathered);
@@ -1014,6 +1035,17 @@ int tpf_debug_last_sched(tpf_handle h) {
   int st = check_handle(h);
   if (st) return st;
   return h->last_sched;
+}
+
+int tpf_debug_set_delay(tpf_handle h, uint32_t seed, int period, int sleeps) {
+  if (period < 0 || sleeps < 0 || sleeps > 1024)
+    return fail(TPF_ERR_INVALID_ARG, "period must be >= 0 and sleeps in [0, 1024]");
+  int st = check_handle(h);
+  if (st) return st;
+  h->delay.seed = seed;
+  h->delay.period = sleeps > 0 ? period : 0;
+  h->delay.sleeps = sleeps;
+  return TPF_OK;
 }
 
 int tpf_debug_set_wait(tpf_handle h, int64_t spins, int unreachable) {

@@ -33,6 +33,16 @@ constexpr int kTileCounters = 1 << 17;
 
 enum TaskKind : int { TK_GEMM = 0, TK_REDUCE = 1, TK_COPY = 2 };
 
+// Debug timing perturbation (tpf_debug_set_delay): a producer task with
+// index i for which mix(seed, i) % period == 0 sleeps sleeps x 64 x 127 clocks
+// (s_sleep 127, bounded) before it publishes or stores its results.
+// period == 0 turns it off.
+struct DelayArgs {
+  uint32_t seed;
+  int period;
+  int sleeps;
+};
+
 // The shard GEMMs of one call.  Tile (shard k, rows, cols) reads A[k] and
 // B[k] and writes dst + k * dst_shard_stride.
 struct GemmOperands {
@@ -49,6 +59,7 @@ struct GemmOperands {
   int M, N, K;                // rows, output width, reduction length per shard
   int b_rows;                 // rows of each B operand (K for KN weights, N for NK)
   int nshard;                 // shard GEMMs (p, or 1 for AllGather->MatMul)
+  DelayArgs delay;            // debug: timing perturbation of the producers
 };
 
 // Sources of a one-launch AllGather (read in place from the kernarg segment).

@@ -193,6 +193,21 @@ __device__ __forceinline__ int claim_tile(Ctrl* ctl, int c, int G, int x) {
   return -1;   // unreachable: G claims are made for G tiles
 }
 
+// Debug timing perturbation: task `task` of a launch sleeps a bounded time
+// before it stores or publishes its results when the seeded hash selects it
+// (the same decision for every thread of the workgroup).
+__device__ __forceinline__ void debug_delay(const DelayArgs& d, uint32_t task) {
+  if (d.period <= 0) return;
+  uint32_t x = d.seed ^ (task * 0x9E3779B9u);
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  if (x % (uint32_t)d.period != 0) return;
+  for (int i = 0; i < d.sleeps; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
 // Thread 0 polls *ctr with relaxed loads (no cache maintenance per poll),
 // backing off exponentially so that many waiting workgroups do not hammer one
 // memory channel, until it reaches target or the bound runs out; then one
@@ -284,6 +299,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void fused_kernel(FusedArgs args) {
       Frag<Cfg> f;
       gemm_tile<Cfg, BL>(f, j);
       store_any<Cfg>(f, j, a.g, shard);
+      debug_delay(a.g.delay, (uint32_t)t);
       if (!a.gather) {
         publish(&ctl->ready[c]);
         if (a.piggyback && c > 0) {
@@ -313,6 +329,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void fused_kernel(FusedArgs args) {
       const int64_t b0 = (int64_t)u * a.copy_seg_bytes;
       const int64_t b1 = min(b0 + a.copy_seg_bytes, a.slice_bytes);
       copy_range(a.src[r], a.gathered + (int64_t)r * a.slice_bytes, b0, b1, tid, Cfg::THREADS);
+      debug_delay(a.g.delay, (uint32_t)t);
       publish(&ctl->landed[r]);
     }
     if (a.timeline && tid == 0 && t < a.timeline_cap) {
@@ -519,6 +536,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void tile_kernel(TileArgs args) {
   Frag<Cfg> f;
   if constexpr (RED == 0) {
     gemm_tile<Cfg, BL>(f, j);
+    debug_delay(a.g.delay, (uint32_t)u);
     store_any<Cfg>(f, j, a.g, shard);
   } else if constexpr (RED >= 2) {
     gemm_tile<Cfg, BL>(f, j);
@@ -531,6 +549,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void tile_kernel(TileArgs args) {
     uint64_t t_mid = 0;
     gemm_tile<Cfg, BL>(f, j);
     store_any<Cfg>(f, j, a.g, shard);   // fp32 partial, or bf16 for the 2-byte message
+    debug_delay(a.g.delay, (uint32_t)u);
     const int T = tm * a.tiles_n + tn;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();

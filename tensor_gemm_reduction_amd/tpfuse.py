@@ -53,6 +53,7 @@ SIGNATURES = {
     "tpf_mlp_sp": (_I, [_VP, _I, _I64, _I64, _I64, _PP, _PP, _PP, _VP, _PP, _PP, _I, _I, _I, _VP, _SZ, _VP]),
     "tpf_sync_status": (_I, [_VP, _VP]),
     "tpf_debug_set_wait": (_I, [_VP, _I64, _I]),
+    "tpf_debug_set_delay": (_I, [_VP, ctypes.c_uint32, _I, _I]),
     "tpf_debug_set_timeline": (_I, [_VP, _VP, _I]),
     "tpf_debug_set_kernel_timing": (_I, [_VP, _I]),
     "tpf_debug_kernel_times": (_I, [_VP, ctypes.POINTER(ctypes.c_float), _I]),
@@ -165,6 +166,11 @@ class Handle:
 
     def debug_set_wait(self, spins: int, unreachable: bool) -> None:
         check(load().tpf_debug_set_wait(self._h, int(spins), 1 if unreachable else 0))
+
+    def set_delay(self, seed: int, period: int, sleeps: int) -> None:
+        """Perturb producer timing (a seeded subset of tasks sleeps before
+        publishing); period = 0 turns it off."""
+        check(load().tpf_debug_set_delay(self._h, int(seed) & 0xFFFFFFFF, int(period), int(sleeps)))
 
     def set_timeline(self, events: Optional[torch.Tensor]) -> None:
         """Record persistent-kernel task events into `events` (uint8 device tensor, 32 B per event)."""

@@ -255,3 +255,13 @@ def test_noalloc_entry_point_checks_on_host():
     assert lib.tpf_matmul_allreduce_noalloc(None, 4, 64, 64, 64, X, W, MIS, tp.BF16, 1, 0, None) == tp.ERR_ALIGNMENT
     text = open(HEADER).read()
     assert "#define TPF_NOALLOC_SCRATCH_BYTES (64u << 20)" in text and tp.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_debug_delay_argument_checks():
+    """The timing-perturbation knob checks its arguments before the handle."""
+    lib = tp.load()
+    assert lib.tpf_debug_set_delay(None, 1, -1, 1) == tp.ERR_INVALID_ARG
+    assert lib.tpf_debug_set_delay(None, 1, 2, 1025) == tp.ERR_INVALID_ARG
+    assert lib.tpf_debug_set_delay(None, 1, 2, -1) == tp.ERR_INVALID_ARG
+    assert lib.tpf_debug_set_delay(None, 1, 2, 4) == tp.ERR_INVALID_ARG      # valid arguments, NULL handle
+    assert "handle" in lib.tpf_last_error().decode()
