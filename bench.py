@@ -478,6 +478,11 @@ def summarize(wl, res, sched_req, n, msg_bytes, timed_label):
         t_m = modes.get("reduce_only", {"ms_median": 0.0})["ms_median"] / n
         rec["model_pipeline_ms"] = round(t_c + (n - 1) * max(t_c, t_m) + t_m, 4)
         rec["model_serial_ms"] = round(n * (t_c + t_m), 4)
+    chunked = {k: v["ms_median"] for k, v in modes.items() if k.startswith(("two_stream", "persistent"))}
+    if chunked and "unfused" in modes:
+        best = min(chunked, key=chunked.get)
+        rec["chunked_best"] = {"mode": best, "ms": round(chunked[best], 4),
+                               "over_unfused": round(chunked[best] / modes["unfused"]["ms_median"], 4)}
     goal = TARGET_HBM_FRAC if hbm_bound else TARGET_MFMA_FRAC
     rec["targets"] = {"roofline_frac_goal": goal, "roofline_frac_met": rec["roofline"]["frac"] >= goal,
                       "exposed_goal": TARGET_EXPOSED,
@@ -486,11 +491,21 @@ def summarize(wl, res, sched_req, n, msg_bytes, timed_label):
     return rec
 
 
+def chunk_sweep(wl, n):
+    """The chunked two-stream scheduler at 2, 4 and 8 chunks beside the
+    default count, for the large-M reducing workloads: where chunking pays."""
+    if wl.M <= 64 or wl.op not in ("allreduce", "reducescatter", "dx"):
+        return []
+    return [(f"two_stream_n{m}", "two_stream", m) for m in (2, 4, 8) if m != n and m <= wl.M]
+
+
 def default_modes(wl, n, requested, sched):
     """(label, scheduler, chunks) triples timed beside the headline."""
     specs = [(m, m, n) for m in requested if m]
     if sched not in [m for m, _, _ in specs]:
         specs.append((sched, sched, n))
+    if "two_stream" in requested:
+        specs += chunk_sweep(wl, n)
     return specs
 
 
@@ -510,6 +525,7 @@ def config_modes(wl, n):
     else:
         specs.append(("persistent", "persistent", n))
         specs.append(("two_stream", "two_stream", n))
+        specs += chunk_sweep(wl, n)
     return specs
 
 
@@ -622,7 +638,8 @@ def main(argv=None):
                   if "graph_ms_per_step" in res else None),
         "modes": head["modes"],
         **{k: head[k] for k in ("exposed_reduce_ms", "exposed_over_fused", "exposed_over_reduce_only",
-                                "fused_over_unfused", "model_pipeline_ms", "model_serial_ms") if k in head},
+                                "fused_over_unfused", "model_pipeline_ms", "model_serial_ms", "chunked_best")
+           if k in head},
         "configs": configs,
     }
     print(json.dumps(out), flush=True)

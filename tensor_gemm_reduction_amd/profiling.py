@@ -107,15 +107,34 @@ def _intersect(u, v):
     return total
 
 
+def kernel_kind(name: str) -> str:
+    """'reduce' for the reduction kernel, 'fold' for the shard-GEMM tiles
+    whose epilogue folds the reduction (tile_kernel's last template argument
+    2..5), 'gemm' for the other GEMM tiles."""
+    if "reduce" in name:
+        return "reduce"
+    if "tile_kernel" in name:
+        head = name.split("(")[0].rstrip(">").rstrip()
+        last = head.rsplit(",", 1)[-1].strip()
+        if last.isdigit() and int(last) >= 2:
+            return "fold"
+    return "gemm"
+
+
 def overlap(trace_path: str, per_step: int, out_path: str, command: str) -> dict:
-    """Summarise the last `per_step` dispatches of the library's kernels."""
+    """Summarise the last `per_step` dispatches of the library's kernels: how
+    long the reduction ran beside GEMM work.  The reduction is either the
+    reduction kernel or the fold-epilogue launches (which also compute the
+    last shard's GEMM tiles)."""
     rows = [r for r in _rows(trace_path, "kernel_trace.csv") if "tpf::" in r["Kernel_Name"]]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     step = rows[-per_step:]
     t0 = min(int(r["Start_Timestamp"]) for r in step)
     t1 = max(int(r["End_Timestamp"]) for r in step)
-    kind = lambda r: "reduce" if "reduce" in r["Kernel_Name"] else "gemm"
-    spans = {"gemm": [], "reduce": []}
+    kinds = {kernel_kind(r["Kernel_Name"]) for r in step}
+    red_kind = "reduce" if "reduce" in kinds else "fold"
+    kind = lambda r: kernel_kind(r["Kernel_Name"])  # noqa: E731
+    spans = {"gemm": [], "reduce": [], "fold": []}
     lines = [f"# rocprofv3 kernel trace: the last step's {per_step} dispatches (microseconds from the step's first start)",
              f"# command: {command}", "",
              f"{'#':>3s} {'kind':6s} {'queue':>5s} {'start_us':>9s} {'end_us':>9s} {'dur_us':>8s}"]
@@ -123,13 +142,14 @@ def overlap(trace_path: str, per_step: int, out_path: str, command: str) -> dict
         a, b = int(r["Start_Timestamp"]) - t0, int(r["End_Timestamp"]) - t0
         spans[kind(r)].append((a, b))
         lines.append(f"{i:3d} {kind(r):6s} {r.get('Queue_Id', '?'):>5s} {a / 1e3:9.2f} {b / 1e3:9.2f} {(b - a) / 1e3:8.2f}")
-    g, red = _union(spans["gemm"]), _union(spans["reduce"])
+    g, red = _union(spans["gemm"]), _union(spans[red_kind])
     res = {"step_us": (t1 - t0) / 1e3, "gemm_busy_us": _covered(g) / 1e3, "reduce_busy_us": _covered(red) / 1e3,
-           "both_us": _intersect(g, red) / 1e3}
+           "both_us": _intersect(g, red) / 1e3, "reduction_carrier": red_kind}
     res["reduce_hidden_frac"] = res["both_us"] / res["reduce_busy_us"] if res["reduce_busy_us"] else 0.0
-    lines += ["", f"step {res['step_us']:.2f} us; a GEMM kernel running {res['gemm_busy_us']:.2f} us; "
-                  f"a reduction kernel running {res['reduce_busy_us']:.2f} us, of which {res['both_us']:.2f} us "
-                  f"({100 * res['reduce_hidden_frac']:.0f} %) beside a GEMM kernel"]
+    what = "a reduction kernel" if red_kind == "reduce" else "a fold-epilogue launch (last shard's tiles + reduction)"
+    lines += ["", f"step {res['step_us']:.2f} us; a plain GEMM kernel running {res['gemm_busy_us']:.2f} us; "
+                  f"{what} running {res['reduce_busy_us']:.2f} us, of which {res['both_us']:.2f} us "
+                  f"({100 * res['reduce_hidden_frac']:.0f} %) beside a plain GEMM kernel"]
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     return res

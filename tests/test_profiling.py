@@ -128,3 +128,24 @@ def test_overlap_of_gemm_and_reduction(tmp_path):
     assert abs(res["reduce_busy_us"] - 0.075) < 1e-12
     assert abs(res["both_us"] - 0.035) < 1e-12        # 25 + 10 ns
     assert len(out.read_text().splitlines()) == 4 + 6 + 2
+
+
+def test_kernel_kind_names_fold_launches():
+    cfg = "tpf::TileCfg<256, 256, 2, 4, 2, 64, 0, 0, 0, 2>"
+    assert P.kernel_kind(f"void tpf::tile_kernel<{cfg}, 0, 0>(tpf::TileArgs)") == "gemm"
+    assert P.kernel_kind(f"void tpf::tile_kernel<{cfg}, 0, 1>(tpf::TileArgs)") == "gemm"      # tile scheduler
+    for red in (2, 3, 4, 5):
+        assert P.kernel_kind(f"void tpf::tile_kernel<{cfg}, 0, {red}>(tpf::TileArgs)") == "fold"
+    assert P.kernel_kind("tpf::reduce_rows_kernel(void const*, long, int)") == "reduce"
+    assert P.kernel_kind("void tpf::fused_kernel<A, 0>(tpf::FusedArgs)") == "gemm"
+
+
+def test_overlap_with_fold_launches_as_the_reduction(tmp_path):
+    """The chunked fold schedule: plain GEMM launches of chunk c+1 beside
+    the fold-epilogue launch of chunk c."""
+    g, f = "tpf::tile_kernel<A, 0, 0>(x)", "tpf::tile_kernel<A, 0, 2>(x)"
+    launches = [(g, 0, 100), (f, 100, 50), (g, 110, 100), (f, 210, 50)]
+    res = P.overlap(trace(tmp_path, launches), 4, str(tmp_path / "o.txt"), "test")
+    assert res["reduction_carrier"] == "fold"
+    assert abs(res["reduce_busy_us"] - 0.100) < 1e-12
+    assert abs(res["both_us"] - 0.040) < 1e-12         # fold 100-150 beside GEMM 110-210
