@@ -318,8 +318,9 @@ int tpf_debug_set_wait(tpf_handle h, int64_t spins, int unreachable);
  * wait for, to stress them (the M027 page §04 asks for the ready events to be
  * checked).  With period > 0 (and sleeps > 0), every later call on this handle
  * makes each producer task whose index i satisfies mix(seed, i) % period == 0
- * (a fixed integer hash) sleep sleeps x 64 x 127 clock cycles (bounded; about
- * 4 us per unit at 2 GHz) before it stores or publishes its results: the GEMM
+ * (a fixed integer hash) execute `sleeps` times the longest single sleep
+ * instruction (s_sleep 127; about 1 us each, measured) before it stores or
+ * publishes its results: the GEMM
  * tiles of the persistent kernel (before they bump a chunk's ready counter),
  * its AllGather copy tasks (before they bump a slice's landed counter), the
  * tile scheduler's tiles (before they bump an output tile's counter) and the

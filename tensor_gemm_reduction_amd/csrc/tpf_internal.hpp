@@ -34,8 +34,8 @@ constexpr int kTileCounters = 1 << 17;
 enum TaskKind : int { TK_GEMM = 0, TK_REDUCE = 1, TK_COPY = 2 };
 
 // Debug timing perturbation (tpf_debug_set_delay): a producer task with
-// index i for which mix(seed, i) % period == 0 sleeps sleeps x 64 x 127 clocks
-// (s_sleep 127, bounded) before it publishes or stores its results.
+// index i for which mix(seed, i) % period == 0 executes s_sleep 127 `sleeps`
+// times (bounded; about 1 us each) before it publishes or stores its results.
 // period == 0 turns it off.
 struct DelayArgs {
   uint32_t seed;

@@ -623,6 +623,11 @@ hipError_t launch_reduce_rows(const void* P, int64_t stride, int p, int row0, in
   const int64_t groups = (e1 - e0) / 4;
   if (groups <= 0) return hipSuccess;
   int64_t grid = (groups + 256 * 2 - 1) / (256 * 2);
+  // A small reduction (decode shapes: a few MB of partials) is bound by the
+  // latency of its loads, not by bandwidth: spread it over every CU, down to
+  // a quarter of a 256-thread block's groups per workgroup.
+  const int64_t spread = std::min<int64_t>((groups + 63) / 64, num_cus);
+  if (grid < spread) grid = spread;
   const int64_t cap = (int64_t)num_cus * 8;
   if (grid > cap) grid = cap;
   hipLaunchKernelGGL(reduce_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, P, stride, p, e0, e1, N, o);

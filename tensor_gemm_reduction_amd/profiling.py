@@ -29,20 +29,29 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments and whitespace: what the compiler sees."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return re.sub(r"\s+", "", text)
+
+
 def source_hash() -> str:
-    """sha256 over the device/host sources of libtpfuse (what the counters describe)."""
+    """sha256 over the code of libtpfuse's sources (what the counters
+    describe); comments and whitespace do not change it."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".hpp", ".cpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
                 h.update(name.encode())
-                h.update(f.read())
+                h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

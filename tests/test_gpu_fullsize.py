@@ -266,3 +266,36 @@ def test_timeline_shows_chunk_overlap():
             overlapped += 1
     assert overlapped == n - 1, f"{overlapped} of {n - 1} chunks overlapped"
     h.close()
+
+
+@pytest.mark.parametrize("name", REDUCING)
+def test_fullsize_against_plain_c_oracle(name):
+    """The plain C oracle (float64 loops, OpenMP over rows) on sampled rows of
+    every configuration at full size, against the timed launch configuration
+    (AUTO, default chunks): first and last rows, both sides of every chunk
+    boundary and seeded random rows, fp32 and bf16 outputs."""
+    from oracle import c_oracle
+    C = c_oracle.default()
+    wl = inputs.WORKLOADS[name]
+    n = wl.default_chunks
+    say(f"C oracle {name}: op={wl.op} p={wl.p} M={wl.M} N={wl.N} K={wl.K} n={n}")
+    inp = inputs.make_inputs(wl, seed=5, device="cuda")
+    y32 = run(wl, inp, torch.float32, n, "auto")
+    y16 = run(wl, inp, torch.bfloat16, n, "auto")
+    torch.cuda.synchronize()
+    rows = {0, 1, wl.M - 2, wl.M - 1}
+    for r0, r1 in O.chunk_bounds(wl.M, n):
+        rows.update({r0, max(0, r1 - 1)})
+    rows.update(int(r) for r in np.random.default_rng(17).integers(0, wl.M, 16))
+    rows = np.array(sorted(r for r in rows if 0 <= r < wl.M))
+    X, W = bits(inp.X), bits(inp.W)
+    if wl.op in ("allreduce", "reducescatter"):
+        ref = C.matmul_allreduce(X, W, rows=rows)
+    elif wl.op == "dx":
+        ref = C.matmul_dx(X, W, rows=rows)
+    else:
+        ref = C.allgather_matmul(X, W[0], rows=rows)[1]
+    idx = torch.as_tensor(rows, device="cuda")
+    what = f"{name} vs C oracle, {len(rows)} rows"
+    assert_f32(y32.index_select(0, idx), ref, what)
+    assert_bf16(y16.index_select(0, idx), ref, what)
