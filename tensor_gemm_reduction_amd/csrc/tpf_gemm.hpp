@@ -14,7 +14,9 @@
 //    K (or N) tails read as zeros.
 //  * K advances in steps of BK (32 or 64) through STAGES LDS buffers: the loads of step
 //    kt+STAGES-1 are issued right after the barrier of step kt, so they
-//    overlap STAGES-1 steps of MFMAs.  One barrier per step.
+//    overlap STAGES-1 steps of MFMAs.  One barrier per step.  With two
+//    stages and K a multiple of BK, each wave's loads are issued between the
+//    MFMAs of the slice that follows the barrier rather than in one burst.
 //  * A tiles are stored [m][BK k]; each lane of
 //    v_mfma_f32_32x32x16_bf16 reads its eight consecutive k with one
 //    ds_read_b128.  16-byte chunks are XOR-swizzled by row so that the 16
@@ -474,11 +476,70 @@ __device__ __forceinline__ void prefetch(const TileLoader<Cfg, BL>& ld, int nk) 
   }
 }
 
+// Steps 0 .. STAGES-2 into their stages, past the end repeating the last
+// step (the interleaved path, K a multiple of BK).
+template <class Cfg, int BL, int S>
+__device__ __forceinline__ void prefetch_all(const TileLoader<Cfg, BL>& ld, int nk) {
+  if constexpr (S < Cfg::STAGES - 1) {
+    ld.issue(stage_ptr<Cfg, S>(), (S < nk ? S : nk - 1) * Cfg::BK);
+    prefetch_all<Cfg, BL, S + 1>(ld, nk);
+  }
+}
+
 // Wait until this wave's loads of step `t` have landed, given that every
 // step up to min(t + STAGES - 2, nk - 1) has been issued.
 template <class Cfg>
 __device__ __forceinline__ void wait_step(int t, int nk) {
   wait_vmcnt(min(Cfg::STAGES - 2, nk - 1 - t) * Cfg::LOADS_PER_WAVE + Cfg::TOUCH_PER_WAVE);
+}
+
+// Loads interleaved with the MFMAs: large two-stage tiles without line
+// touches or the ping-pong schedule, when K is a multiple of BK.  (The
+// decode-sized tiles measured 2 % slower with it: one MFMA per slice leaves
+// nothing to interleave with.)
+#ifndef TPF_ILOAD
+#define TPF_ILOAD 1
+#endif
+template <class Cfg, int BL>
+__device__ __forceinline__ constexpr bool iload_ok() {
+  return TPF_ILOAD && Cfg::L2PF == 0 && !Cfg::PP && Cfg::BM >= 128;
+}
+
+// The last k slice's MFMAs of the current step, with the global -> LDS loads
+// of step kn into stage S issued between them.  After a K-step barrier all
+// waves of the workgroup would otherwise issue their loads at once; the
+// address unit's queue then fills, and a wave stalled on a load cannot issue
+// its MFMAs either (in-order issue), so the matrix core idles.  Interleaved,
+// the queue drains while the MFMAs run (measured 6-10 % faster on the large
+// forward shapes).  Only for K a multiple of BK (no tail step): the step's
+// offset goes into the scalar offset, as in TileLoader::issue.  Past the
+// last step (kn >= nk) the last step is loaded again into the free stage,
+// which nothing reads afterwards.
+template <class Cfg, int BL, int S>
+__device__ __forceinline__ void mfma_step_loads(Frag<Cfg>& f, const Operands<Cfg>& o, const TileLoader<Cfg, BL>& ld,
+                                                int kn, int nk) {
+  constexpr int NL = Cfg::A_PER_WAVE + Cfg::B_PER_WAVE;
+  constexpr int NM = Cfg::TM * Cfg::TN;
+  char* la = stage_ptr<Cfg, S>();
+  char* lb = la + Cfg::LDS_A;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int k0 = (kn < nk ? kn : nk - 1) * Cfg::BK;
+  const int ka = __builtin_amdgcn_readfirstlane(k0 * (int)(a_trans(BL) ? ld.lda_bytes : 2u));
+  const int kb = __builtin_amdgcn_readfirstlane(k0 * (int)(b_layout(BL) == B_NK ? 2u : ld.ldb_bytes));
+#pragma unroll
+  for (int q = 0; q < (NM > NL ? NM : NL); ++q) {
+    if (q < NM) {
+      const int i = q / Cfg::TN, jn = q % Cfg::TN;
+      f.acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[i], o.b[jn], f.acc[i][jn], 0, 0, 0);
+    }
+    if (q < Cfg::A_PER_WAVE)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ld.ra, (lds_void_t*)(la + (wv * Cfg::A_PER_WAVE + q) * 1024), 16,
+                                               (int)ld.a_off[q], ka, 0, 0);
+    else if (q < NL)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ld.rb, (lds_void_t*)(lb + (wv * Cfg::B_PER_WAVE + (q - Cfg::A_PER_WAVE)) * 1024), 16,
+          (int)ld.b_off[q - Cfg::A_PER_WAVE], kb, 0, 0);
+  }
 }
 
 // One K step on stage S, software-pipelined across steps.  On entry the
@@ -498,9 +559,6 @@ __device__ __forceinline__ void kstep(Frag<Cfg>& f, const TileLoader<Cfg, BL>& l
   for (int s = 0; s < SUB - 1; ++s) {
     read_operands<Cfg, BL>(o[(s + 1) & 1], cur, s + 1, wm, wn, lane);
     mfma_step<Cfg>(f, o[s & 1]);
-#ifdef TPF_IGLP
-    __builtin_amdgcn_iglp_opt(TPF_IGLP);
-#endif
   }
   if (kt + 1 < nk) {
     wait_step<Cfg>(kt + 1, nk);
@@ -511,13 +569,37 @@ __device__ __forceinline__ void kstep(Frag<Cfg>& f, const TileLoader<Cfg, BL>& l
   mfma_step<Cfg>(f, o[1]);
 }
 
+// The same K step without branches, for K a multiple of BK: the barrier is
+// passed at every step (the last one too), and the loads of step kt + STAGES
+// -- past the end, the last step again, into the stage every wave has
+// finished reading -- are issued one after each MFMA of the last k slice.
 template <class Cfg, int BL, int S>
+__device__ __forceinline__ void kstep_il(Frag<Cfg>& f, const TileLoader<Cfg, BL>& ld, Operands<Cfg> (&o)[2], int kt,
+                                         int nk, int wm, int wn, int lane) {
+  constexpr int SUB = Cfg::BK / 16;
+  static_assert(SUB % 2 == 0, "even number of k slices per step");
+  const char* cur = stage_ptr<Cfg, S>();
+#pragma unroll
+  for (int s = 0; s < SUB - 1; ++s) {
+    read_operands<Cfg, BL>(o[(s + 1) & 1], cur, s + 1, wm, wn, lane);
+    mfma_step<Cfg>(f, o[s & 1]);
+  }
+  // Every step issues exactly LOADS_PER_WAVE loads, so the loads of the
+  // STAGES - 2 steps after step kt + 1 may stay in flight.
+  wait_vmcnt((Cfg::STAGES - 2) * Cfg::LOADS_PER_WAVE);
+  __syncthreads();
+  read_operands<Cfg, BL>(o[0], stage_ptr<Cfg, (S + 1) % Cfg::STAGES>(), 0, wm, wn, lane);
+  mfma_step_loads<Cfg, BL, S>(f, o[1], ld, kt + Cfg::STAGES, nk);
+}
+
+template <class Cfg, int BL, int S, bool IL>
 __device__ __forceinline__ void ksteps(Frag<Cfg>& f, const TileLoader<Cfg, BL>& ld, Operands<Cfg> (&o)[2], int kt,
                                        int nk, int wm, int wn, int lane) {
   if constexpr (S < Cfg::STAGES) {
     if (kt + S < nk) {
-      kstep<Cfg, BL, S>(f, ld, o, kt + S, nk, wm, wn, lane);
-      ksteps<Cfg, BL, S + 1>(f, ld, o, kt, nk, wm, wn, lane);
+      if constexpr (IL) kstep_il<Cfg, BL, S>(f, ld, o, kt + S, nk, wm, wn, lane);
+      else kstep<Cfg, BL, S>(f, ld, o, kt + S, nk, wm, wn, lane);
+      ksteps<Cfg, BL, S + 1, IL>(f, ld, o, kt, nk, wm, wn, lane);
     }
   }
 }
@@ -629,14 +711,29 @@ __device__ __forceinline__ void gemm_tile(Frag<Cfg>& f, const TileJob& j) {
   ld.init(j);
   const int nk = (j.K + Cfg::BK - 1) / Cfg::BK;
   // Steps 0 .. STAGES-2 are loaded up front; step STAGES-1 is issued into
-  // the last stage right away (nothing has used it yet).
-  prefetch<Cfg, BL, 0>(ld, nk);
-  wait_step<Cfg>(0, nk);
-  __syncthreads();
-  if (Cfg::STAGES - 1 < nk) issue_stage<Cfg, BL, Cfg::STAGES - 1>(ld, Cfg::STAGES - 1, nk);
+  // the last stage right away (nothing has used it yet).  On the
+  // interleaved path every stage is loaded (steps past the end repeat the
+  // last step), so that each step has exactly LOADS_PER_WAVE loads behind it.
+  const bool il = iload_ok<Cfg, BL>() && j.K % Cfg::BK == 0;   // uniform
+  if (il) {
+    prefetch_all<Cfg, BL, 0>(ld, nk);
+    wait_vmcnt((Cfg::STAGES - 2) * Cfg::LOADS_PER_WAVE);
+    __syncthreads();
+    ld.issue(stage_ptr<Cfg, Cfg::STAGES - 1>(), (Cfg::STAGES - 1 < nk ? Cfg::STAGES - 1 : nk - 1) * Cfg::BK);
+  } else {
+    prefetch<Cfg, BL, 0>(ld, nk);
+    wait_step<Cfg>(0, nk);
+    __syncthreads();
+    if (Cfg::STAGES - 1 < nk) issue_stage<Cfg, BL, Cfg::STAGES - 1>(ld, Cfg::STAGES - 1, nk);
+  }
   Operands<Cfg> o[2];
   read_operands<Cfg, BL>(o[0], stage_ptr<Cfg, 0>(), 0, wm, wn, lane);
-  for (int kt = 0; kt < nk; kt += Cfg::STAGES) ksteps<Cfg, BL, 0>(f, ld, o, kt, nk, wm, wn, lane);
+  if (il) {
+    for (int kt = 0; kt < nk; kt += Cfg::STAGES) ksteps<Cfg, BL, 0, iload_ok<Cfg, BL>()>(f, ld, o, kt, nk, wm, wn, lane);
+    wait_vmcnt(0);   // the repeated loads past the last step
+  } else {
+    for (int kt = 0; kt < nk; kt += Cfg::STAGES) ksteps<Cfg, BL, 0, false>(f, ld, o, kt, nk, wm, wn, lane);
+  }
   __syncthreads();
 }
 

@@ -179,8 +179,14 @@ enum CfgId : int { CFG_LARGE = 0, CFG_SMALL = 1, CFG_MID = 2 };
 // compute the same bits.
 using CfgLarge = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN, TPF_LARGE_STAGES, TPF_LARGE_BK,
                          TPF_LARGE_L2PF, TPF_LARGE_PP, TPF_LARGE_PPMODE>;
-using CfgLargeFused = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN, TPF_LARGE_STAGES,
-                              TPF_LARGE_BK, TPF_FUSED_L2PF, TPF_LARGE_PP, TPF_LARGE_PPMODE>;
+#ifndef TPF_FUSED_STAGES
+#define TPF_FUSED_STAGES 2
+#endif
+#ifndef TPF_FUSED_BK
+#define TPF_FUSED_BK 64
+#endif
+using CfgLargeFused = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN, TPF_FUSED_STAGES,
+                              TPF_FUSED_BK, TPF_FUSED_L2PF, TPF_LARGE_PP, TPF_LARGE_PPMODE>;
 #ifndef TPF_SMALL_BM
 #define TPF_SMALL_BM 32
 #endif
