@@ -47,7 +47,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset that is always out of range (operands < 2 GiB)
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int BK_ = 64, int L2PF_ = 1, int PP_ = 0,
-          int PPMODE_ = 0, int SWB_ = 2>
+          int PPMODE_ = 0, int SWB_ = 2, int STAGES_A_ = 0>
 struct TileCfg {
   // PP: ping-pong schedule (two wave groups one barrier phase apart; only
   // group 0 issues global loads).  PPMODE selects how waves form the groups:
@@ -66,14 +66,18 @@ struct TileCfg {
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int THREADS = 64 * NW;
   static constexpr int STAGES = STAGES_;
+  // A tiles may have one more LDS slot than B tiles (STAGES_A = STAGES + 1):
+  // then each step's A loads go out during the MFMAs before the barrier, one
+  // step earlier, and only the B loads follow the barrier.
+  static constexpr int STAGES_A = STAGES_A_ ? STAGES_A_ : STAGES_;
+  static_assert(STAGES_A == STAGES || STAGES_A == STAGES + 1, "A slots: STAGES or STAGES + 1");
   static constexpr int SWB = SWB_;    // KN-B 32-byte block swizzle: block ^ (SWB * (k & 3))
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static_assert(TM >= 1 && TN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile of 32x32 MFMA blocks");
   static constexpr int LDS_A = BM * BK * 2;
   static constexpr int LDS_B = BN * BK * 2;
-  static constexpr int LDS_STAGE = LDS_A + LDS_B;
-  static constexpr int LDS_BYTES = STAGES * LDS_STAGE;
+  static constexpr int LDS_BYTES = STAGES_A * LDS_A + STAGES * LDS_B;
   static constexpr int A_INSTR = LDS_A / 1024;   // 1 KiB load instructions per A tile
   static constexpr int B_INSTR = LDS_B / 1024;
   static constexpr int NLW = PP ? NW / 2 : NW;      // waves that issue global loads
@@ -91,6 +95,12 @@ struct TileCfg {
   // A stored [K][M] (transposed A) uses the KN-style layout: rows of BM
   // elements that tile 1 KiB.
   static constexpr bool KM_OK = BM >= 128 && (BM * 2) % 256 == 0 && 1024 % (BM * 2 > 1024 ? 1024 : BM * 2) == 0;
+};
+
+// The LDS slots of one K step: its A tile and its B tile.
+struct Stage {
+  char* a;
+  char* b;
 };
 
 // Operand description of one tile job.
@@ -130,6 +140,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // collide, so the chunk is XORed with (row / ROWS_PER_PERIOD) mod KCH.
 template <class Cfg>
 __device__ __forceinline__ int swz_row(int row) { return (row / Cfg::ROWS_PER_PERIOD) & (Cfg::KCH - 1); }
+
+// Workgroup barrier for the K loop that orders LDS only: this wave's LDS
+// reads have returned (the slot they read may be refilled once every wave
+// has passed), and the compiler keeps memory accesses on their side of it.
+// __syncthreads() would also wait for every outstanding global load
+// (vmcnt(0)), including loads issued for later steps; the loads a step needs
+// are waited for explicitly instead (wait_vmcnt).
+#ifndef TPF_LDS_BARRIER
+#define TPF_LDS_BARRIER 1
+#endif
+__device__ __forceinline__ void lds_barrier() {
+#if TPF_LDS_BARRIER
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#else
+  __syncthreads();
+#endif
+}
 
 // s_waitcnt vmcnt(n) for a small compile-time bound on outstanding loads.
 __device__ __forceinline__ void wait_vmcnt(int n) {
@@ -181,7 +208,7 @@ struct TileLoader {
     rb = make_rsrc(j.B, (int64_t)j.b_rows * j.ldb * 2);
     if constexpr (a_trans(BL)) {
       // A stored [K][M]: the tile is 64 rows of k, each BM elements of m.
-      static_assert(Cfg::KM_OK && Cfg::L2PF == 0, "transposed A needs BM-wide rows tiling 1 KiB, no touch");
+      static_assert(Cfg::KM_OK, "transposed A needs BM-wide rows tiling 1 KiB");
       constexpr int ROW_BYTES = Cfg::BM * 2;
 #pragma unroll
       for (int i = 0; i < Cfg::A_PER_WAVE; ++i) {
@@ -230,7 +257,7 @@ struct TileLoader {
       int isb = 0;
       if (line < Cfg::BM) {                       // A row `line`, 64 k = 128 bytes
         const int gm = j.m0 + line;
-        if (gm < j.a_rows) off = (uint32_t)((int64_t)gm * j.lda * 2);
+        if (!a_trans(BL) && gm < j.a_rows) off = (uint32_t)((int64_t)gm * j.lda * 2);
       } else if (line < Cfg::TOUCH_LINES) {
         const int bl = line - Cfg::BM;
         isb = 1;
@@ -301,10 +328,10 @@ struct TileLoader {
     }
   }
 
-  __device__ __forceinline__ void issue(char* stage, int k0) const {
+  __device__ __forceinline__ void issue(Stage st, int k0) const {
     const int wave = loader_wave(), lane = threadIdx.x & 63;
-    char* la = stage;
-    char* lb = stage + Cfg::LDS_A;
+    char* la = st.a;
+    char* lb = st.b;
     const bool tail = k0 + Cfg::BK > K;   // the same for the whole workgroup
     if (b_layout(BL) == B_KN && !tail) {
       // Every load of a whole K step is in range along k: the step's offset
@@ -360,8 +387,7 @@ struct Operands {
 };
 
 template <class Cfg, int BL>
-__device__ __forceinline__ void read_a(Operands<Cfg>& o, const char* stage, int s, int wm, int wn, int lane) {
-  const char* la = stage;
+__device__ __forceinline__ void read_a(Operands<Cfg>& o, const char* la, int s, int wm, int wn, int lane) {
   const int r32 = lane & 31, half = lane >> 5;
   const int kc = s * 2 + half;
   if constexpr (a_trans(BL)) {
@@ -392,8 +418,7 @@ __device__ __forceinline__ void read_a(Operands<Cfg>& o, const char* stage, int 
 }
 
 template <class Cfg, int BL>
-__device__ __forceinline__ void read_b(Operands<Cfg>& o, const char* stage, int s, int wm, int wn, int lane) {
-  const char* lb = stage + Cfg::LDS_A;
+__device__ __forceinline__ void read_b(Operands<Cfg>& o, const char* lb, int s, int wm, int wn, int lane) {
   const int r32 = lane & 31, half = lane >> 5;
   const int kc = s * 2 + half;
   (void)wm;
@@ -425,9 +450,9 @@ __device__ __forceinline__ void read_b(Operands<Cfg>& o, const char* stage, int 
 
 // The fragments of one 16-wide k slice.
 template <class Cfg, int BL>
-__device__ __forceinline__ void read_operands(Operands<Cfg>& o, const char* stage, int s, int wm, int wn, int lane) {
-  read_a<Cfg, BL>(o, stage, s, wm, wn, lane);
-  read_b<Cfg, BL>(o, stage, s, wm, wn, lane);
+__device__ __forceinline__ void read_operands(Operands<Cfg>& o, Stage st, int s, int wm, int wn, int lane) {
+  read_a<Cfg, BL>(o, st.a, s, wm, wn, lane);
+  read_b<Cfg, BL>(o, st.b, s, wm, wn, lane);
 }
 
 template <class Cfg>
@@ -439,15 +464,32 @@ __device__ __forceinline__ void mfma_step(Frag<Cfg>& f, const Operands<Cfg>& o) 
       f.acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[i], o.b[jn], f.acc[i][jn], 0, 0, 0);
 }
 
-// Each LDS stage is its own __shared__ object.  The loads of a later step are
-// LDS writes in flight (buffer_load ... lds) while the current stage is read;
-// with one object per stage, and every access naming its stage at compile
-// time, the compiler can see that they do not overlap and does not wait for
-// the in-flight loads before reading the current stage.
+// Each LDS slot (the A tile or the B tile of one stage) is its own __shared__
+// object.  The loads of a later step are LDS writes in flight (buffer_load
+// ... lds) while the current slots are read; with one object per slot, and
+// every access naming its slot at compile time, the compiler can see that
+// they do not overlap and does not wait for the in-flight loads before
+// reading the current slots.
+template <class Cfg, int S>
+__device__ __forceinline__ char* a_slot() {
+  __shared__ __attribute__((aligned(1024))) char buf[Cfg::LDS_A];
+  return buf;
+}
+template <class Cfg, int S>
+__device__ __forceinline__ char* b_slot() {
+  __shared__ __attribute__((aligned(1024))) char buf[Cfg::LDS_B];
+  return buf;
+}
+// A slot SA and B slot SB.
+template <class Cfg, int SA, int SB = SA>
+__device__ __forceinline__ Stage stage() {
+  return Stage{a_slot<Cfg, SA>(), b_slot<Cfg, SB>()};
+}
+// LDS that is idle once gemm_tile has returned (A slot 0): LDS_A bytes.
 template <class Cfg, int S>
 __device__ __forceinline__ char* stage_ptr() {
-  __shared__ __attribute__((aligned(1024))) char buf[Cfg::LDS_STAGE];
-  return buf;
+  static_assert(S == 0, "only the first slot serves as scratch");
+  return a_slot<Cfg, 0>();
 }
 
 template <class Cfg>
@@ -461,7 +503,7 @@ __device__ __forceinline__ char* touch_scratch() {
 // instructions per call, so vmcnt arithmetic stays per-step.
 template <class Cfg, int BL, int S>
 __device__ __forceinline__ void issue_stage(const TileLoader<Cfg, BL>& ld, int step, int nk) {
-  ld.issue(stage_ptr<Cfg, S>(), step * Cfg::BK);
+  ld.issue(stage<Cfg, S>(), step * Cfg::BK);
   if constexpr (Cfg::L2PF > 0) {
     const int ts = step + Cfg::L2PF;
     ld.touch(touch_scratch<Cfg>(), (ts < nk ? ts : nk - 1) * Cfg::BK);
@@ -481,7 +523,11 @@ __device__ __forceinline__ void prefetch(const TileLoader<Cfg, BL>& ld, int nk) 
 template <class Cfg, int BL, int S>
 __device__ __forceinline__ void prefetch_all(const TileLoader<Cfg, BL>& ld, int nk) {
   if constexpr (S < Cfg::STAGES - 1) {
-    ld.issue(stage_ptr<Cfg, S>(), (S < nk ? S : nk - 1) * Cfg::BK);
+    ld.issue(stage<Cfg, S>(), (S < nk ? S : nk - 1) * Cfg::BK);
+    if constexpr (Cfg::L2PF > 0) {   // as every step: its loads, then one touch
+      const int ts = S + Cfg::L2PF;
+      ld.touch(touch_scratch<Cfg>(), (ts < nk ? ts : nk - 1) * Cfg::BK);
+    }
     prefetch_all<Cfg, BL, S + 1>(ld, nk);
   }
 }
@@ -500,45 +546,79 @@ __device__ __forceinline__ void wait_step(int t, int nk) {
 #ifndef TPF_ILOAD
 #define TPF_ILOAD 1
 #endif
+
 template <class Cfg, int BL>
 __device__ __forceinline__ constexpr bool iload_ok() {
-  return TPF_ILOAD && Cfg::L2PF == 0 && !Cfg::PP && Cfg::BM >= 128;
+  return TPF_ILOAD && !Cfg::PP && Cfg::BM >= 128;
 }
 
-// The last k slice's MFMAs of the current step, with the global -> LDS loads
-// of step kn into stage S issued between them.  After a K-step barrier all
-// waves of the workgroup would otherwise issue their loads at once; the
-// address unit's queue then fills, and a wave stalled on a load cannot issue
-// its MFMAs either (in-order issue), so the matrix core idles.  Interleaved,
-// the queue drains while the MFMAs run (measured 6-10 % faster on the large
-// forward shapes).  Only for K a multiple of BK (no tail step): the step's
-// offset goes into the scalar offset, as in TileLoader::issue.  Past the
-// last step (kn >= nk) the last step is loaded again into the free stage,
-// which nothing reads afterwards.
-template <class Cfg, int BL, int S>
+
+
+// Loads of one K step on the interleaved path are numbered q = 0 .. NL-1;
+// IL_BFIRST puts the B tile's loads first.  IL_LATE of them (the last ones)
+// are issued in the first k slice of the next step instead of right after
+// the barrier.
+
+// Scalar offsets of step kn (clamped to the last step) and its load q into
+// stage S.
+template <class Cfg, int BL>
+struct IlOffsets {
+  int wv, ka, kb;
+  __device__ __forceinline__ IlOffsets(const TileLoader<Cfg, BL>& ld, int kn, int nk) {
+    wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int k0 = (kn < nk ? kn : nk - 1) * Cfg::BK;
+    ka = __builtin_amdgcn_readfirstlane(k0 * (int)(a_trans(BL) ? ld.lda_bytes : 2u));
+    kb = __builtin_amdgcn_readfirstlane(k0 * (int)(b_layout(BL) == B_NK ? 2u : ld.ldb_bytes));
+  }
+  __device__ __forceinline__ void load(const TileLoader<Cfg, BL>& ld, Stage st, int q) const {
+    char* la = st.a;
+    char* lb = st.b;
+    const bool isa = q < Cfg::A_PER_WAVE;   // A tile's loads first, then B's
+    const int i = isa ? q : q - Cfg::A_PER_WAVE;
+    if (isa)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ld.ra, (lds_void_t*)(la + (wv * Cfg::A_PER_WAVE + i) * 1024), 16,
+                                               (int)ld.a_off[i], ka, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ld.rb, (lds_void_t*)(lb + (wv * Cfg::B_PER_WAVE + i) * 1024), 16,
+                                               (int)ld.b_off[i], kb, 0, 0);
+  }
+};
+
+// Loads Q0 .. Q1-1 of step kn into stage S, without MFMAs (prologue).
+template <class Cfg, int BL, int SA, int SB, int Q0, int Q1>
+__device__ __forceinline__ void il_loads(const TileLoader<Cfg, BL>& ld, int kn, int nk) {
+  const IlOffsets<Cfg, BL> x(ld, kn, nk);
+#pragma unroll
+  for (int q = Q0; q < Q1; ++q) x.load(ld, stage<Cfg, SA, SB>(), q);
+}
+
+// One k slice's MFMAs with loads Q0 .. Q1-1 of step kn into stage S issued
+// between them.  After a K-step barrier all waves of the workgroup would
+// otherwise issue their loads at once; the address unit's queue then fills,
+// and a wave stalled on a load cannot issue its MFMAs either (in-order
+// issue), so the matrix core idles.  Interleaved, the queue drains while the
+// MFMAs run (measured 6-10 % faster on the large shapes).  Only for K a
+// multiple of BK (no tail step): the step's offset goes into the scalar
+// offset, as in TileLoader::issue.  Past the last step (kn >= nk) the last
+// step is loaded again into the free stage, which nothing reads afterwards.
+template <class Cfg, int BL, int SA, int SB, int Q0, int Q1>
 __device__ __forceinline__ void mfma_step_loads(Frag<Cfg>& f, const Operands<Cfg>& o, const TileLoader<Cfg, BL>& ld,
                                                 int kn, int nk) {
-  constexpr int NL = Cfg::A_PER_WAVE + Cfg::B_PER_WAVE;
+  constexpr int NLP = Q1 - Q0;
   constexpr int NM = Cfg::TM * Cfg::TN;
-  char* la = stage_ptr<Cfg, S>();
-  char* lb = la + Cfg::LDS_A;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int k0 = (kn < nk ? kn : nk - 1) * Cfg::BK;
-  const int ka = __builtin_amdgcn_readfirstlane(k0 * (int)(a_trans(BL) ? ld.lda_bytes : 2u));
-  const int kb = __builtin_amdgcn_readfirstlane(k0 * (int)(b_layout(BL) == B_NK ? 2u : ld.ldb_bytes));
+  const IlOffsets<Cfg, BL> x(ld, kn, nk);
 #pragma unroll
-  for (int q = 0; q < (NM > NL ? NM : NL); ++q) {
+  for (int q = 0; q < (NM > NLP ? NM : NLP); ++q) {
     if (q < NM) {
       const int i = q / Cfg::TN, jn = q % Cfg::TN;
       f.acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[i], o.b[jn], f.acc[i][jn], 0, 0, 0);
     }
-    if (q < Cfg::A_PER_WAVE)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ld.ra, (lds_void_t*)(la + (wv * Cfg::A_PER_WAVE + q) * 1024), 16,
-                                               (int)ld.a_off[q], ka, 0, 0);
-    else if (q < NL)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ld.rb, (lds_void_t*)(lb + (wv * Cfg::B_PER_WAVE + (q - Cfg::A_PER_WAVE)) * 1024), 16,
-          (int)ld.b_off[q - Cfg::A_PER_WAVE], kb, 0, 0);
+    if (q < NLP) x.load(ld, stage<Cfg, SA, SB>(), Q0 + q);
+  }
+  if constexpr (Cfg::L2PF > 0 && Cfg::STAGES_A == Cfg::STAGES && Q1 == Cfg::A_PER_WAVE + Cfg::B_PER_WAVE) {
+    // after the loads, so that waiting for them never waits for the touch
+    const int ts = kn + Cfg::L2PF;
+    ld.touch(touch_scratch<Cfg>(), (ts < nk ? ts : nk - 1) * Cfg::BK);
   }
 }
 
@@ -554,7 +634,7 @@ __device__ __forceinline__ void kstep(Frag<Cfg>& f, const TileLoader<Cfg, BL>& l
                                       int nk, int wm, int wn, int lane) {
   constexpr int SUB = Cfg::BK / 16;
   static_assert(SUB % 2 == 0, "even number of k slices per step");
-  const char* cur = stage_ptr<Cfg, S>();
+  const Stage cur = stage<Cfg, S>();
 #pragma unroll
   for (int s = 0; s < SUB - 1; ++s) {
     read_operands<Cfg, BL>(o[(s + 1) & 1], cur, s + 1, wm, wn, lane);
@@ -564,7 +644,7 @@ __device__ __forceinline__ void kstep(Frag<Cfg>& f, const TileLoader<Cfg, BL>& l
     wait_step<Cfg>(kt + 1, nk);
     __syncthreads();
     if (kt + Cfg::STAGES < nk) issue_stage<Cfg, BL, S>(ld, kt + Cfg::STAGES, nk);
-    read_operands<Cfg, BL>(o[0], stage_ptr<Cfg, (S + 1) % Cfg::STAGES>(), 0, wm, wn, lane);
+    read_operands<Cfg, BL>(o[0], stage<Cfg, (S + 1) % Cfg::STAGES>(), 0, wm, wn, lane);
   }
   mfma_step<Cfg>(f, o[1]);
 }
@@ -578,18 +658,70 @@ __device__ __forceinline__ void kstep_il(Frag<Cfg>& f, const TileLoader<Cfg, BL>
                                          int nk, int wm, int wn, int lane) {
   constexpr int SUB = Cfg::BK / 16;
   static_assert(SUB % 2 == 0, "even number of k slices per step");
-  const char* cur = stage_ptr<Cfg, S>();
+  constexpr int NL = Cfg::A_PER_WAVE + Cfg::B_PER_WAVE;
+  const Stage cur = stage<Cfg, S>();
 #pragma unroll
   for (int s = 0; s < SUB - 1; ++s) {
     read_operands<Cfg, BL>(o[(s + 1) & 1], cur, s + 1, wm, wn, lane);
     mfma_step<Cfg>(f, o[s & 1]);
   }
-  // Every step issues exactly LOADS_PER_WAVE loads, so the loads of the
-  // STAGES - 2 steps after step kt + 1 may stay in flight.
-  wait_vmcnt((Cfg::STAGES - 2) * Cfg::LOADS_PER_WAVE);
-  __syncthreads();
-  read_operands<Cfg, BL>(o[0], stage_ptr<Cfg, (S + 1) % Cfg::STAGES>(), 0, wm, wn, lane);
-  mfma_step_loads<Cfg, BL, S>(f, o[1], ld, kt + Cfg::STAGES, nk);
+  // Every step issues exactly LOADS_PER_WAVE loads (the touch last), so the
+  // loads of the STAGES - 2 steps after step kt + 1 and the last touch may
+  // stay in flight.
+  wait_vmcnt((Cfg::STAGES - 2) * Cfg::LOADS_PER_WAVE + Cfg::TOUCH_PER_WAVE);
+  lds_barrier();
+  read_operands<Cfg, BL>(o[0], stage<Cfg, (S + 1) % Cfg::STAGES>(), 0, wm, wn, lane);
+  mfma_step_loads<Cfg, BL, S, S, 0, NL>(f, o[1], ld, kt + Cfg::STAGES, nk);
+}
+
+// K step T (mod lcm of the slot counts) with one more A slot than B slots:
+// the A loads of step kt + 2 go out between the MFMAs of slices 0 .. SUB-2
+// (their slot held step kt - 1, free since the previous barrier), the B
+// loads of step kt + 2 between those of the last slice, after the barrier.
+// The address unit then has the whole step for the A loads, and the A loads
+// have almost two steps to land.
+template <class Cfg, int BL, int T>
+__device__ __forceinline__ void kstep_ila(Frag<Cfg>& f, const TileLoader<Cfg, BL>& ld, Operands<Cfg> (&o)[2], int kt,
+                                          int nk, int wm, int wn, int lane) {
+  constexpr int SUB = Cfg::BK / 16;
+  static_assert(SUB % 2 == 0, "even number of k slices per step");
+  static_assert(Cfg::STAGES == 2 && Cfg::STAGES_A == 3 && Cfg::L2PF == 0, "two B slots, three A slots");
+  constexpr int SA = T % Cfg::STAGES_A, SB = T % Cfg::STAGES;
+  constexpr int SAN = (SA + 2) % Cfg::STAGES_A;        // A slot of step kt + 2
+  constexpr int NA = Cfg::A_PER_WAVE, NB = Cfg::B_PER_WAVE;
+  const Stage cur = stage<Cfg, SA, SB>();
+#pragma unroll
+  for (int s = 0; s < SUB - 1; ++s) {
+    read_operands<Cfg, BL>(o[(s + 1) & 1], cur, s + 1, wm, wn, lane);
+    // A loads [0, Q1_0) in slice 0, [Q1_0, Q1_1) in slice 1, the rest in
+    // slice 2 (front-loaded: the earliest have the longest to land)
+    constexpr int Q1_0 = (NA + SUB - 2) / (SUB - 1);
+    constexpr int Q1_1 = (2 * NA + SUB - 2) / (SUB - 1);
+    if (s == 0)
+      mfma_step_loads<Cfg, BL, SAN, SB, 0, Q1_0>(f, o[0], ld, kt + 2, nk);
+    else if (s == 1)
+      mfma_step_loads<Cfg, BL, SAN, SB, Q1_0, Q1_1>(f, o[1], ld, kt + 2, nk);
+    else if (s == 2)
+      mfma_step_loads<Cfg, BL, SAN, SB, Q1_1, NA>(f, o[0], ld, kt + 2, nk);
+    else
+      mfma_step<Cfg>(f, o[s & 1]);
+  }
+  // The A loads of step kt + 2 were issued after step kt + 1's.
+  wait_vmcnt(NA);
+  lds_barrier();
+  read_operands<Cfg, BL>(o[0], stage<Cfg, (SA + 1) % Cfg::STAGES_A, (SB + 1) % Cfg::STAGES>(), 0, wm, wn, lane);
+  mfma_step_loads<Cfg, BL, SAN, SB, NA, NA + NB>(f, o[1], ld, kt + 2, nk);
+}
+
+template <class Cfg, int BL, int T>
+__device__ __forceinline__ void ksteps_ila(Frag<Cfg>& f, const TileLoader<Cfg, BL>& ld, Operands<Cfg> (&o)[2], int kt,
+                                           int nk, int wm, int wn, int lane) {
+  if constexpr (T < 6) {
+    if (kt + T < nk) {
+      kstep_ila<Cfg, BL, T>(f, ld, o, kt + T, nk, wm, wn, lane);
+      ksteps_ila<Cfg, BL, T + 1>(f, ld, o, kt, nk, wm, wn, lane);
+    }
+  }
 }
 
 template <class Cfg, int BL, int S, bool IL>
@@ -631,9 +763,9 @@ __device__ __forceinline__ void pp_step(Frag<Cfg>& f, const TileLoader<Cfg, BL>&
   // ---- M(t)
   if (grp == 0) {
     constexpr int SL = (S + Cfg::STAGES - 1) % Cfg::STAGES;   // stage of step t-1 (== step t+STAGES-1)
-    if (t + Cfg::STAGES - 1 < nk) ld.issue(stage_ptr<Cfg, SL>(), (t + Cfg::STAGES - 1) * Cfg::BK);
+    if (t + Cfg::STAGES - 1 < nk) ld.issue(stage<Cfg, SL>(), (t + Cfg::STAGES - 1) * Cfg::BK);
   }
-  const char* cur = stage_ptr<Cfg, S>();
+  const Stage cur = stage<Cfg, S>();
 #pragma unroll
   for (int s = 0; s < SUB; ++s) read_operands<Cfg, BL>(o[s], cur, s, wm, wn, lane);
   __syncthreads();
@@ -661,7 +793,7 @@ __device__ __forceinline__ void pp_steps(Frag<Cfg>& f, const TileLoader<Cfg, BL>
 template <class Cfg, int BL, int S>
 __device__ __forceinline__ void pp_prefetch(const TileLoader<Cfg, BL>& ld, int nk) {
   if constexpr (S < Cfg::STAGES - 1) {
-    if (S < nk) ld.issue(stage_ptr<Cfg, S>(), S * Cfg::BK);
+    if (S < nk) ld.issue(stage<Cfg, S>(), S * Cfg::BK);
     pp_prefetch<Cfg, BL, S + 1>(ld, nk);
   }
 }
@@ -715,11 +847,32 @@ __device__ __forceinline__ void gemm_tile(Frag<Cfg>& f, const TileJob& j) {
   // interleaved path every stage is loaded (steps past the end repeat the
   // last step), so that each step has exactly LOADS_PER_WAVE loads behind it.
   const bool il = iload_ok<Cfg, BL>() && j.K % Cfg::BK == 0;   // uniform
+  if constexpr (Cfg::STAGES_A > Cfg::STAGES) {
+    if (il) {
+      // Steps 0 and 1 into fresh slots, A then B each (the order the steps
+      // after them keep); wait for step 0.
+      ld.issue(stage<Cfg, 0, 0>(), 0);
+      ld.issue(stage<Cfg, 1, 1>(), (1 < nk ? 1 : nk - 1) * Cfg::BK);
+      wait_vmcnt(Cfg::LOADS_PER_WAVE);
+      __syncthreads();
+      Operands<Cfg> o[2];
+      read_operands<Cfg, BL>(o[0], stage<Cfg, 0, 0>(), 0, wm, wn, lane);
+      for (int kt = 0; kt < nk; kt += 6) ksteps_ila<Cfg, BL, 0>(f, ld, o, kt, nk, wm, wn, lane);
+      wait_vmcnt(0);   // the repeated loads past the last step
+      __syncthreads();
+      return;
+    }
+  }
   if (il) {
     prefetch_all<Cfg, BL, 0>(ld, nk);
-    wait_vmcnt((Cfg::STAGES - 2) * Cfg::LOADS_PER_WAVE);
+    wait_vmcnt((Cfg::STAGES - 2) * Cfg::LOADS_PER_WAVE + Cfg::TOUCH_PER_WAVE);
     __syncthreads();
-    ld.issue(stage_ptr<Cfg, Cfg::STAGES - 1>(), (Cfg::STAGES - 1 < nk ? Cfg::STAGES - 1 : nk - 1) * Cfg::BK);
+    il_loads<Cfg, BL, Cfg::STAGES - 1, Cfg::STAGES - 1, 0, Cfg::A_PER_WAVE + Cfg::B_PER_WAVE>(ld, Cfg::STAGES - 1,
+                                                                                         nk);
+    if constexpr (Cfg::L2PF > 0) {
+      const int ts = Cfg::STAGES - 1 + Cfg::L2PF;
+      ld.touch(touch_scratch<Cfg>(), (ts < nk ? ts : nk - 1) * Cfg::BK);
+    }
   } else {
     prefetch<Cfg, BL, 0>(ld, nk);
     wait_step<Cfg>(0, nk);
@@ -727,7 +880,7 @@ __device__ __forceinline__ void gemm_tile(Frag<Cfg>& f, const TileJob& j) {
     if (Cfg::STAGES - 1 < nk) issue_stage<Cfg, BL, Cfg::STAGES - 1>(ld, Cfg::STAGES - 1, nk);
   }
   Operands<Cfg> o[2];
-  read_operands<Cfg, BL>(o[0], stage_ptr<Cfg, 0>(), 0, wm, wn, lane);
+  read_operands<Cfg, BL>(o[0], stage<Cfg, 0>(), 0, wm, wn, lane);
   if (il) {
     for (int kt = 0; kt < nk; kt += Cfg::STAGES) ksteps<Cfg, BL, 0, iload_ok<Cfg, BL>()>(f, ld, o, kt, nk, wm, wn, lane);
     wait_vmcnt(0);   // the repeated loads past the last step

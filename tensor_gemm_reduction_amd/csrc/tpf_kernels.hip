@@ -424,9 +424,9 @@ __device__ __forceinline__ float message_value(float acc) {
 // in shard order and then its own value, and stores the four results.
 template <class Cfg>
 struct FoldBand {
-  static constexpr int ROWS = Cfg::LDS_STAGE >= 64 * Cfg::BN * 4 ? 64 : 32;   // rows per band
+  static constexpr int ROWS = Cfg::LDS_A >= 64 * Cfg::BN * 4 ? 64 : 32;   // rows per band
   static_assert(Cfg::BM % ROWS == 0 && Cfg::WM % 32 == 0 && ROWS % 32 == 0, "bands of whole 32-row blocks");
-  static_assert(ROWS * Cfg::BN * 4 <= Cfg::LDS_STAGE, "a band fits one LDS stage");
+  static_assert(ROWS * Cfg::BN * 4 <= Cfg::LDS_A, "a band fits the idle LDS slot");
 };
 
 // Sum of the partials of shards 0 .. np-1 at elements e .. e+3, left to right
