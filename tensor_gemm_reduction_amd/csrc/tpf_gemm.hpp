@@ -642,7 +642,7 @@ __device__ __forceinline__ void kstep(Frag<Cfg>& f, const TileLoader<Cfg, BL>& l
   }
   if (kt + 1 < nk) {
     wait_step<Cfg>(kt + 1, nk);
-    __syncthreads();
+    lds_barrier();
     if (kt + Cfg::STAGES < nk) issue_stage<Cfg, BL, S>(ld, kt + Cfg::STAGES, nk);
     read_operands<Cfg, BL>(o[0], stage<Cfg, (S + 1) % Cfg::STAGES>(), 0, wm, wn, lane);
   }

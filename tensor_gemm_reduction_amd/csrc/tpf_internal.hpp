@@ -209,7 +209,10 @@ using CfgLargeFused = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARG
 //   M <= 64:  64 x 256 tiles, 3 stages of 40 KiB: each weight tile is read by
 //             one workgroup instead of two (47 % -> 61 % of HBM bandwidth at M = 64).
 using CfgSmall = TileCfg<TPF_SMALL_BM, TPF_SMALL_BN, 1, 4, TPF_SMALL_STAGES, 64, 0>;
-using CfgMid = TileCfg<64, 256, 1, 4, 3, 64, 0>;
+#ifndef TPF_MID_STAGES
+#define TPF_MID_STAGES 3
+#endif
+using CfgMid = TileCfg<64, 256, 1, 4, TPF_MID_STAGES, 64, 0>;
 
 int cfg_bm(int cfg);
 int cfg_bn(int cfg);
