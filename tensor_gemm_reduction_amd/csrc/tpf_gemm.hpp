@@ -485,11 +485,11 @@ template <class Cfg, int SA, int SB = SA>
 __device__ __forceinline__ Stage stage() {
   return Stage{a_slot<Cfg, SA>(), b_slot<Cfg, SB>()};
 }
-// LDS that is idle once gemm_tile has returned (A slot 0): LDS_A bytes.
+// LDS that is idle once gemm_tile has returned (A slot S): LDS_A bytes each.
 template <class Cfg, int S>
 __device__ __forceinline__ char* stage_ptr() {
-  static_assert(S == 0, "only the first slot serves as scratch");
-  return a_slot<Cfg, 0>();
+  static_assert(S < Cfg::STAGES_A, "an A slot");
+  return a_slot<Cfg, S>();
 }
 
 template <class Cfg>
@@ -524,10 +524,6 @@ template <class Cfg, int BL, int S>
 __device__ __forceinline__ void prefetch_all(const TileLoader<Cfg, BL>& ld, int nk) {
   if constexpr (S < Cfg::STAGES - 1) {
     ld.issue(stage<Cfg, S>(), (S < nk ? S : nk - 1) * Cfg::BK);
-    if constexpr (Cfg::L2PF > 0) {   // as every step: its loads, then one touch
-      const int ts = S + Cfg::L2PF;
-      ld.touch(touch_scratch<Cfg>(), (ts < nk ? ts : nk - 1) * Cfg::BK);
-    }
     prefetch_all<Cfg, BL, S + 1>(ld, nk);
   }
 }
@@ -549,7 +545,7 @@ __device__ __forceinline__ void wait_step(int t, int nk) {
 
 template <class Cfg, int BL>
 __device__ __forceinline__ constexpr bool iload_ok() {
-  return TPF_ILOAD && !Cfg::PP && Cfg::BM >= 128;
+  return TPF_ILOAD && !Cfg::PP && Cfg::BM >= 128 && Cfg::L2PF == 0;
 }
 
 
@@ -615,11 +611,6 @@ __device__ __forceinline__ void mfma_step_loads(Frag<Cfg>& f, const Operands<Cfg
     }
     if (q < NLP) x.load(ld, stage<Cfg, SA, SB>(), Q0 + q);
   }
-  if constexpr (Cfg::L2PF > 0 && Cfg::STAGES_A == Cfg::STAGES && Q1 == Cfg::A_PER_WAVE + Cfg::B_PER_WAVE) {
-    // after the loads, so that waiting for them never waits for the touch
-    const int ts = kn + Cfg::L2PF;
-    ld.touch(touch_scratch<Cfg>(), (ts < nk ? ts : nk - 1) * Cfg::BK);
-  }
 }
 
 // One K step on stage S, software-pipelined across steps.  On entry the
@@ -665,10 +656,9 @@ __device__ __forceinline__ void kstep_il(Frag<Cfg>& f, const TileLoader<Cfg, BL>
     read_operands<Cfg, BL>(o[(s + 1) & 1], cur, s + 1, wm, wn, lane);
     mfma_step<Cfg>(f, o[s & 1]);
   }
-  // Every step issues exactly LOADS_PER_WAVE loads (the touch last), so the
-  // loads of the STAGES - 2 steps after step kt + 1 and the last touch may
-  // stay in flight.
-  wait_vmcnt((Cfg::STAGES - 2) * Cfg::LOADS_PER_WAVE + Cfg::TOUCH_PER_WAVE);
+  // Every step issues exactly LOADS_PER_WAVE loads, so the loads of the
+  // STAGES - 2 steps after step kt + 1 may stay in flight.
+  wait_vmcnt((Cfg::STAGES - 2) * Cfg::LOADS_PER_WAVE);
   lds_barrier();
   read_operands<Cfg, BL>(o[0], stage<Cfg, (S + 1) % Cfg::STAGES>(), 0, wm, wn, lane);
   mfma_step_loads<Cfg, BL, S, S, 0, NL>(f, o[1], ld, kt + Cfg::STAGES, nk);
@@ -865,14 +855,10 @@ __device__ __forceinline__ void gemm_tile(Frag<Cfg>& f, const TileJob& j) {
   }
   if (il) {
     prefetch_all<Cfg, BL, 0>(ld, nk);
-    wait_vmcnt((Cfg::STAGES - 2) * Cfg::LOADS_PER_WAVE + Cfg::TOUCH_PER_WAVE);
+    wait_vmcnt((Cfg::STAGES - 2) * Cfg::LOADS_PER_WAVE);
     __syncthreads();
     il_loads<Cfg, BL, Cfg::STAGES - 1, Cfg::STAGES - 1, 0, Cfg::A_PER_WAVE + Cfg::B_PER_WAVE>(ld, Cfg::STAGES - 1,
                                                                                          nk);
-    if constexpr (Cfg::L2PF > 0) {
-      const int ts = Cfg::STAGES - 1 + Cfg::L2PF;
-      ld.touch(touch_scratch<Cfg>(), (ts < nk ? ts : nk - 1) * Cfg::BK);
-    }
   } else {
     prefetch<Cfg, BL, 0>(ld, nk);
     wait_step<Cfg>(0, nk);

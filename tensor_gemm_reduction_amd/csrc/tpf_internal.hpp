@@ -152,7 +152,7 @@ enum CfgId : int { CFG_LARGE = 0, CFG_SMALL = 1, CFG_MID = 2 };
 #define TPF_LARGE_L2PF 0
 #endif
 #ifndef TPF_FUSED_L2PF
-#define TPF_FUSED_L2PF 1
+#define TPF_FUSED_L2PF 0
 #endif
 #ifndef TPF_LARGE_PP
 #define TPF_LARGE_PP 0
@@ -172,14 +172,13 @@ enum CfgId : int { CFG_LARGE = 0, CFG_SMALL = 1, CFG_MID = 2 };
 #ifndef TPF_LARGE_BN
 #define TPF_LARGE_BN 256
 #endif
-// The one-tile-per-workgroup kernels run without the L2 line touch (measured
-// 1-2 % faster under sustained load); the persistent kernel, whose
-// workgroups move between chunks and re-stream weights, keeps it (measured
-// 30 % faster with it).  The touch moves no data into registers, so both
-// compute the same bits.
-// The large tiles give A one more LDS slot than B (3 x 32 KiB + 2 x 32 KiB =
-// the whole 160 KiB): each step's A loads then go out during the MFMAs
-// before the barrier (measured 3-7 % faster than two slots each).
+// The large tiles (one per workgroup, and the persistent kernel's) give A
+// one more LDS slot than B (3 x 32 KiB + 2 x 32 KiB = the whole 160 KiB):
+// each step's A loads then go out during the MFMAs before the barrier
+// (measured 3-7 % faster than two slots each, and the persistent kernel
+// 5-14 % faster than with two slots and the L2 line touch it used before).
+// Neither uses the L2 line touch any more (TileCfg's L2PF; an extra load
+// instruction per step measured 8-12 % slower with interleaved loads).
 #ifndef TPF_LARGE_STAGES_A
 #define TPF_LARGE_STAGES_A 3
 #endif
@@ -191,8 +190,11 @@ using CfgLarge = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN,
 #ifndef TPF_FUSED_BK
 #define TPF_FUSED_BK 64
 #endif
+#ifndef TPF_FUSED_STAGES_A
+#define TPF_FUSED_STAGES_A 3
+#endif
 using CfgLargeFused = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN, TPF_FUSED_STAGES,
-                              TPF_FUSED_BK, TPF_FUSED_L2PF, TPF_LARGE_PP, TPF_LARGE_PPMODE>;
+                              TPF_FUSED_BK, TPF_FUSED_L2PF, TPF_LARGE_PP, TPF_LARGE_PPMODE, 2, TPF_FUSED_STAGES_A>;
 #ifndef TPF_SMALL_BM
 #define TPF_SMALL_BM 32
 #endif

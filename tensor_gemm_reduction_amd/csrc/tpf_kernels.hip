@@ -418,15 +418,26 @@ __device__ __forceinline__ float message_value(float acc) {
 }
 
 // The fold epilogue streams the partials with 16-byte loads: the tile's
-// accumulators are staged through the (idle) LDS stage 0 in bands of
+// accumulators are staged through idle LDS slots in bands of
 // FoldBand::ROWS rows, then every thread takes groups of four consecutive
 // columns of a band row, loads the p-1 partials of those elements, adds them
 // in shard order and then its own value, and stores the four results.
 template <class Cfg>
 struct FoldBand {
-  static constexpr int ROWS = Cfg::LDS_A >= 64 * Cfg::BN * 4 ? 64 : 32;   // rows per band
-  static_assert(Cfg::BM % ROWS == 0 && Cfg::WM % 32 == 0 && ROWS % 32 == 0, "bands of whole 32-row blocks");
-  static_assert(ROWS * Cfg::BN * 4 <= Cfg::LDS_A, "a band fits the idle LDS slot");
+  // A band of 64 rows spans the first two A slots when one holds fewer rows
+  // (rows [0, SLOT_ROWS) in slot 0, the rest in slot 1).
+  static constexpr int SLOT_ROWS = Cfg::LDS_A / (Cfg::BN * 4);
+  static constexpr int ROWS = 64;
+  static_assert(SLOT_ROWS >= 64 || (SLOT_ROWS == 32 && Cfg::STAGES_A >= 2), "a band fits two idle LDS slots");
+  static_assert(Cfg::BM % ROWS == 0 && Cfg::WM % 32 == 0, "bands of whole 32-row blocks");
+  __device__ __forceinline__ static float* row_ptr(int row) {
+    if constexpr (SLOT_ROWS >= ROWS) {
+      return reinterpret_cast<float*>(stage_ptr<Cfg, 0>()) + row * Cfg::BN;
+    } else {
+      return row < SLOT_ROWS ? reinterpret_cast<float*>(stage_ptr<Cfg, 0>()) + row * Cfg::BN
+                             : reinterpret_cast<float*>(stage_ptr<Cfg, 1>()) + (row - SLOT_ROWS) * Cfg::BN;
+    }
+  }
 };
 
 // Sum of the partials of shards 0 .. np-1 at elements e .. e+3, left to right
@@ -454,7 +465,6 @@ __device__ __forceinline__ void fold_store_pp(const Frag<Cfg>& f, const TileJob&
   constexpr int GROUPS = BR * Cfg::BN / 4;                 // four-column groups per band
   constexpr int PER = GROUPS / Cfg::THREADS;
   static_assert(GROUPS % Cfg::THREADS == 0, "whole groups per thread");
-  float* band = reinterpret_cast<float*>(stage_ptr<Cfg, 0>());   // [BR][BN] fp32
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   const int r32 = lane & 31, half = lane >> 5;
@@ -472,10 +482,11 @@ __device__ __forceinline__ void fold_store_pp(const Frag<Cfg>& f, const TileJob&
 #pragma unroll
         for (int jn = 0; jn < Cfg::TN; ++jn) {
           const int col = wn * Cfg::WN + jn * 32 + r32;
+          float* blk = FoldBand<Cfg>::row_ptr(r0 - b0);   // a 32-row block lies in one slot
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int row = r0 - b0 + 8 * (v >> 2) + 4 * half + (v & 3);
-            band[row * Cfg::BN + col] = f.acc[i][jn][v];
+            const int row = 8 * (v >> 2) + 4 * half + (v & 3);
+            blk[row * Cfg::BN + col] = f.acc[i][jn][v];
           }
         }
       }
@@ -489,7 +500,7 @@ __device__ __forceinline__ void fold_store_pp(const Frag<Cfg>& f, const TileJob&
         const int64_t e = (int64_t)(j.m0 + b0 + row) * N + j.n0 + c;
         // This shard's own values as the message it would have stored
         // (rounded to bf16 first for 2-byte messages).
-        f32x4_t own = *reinterpret_cast<const f32x4_t*>(band + row * Cfg::BN + c);
+        f32x4_t own = *reinterpret_cast<const f32x4_t*>(FoldBand<Cfg>::row_ptr(row) + c);
 #pragma unroll
         for (int t = 0; t < 4; ++t) own[t] = message_value<PB>(own[t]);
         const f32x4_t s = np > 0 ? fold_partials4<PP, PB>(a.P, a.p_stride, np, e) + own : own;
