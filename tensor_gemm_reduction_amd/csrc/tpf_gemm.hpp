@@ -47,7 +47,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset that is always out of range (operands < 2 GiB)
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int BK_ = 64, int L2PF_ = 1, int PP_ = 0,
-          int PPMODE_ = 0, int SWB_ = 2, int STAGES_A_ = 0>
+          int PPMODE_ = 0, int SWB_ = 2, int STAGES_A_ = 0, int STAGES_B_ = 0>
 struct TileCfg {
   // PP: ping-pong schedule (two wave groups one barrier phase apart; only
   // group 0 issues global loads).  PPMODE selects how waves form the groups:
@@ -70,14 +70,17 @@ struct TileCfg {
   // then each step's A loads go out during the MFMAs before the barrier, one
   // step earlier, and only the B loads follow the barrier.
   static constexpr int STAGES_A = STAGES_A_ ? STAGES_A_ : STAGES_;
+  static constexpr int STAGES_B = STAGES_B_ ? STAGES_B_ : STAGES_;   // or B has the extra slot
   static_assert(STAGES_A == STAGES || STAGES_A == STAGES + 1, "A slots: STAGES or STAGES + 1");
+  static_assert(STAGES_B == STAGES || STAGES_B == STAGES + 1, "B slots: STAGES or STAGES + 1");
+  static_assert(STAGES_A == STAGES || STAGES_B == STAGES, "one operand with an extra slot");
   static constexpr int SWB = SWB_;    // KN-B 32-byte block swizzle: block ^ (SWB * (k & 3))
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static_assert(TM >= 1 && TN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile of 32x32 MFMA blocks");
   static constexpr int LDS_A = BM * BK * 2;
   static constexpr int LDS_B = BN * BK * 2;
-  static constexpr int LDS_BYTES = STAGES_A * LDS_A + STAGES * LDS_B;
+  static constexpr int LDS_BYTES = STAGES_A * LDS_A + STAGES_B * LDS_B;
   static constexpr int A_INSTR = LDS_A / 1024;   // 1 KiB load instructions per A tile
   static constexpr int B_INSTR = LDS_B / 1024;
   static constexpr int NLW = PP ? NW / 2 : NW;      // waves that issue global loads
@@ -664,43 +667,49 @@ __device__ __forceinline__ void kstep_il(Frag<Cfg>& f, const TileLoader<Cfg, BL>
   mfma_step_loads<Cfg, BL, S, S, 0, NL>(f, o[1], ld, kt + Cfg::STAGES, nk);
 }
 
-// K step T (mod lcm of the slot counts) with one more A slot than B slots:
-// the A loads of step kt + 2 go out between the MFMAs of slices 0 .. SUB-2
-// (their slot held step kt - 1, free since the previous barrier), the B
-// loads of step kt + 2 between those of the last slice, after the barrier.
-// The address unit then has the whole step for the A loads, and the A loads
-// have almost two steps to land.
+// K step T (mod lcm of the slot counts) with one more LDS slot for one
+// operand (the "early" one; A by default): the early operand's loads of step
+// kt + 2 go out between the MFMAs of slices 0 .. SUB-2 (their slot held step
+// kt - 1, free since the previous barrier), the other operand's loads of step
+// kt + 2 between those of the last slice, after the barrier.  The address
+// unit then has the whole step for the early loads, and they have almost two
+// steps to land.
 template <class Cfg, int BL, int T>
 __device__ __forceinline__ void kstep_ila(Frag<Cfg>& f, const TileLoader<Cfg, BL>& ld, Operands<Cfg> (&o)[2], int kt,
                                           int nk, int wm, int wn, int lane) {
   constexpr int SUB = Cfg::BK / 16;
   static_assert(SUB % 2 == 0, "even number of k slices per step");
-  static_assert(Cfg::STAGES == 2 && Cfg::STAGES_A == 3 && Cfg::L2PF == 0, "two B slots, three A slots");
-  constexpr int SA = T % Cfg::STAGES_A, SB = T % Cfg::STAGES;
-  constexpr int SAN = (SA + 2) % Cfg::STAGES_A;        // A slot of step kt + 2
+  static_assert(Cfg::STAGES == 2 && Cfg::STAGES_A + Cfg::STAGES_B == 5 && Cfg::L2PF == 0,
+                "two slots for one operand, three for the other");
+  constexpr bool EB = Cfg::STAGES_B > Cfg::STAGES;     // B is the early operand
+  constexpr int SA = T % Cfg::STAGES_A, SB = T % Cfg::STAGES_B;
+  constexpr int SAN = (SA + 2) % Cfg::STAGES_A;        // slots of step kt + 2
+  constexpr int SBN = (SB + 2) % Cfg::STAGES_B;
   constexpr int NA = Cfg::A_PER_WAVE, NB = Cfg::B_PER_WAVE;
+  constexpr int QE0 = EB ? NA : 0, NE = EB ? NB : NA;  // early loads [QE0, QE0 + NE)
+  constexpr int QL0 = EB ? 0 : NA, NLT = EB ? NA : NB; // late loads
   const Stage cur = stage<Cfg, SA, SB>();
 #pragma unroll
   for (int s = 0; s < SUB - 1; ++s) {
     read_operands<Cfg, BL>(o[(s + 1) & 1], cur, s + 1, wm, wn, lane);
-    // A loads [0, Q1_0) in slice 0, [Q1_0, Q1_1) in slice 1, the rest in
+    // early loads [0, Q1_0) in slice 0, [Q1_0, Q1_1) in slice 1, the rest in
     // slice 2 (front-loaded: the earliest have the longest to land)
-    constexpr int Q1_0 = (NA + SUB - 2) / (SUB - 1);
-    constexpr int Q1_1 = (2 * NA + SUB - 2) / (SUB - 1);
+    constexpr int Q1_0 = QE0 + (NE + SUB - 2) / (SUB - 1);
+    constexpr int Q1_1 = QE0 + (2 * NE + SUB - 2) / (SUB - 1);
     if (s == 0)
-      mfma_step_loads<Cfg, BL, SAN, SB, 0, Q1_0>(f, o[0], ld, kt + 2, nk);
+      mfma_step_loads<Cfg, BL, SAN, SBN, QE0, Q1_0>(f, o[0], ld, kt + 2, nk);
     else if (s == 1)
-      mfma_step_loads<Cfg, BL, SAN, SB, Q1_0, Q1_1>(f, o[1], ld, kt + 2, nk);
+      mfma_step_loads<Cfg, BL, SAN, SBN, Q1_0, Q1_1>(f, o[1], ld, kt + 2, nk);
     else if (s == 2)
-      mfma_step_loads<Cfg, BL, SAN, SB, Q1_1, NA>(f, o[0], ld, kt + 2, nk);
+      mfma_step_loads<Cfg, BL, SAN, SBN, Q1_1, QE0 + NE>(f, o[0], ld, kt + 2, nk);
     else
       mfma_step<Cfg>(f, o[s & 1]);
   }
-  // The A loads of step kt + 2 were issued after step kt + 1's.
-  wait_vmcnt(NA);
+  // The early loads of step kt + 2 were issued after step kt + 1's.
+  wait_vmcnt(NE);
   lds_barrier();
-  read_operands<Cfg, BL>(o[0], stage<Cfg, (SA + 1) % Cfg::STAGES_A, (SB + 1) % Cfg::STAGES>(), 0, wm, wn, lane);
-  mfma_step_loads<Cfg, BL, SAN, SB, NA, NA + NB>(f, o[1], ld, kt + 2, nk);
+  read_operands<Cfg, BL>(o[0], stage<Cfg, (SA + 1) % Cfg::STAGES_A, (SB + 1) % Cfg::STAGES_B>(), 0, wm, wn, lane);
+  mfma_step_loads<Cfg, BL, SAN, SBN, QL0, QL0 + NLT>(f, o[1], ld, kt + 2, nk);
 }
 
 template <class Cfg, int BL, int T>
@@ -837,7 +846,7 @@ __device__ __forceinline__ void gemm_tile(Frag<Cfg>& f, const TileJob& j) {
   // interleaved path every stage is loaded (steps past the end repeat the
   // last step), so that each step has exactly LOADS_PER_WAVE loads behind it.
   const bool il = iload_ok<Cfg, BL>() && j.K % Cfg::BK == 0;   // uniform
-  if constexpr (Cfg::STAGES_A > Cfg::STAGES) {
+  if constexpr (Cfg::STAGES_A > Cfg::STAGES || Cfg::STAGES_B > Cfg::STAGES) {
     if (il) {
       // Steps 0 and 1 into fresh slots, A then B each (the order the steps
       // after them keep); wait for step 0.

@@ -182,8 +182,11 @@ enum CfgId : int { CFG_LARGE = 0, CFG_SMALL = 1, CFG_MID = 2 };
 #ifndef TPF_LARGE_STAGES_A
 #define TPF_LARGE_STAGES_A 3
 #endif
+#ifndef TPF_LARGE_STAGES_B
+#define TPF_LARGE_STAGES_B 0
+#endif
 using CfgLarge = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN, TPF_LARGE_STAGES, TPF_LARGE_BK,
-                         TPF_LARGE_L2PF, TPF_LARGE_PP, TPF_LARGE_PPMODE, 2, TPF_LARGE_STAGES_A>;
+                         TPF_LARGE_L2PF, TPF_LARGE_PP, TPF_LARGE_PPMODE, 2, TPF_LARGE_STAGES_A, TPF_LARGE_STAGES_B>;
 #ifndef TPF_FUSED_STAGES
 #define TPF_FUSED_STAGES 2
 #endif
