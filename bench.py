@@ -144,10 +144,10 @@ def kernel_bytes(wl, part_bytes=4, sched="unfused"):
     return p * (2.0 * M * K + 2.0 * K * N + part_bytes * M * N)
 
 
-def kernel_name(sched, op=""):
+def kernel_name(sched, op="", M=0):
     """The kernel (or, for the fold scheduler, the pair of launches) that
     dominates one step of the scheduler the library ran: what `roofline`
-    prices."""
+    prices (the single-launch path picks its tile kernel by the row count M)."""
     if op.startswith("wgrad"):
         return "tile_kernel A_KM (weight-gradient GEMM tiles, transposed A)"
     if op == "rowpar_dx":
@@ -157,8 +157,13 @@ def kernel_name(sched, op=""):
             return ("tile_kernel pair (FC2: shards 0..p-2 into partials, then shard p-1 with the fold epilogue; "
                     "FC1 with GeLU runs before it)")
         if sched == "stationary":
-            return "stationary_kernel (FC2: every shard of an output tile in one workgroup; FC1 runs before it)"
+            return ("stationary_large_kernel (FC2: every shard of a 128x256 output tile in one workgroup; "
+                    "FC1 runs before it)" if M > 64 else
+                    "stationary_kernel (FC2: every shard of an output tile in one workgroup; FC1 runs before it)")
         return "tile_kernel RED=0 (FC2 shard GEMM tiles; FC1 with GeLU runs before it)"
+    if sched == "stationary" and M > 64:
+        return ("stationary_large_kernel (one launch: each workgroup runs every shard's K loop for its 128x256 "
+                "output tile and keeps the running sum in registers)")
     if sched == "stationary":
         return "stationary_kernel (one launch: each workgroup computes every shard's partial of its output tile and folds them on chip)"
     if sched == "persistent":
@@ -456,7 +461,7 @@ def summarize(wl, res, sched_req, n, msg_bytes, timed_label):
         "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
                      "algorithmic_bytes": comp, "launch_bytes": lbytes, "algorithmic_flops": kflops,
-                     "kernel": kernel_name(ran, wl.op), "avg_kernel_ms": round(avg_kernel_ms, 4),
+                     "kernel": kernel_name(ran, wl.op, wl.M), "avg_kernel_ms": round(avg_kernel_ms, 4),
                      "timed_launches": len(launch_ms) if launch_ms else 0,
                      "avg_step_event_ms": round(res["step_event_ms"], 4)},
     }
@@ -517,8 +522,8 @@ def config_modes(wl, n):
              ("unfused", "unfused", n)]
     if wl.op != "allgather":
         specs.append(("fold", "fold", n))
-    if wl.M <= 64:
         specs.append(("stationary", "stationary", n))
+    if wl.M <= 64:
         for m in (1, 2, 4):
             specs.append((f"persistent_n{m}", "persistent", m))
             specs.append((f"two_stream_n{m}", "two_stream", m))

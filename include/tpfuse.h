@@ -129,18 +129,19 @@ extern "C" {
                                     is its epilogue.  n_chunks is checked but does not change the
                                     schedule.  For M <= 64 (one shard's tiles could not fill the GPU)
                                     and for AllGather->MatMul it runs as TPF_SCHED_UNFUSED. */
-#define TPF_SCHED_STATIONARY 8   /* one launch, output-stationary: each workgroup owns an output tile of
-                                    32 (M <= 32) or 64 rows and 32 columns, computes every shard's fp32
-                                    partial of it (each the same MFMA chain as the partials the other
-                                    schedulers store), and folds them on chip in shard order, rounding
-                                    once: no partial goes to memory, no workspace, no second launch.
-                                    Built for decode-shaped M, where the weights dominate the traffic and
-                                    the tile's small height costs nothing; correct for any M, but slower
-                                    than TPF_SCHED_UNFUSED on the measured shapes (so AUTO does not
-                                    pick it).  For dX
-                                    (weights used transposed) and AllGather->MatMul it runs as
-                                    TPF_SCHED_UNFUSED.  n_chunks is checked but does not change the
-                                    schedule. */
+#define TPF_SCHED_STATIONARY 8   /* one launch, output-stationary: each workgroup owns an output tile,
+                                    runs every shard's GEMM for it (each the same MFMA chain as the
+                                    partials the other schedulers store) and folds the shards' fp32
+                                    results on chip in shard order, rounding once: no partial goes to
+                                    memory, no workspace, no second launch.  M <= 64: tiles of 32 or 64
+                                    rows by 32 columns, the partials folded in LDS, for weights stored
+                                    [K][N] only (dX runs as TPF_SCHED_UNFUSED there).  M > 64: tiles of
+                                    128 x 256 with the running sum in registers, for every reducing
+                                    call including dX.  Same bits as every other scheduler; slower
+                                    than TPF_SCHED_UNFUSED or TPF_SCHED_FOLD on the measured shapes
+                                    (so AUTO does not pick it), but it needs no workspace at all.
+                                    AllGather->MatMul runs as TPF_SCHED_UNFUSED.  n_chunks is checked
+                                    but does not change the schedule. */
 
 /* Message precision, OR-ed into the `sched` argument of the reducing calls
  * (tpf_matmul_allreduce, tpf_matmul_reducescatter, tpf_matmul_dx, and
@@ -187,9 +188,9 @@ int tpf_destroy(tpf_handle h);
  * with TPF_MSG_BF16 in `sched`): one local output [M, N] per shard (N = output
  * width: N for the row-parallel ops, K_in for tpf_matmul_dx), except that
  * TPF_SCHED_STATIONARY needs none for the row-parallel calls and the MLP
- * block (it still needs the full size for tpf_matmul_dx, which it runs
- * unfused).  AUTO asks for the full size, which covers every scheduler it may
- * pick.  `K` is the per-shard reduction length.  AllGather->MatMul needs
+ * block, nor for tpf_matmul_dx with M > 64 (with M <= 64 it runs dX unfused
+ * and needs the full size).  AUTO asks for the full size, which covers every
+ * scheduler it may pick.  `K` is the per-shard reduction length.  AllGather->MatMul needs
  * none.  Returns 0 for invalid arguments. */
 size_t tpf_workspace_size(int op, int p, int64_t M, int64_t N, int64_t K, int n_chunks, int sched);
 

@@ -38,7 +38,7 @@ def hipcc() -> str:
 
 # tpf_kernels.hip is compiled as KERNEL_PARTS translation units (-DTPF_PART=n),
 # in parallel; see the part list at the top of that file.
-KERNEL_PARTS = 8
+KERNEL_PARTS = 9
 
 
 def _compile_jobs(cc: str):

@@ -154,7 +154,7 @@ int check_ptr(const void* ptr, const char* name) {
 // row-parallel calls); with weights used transposed (dX) it runs as
 // TPF_SCHED_UNFUSED and needs the full workspace.
 size_t partial_bytes(int p, int64_t M, int64_t N, int sched, bool weights_kn = false) {
-  if ((sched & 0xff) == TPF_SCHED_STATIONARY && weights_kn) return 0;
+  if ((sched & 0xff) == TPF_SCHED_STATIONARY && (weights_kn || pick_cfg(M) == CFG_LARGE)) return 0;
   return (size_t)p * (size_t)M * (size_t)N * (msg_bf16(sched) ? 2 : 4);
 }
 
@@ -312,7 +312,7 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
   if (sched == TPF_SCHED_FOLD && cfg != CFG_LARGE) sched = TPF_SCHED_UNFUSED;
   // The single launch streams weights stored [K][N]; dX's transposed weights
   // run GEMM-then-reduce (the same bits).
-  if (sched == TPF_SCHED_STATIONARY && rc.bl != B_KN) sched = TPF_SCHED_UNFUSED;
+  if (sched == TPF_SCHED_STATIONARY && rc.bl != B_KN && cfg != CFG_LARGE) sched = TPF_SCHED_UNFUSED;
   h->last_sched = sched;
   switch (sched) {
     case TPF_SCHED_GEMM_ONLY:
@@ -369,6 +369,13 @@ int run_reduce_call(tpf_handle h, const ReduceCall& rc, hipStream_t stream) {
       TPF_TIMED(h, stream, launch_fold(cfg, rc.bl, g, rc.ro, rc.P, stride, rc.p, 0, rc.M, rc.N, stream));
       return TPF_OK;
     case TPF_SCHED_STATIONARY: {
+      if (cfg == CFG_LARGE) {
+        StatLargeArgs a{};
+        a.g = g;
+        a.ro = rc.ro;
+        TPF_TIMED(h, stream, launch_stationary_large(rc.bl, a, stream));
+        return TPF_OK;
+      }
       StationaryArgs a{};
       for (int k = 0; k < rc.p; ++k) {
         a.A[k] = g.A[k];

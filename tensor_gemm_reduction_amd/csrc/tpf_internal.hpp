@@ -196,6 +196,13 @@ using CfgLarge = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN,
 #ifndef TPF_FUSED_STAGES_A
 #define TPF_FUSED_STAGES_A 3
 #endif
+// Output-stationary large tiles: 128 x 256 (wave tiles of 64 x 64), so that
+// the running sum over the shards and the current shard's accumulators both
+// stay in registers; A has the third LDS slot (3 x 16 + 2 x 32 KiB).
+#ifndef TPF_STL_CFG
+#define TPF_STL_CFG TileCfg<128, 256, 2, 4, 2, 64, 0, 0, 0, 2, 3>
+#endif
+using CfgStatLarge = TPF_STL_CFG;
 using CfgLargeFused = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN, TPF_FUSED_STAGES,
                               TPF_FUSED_BK, TPF_FUSED_L2PF, TPF_LARGE_PP, TPF_LARGE_PPMODE, 2, TPF_FUSED_STAGES_A>;
 #ifndef TPF_SMALL_BM
@@ -244,5 +251,15 @@ hipError_t launch_clear_status(Ctrl* c, hipStream_t s);
 // (the launcher sets the tile grid from the tile shape it picks for M and p).
 struct StationaryArgs;
 hipError_t launch_stationary(const StationaryArgs& a, int pbf16, int out, hipStream_t s);
+// Output-stationary single launch with large tiles (more than 64 rows): one
+// workgroup per 128 x 256 output tile runs every shard's K loop and keeps the
+// running sum over the shards in registers (g: the p shards' operands, N the
+// output width; ro: the AllReduce or ReduceScatter destination).
+struct StatLargeArgs {
+  GemmOperands g;
+  ReduceOut ro;
+  int tiles_m, tiles_n;
+};
+hipError_t launch_stationary_large(int bl, const StatLargeArgs& a, hipStream_t s);
 
 }  // namespace tpf

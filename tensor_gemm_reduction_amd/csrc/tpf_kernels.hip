@@ -27,12 +27,13 @@
 #include "tpf_stationary.hpp"
 
 // The launchers are split into parts so that the build can compile them as
-// separate translation units in parallel (-DTPF_PART=n, n = 0..7); without
+// separate translation units in parallel (-DTPF_PART=n, n = 0..8); without
 // TPF_PART every part is compiled.
 //   0: reductions, copies, status, dispatch      1: persistent kernel, large tiles
 //   2: large tiles (plain, tile scheduler)        3: fold epilogue, fp32 messages
 //   4: decode-shaped (small and mid) tiles        5: persistent kernel, small and mid tiles
-//   6: fold epilogue, bf16 messages               7: output-stationary single launch
+//   6: fold epilogue, bf16 messages               7: output-stationary single launch (decode)
+//   8: output-stationary single launch (large tiles)
 #ifdef TPF_PART
 #define TPF_IN_PART(n) (TPF_PART == (n))
 #else
@@ -836,6 +837,118 @@ hipError_t launch_stationary(const StationaryArgs& a, int pbf16, int out, hipStr
                                            : launch_st_cfg<StSmallAnyP>(a, pbf16, out, s);
   return a.p <= st_max_shards<StMid>() ? launch_st_cfg<StMid>(a, pbf16, out, s)
                                        : launch_st_cfg<StMidAnyP>(a, pbf16, out, s);
+}
+#endif
+
+// ---------------------------------------------------------------------------
+// Output-stationary single launch, large tiles (part 8)
+// ---------------------------------------------------------------------------
+// One workgroup per 128 x 256 output tile, in the shard GEMMs' grouped,
+// XCD-aware tile order.  For k = 0 .. p-1 it runs shard k's K loop (the same
+// MFMA chain from a zero accumulator as every other path, so the result is
+// the partial shard k would send, rounded to bf16 first for 2-byte messages)
+// and folds it into a running sum kept in registers: S = P_0, then
+// S = S + P_k in shard order -- the reduction kernel's additions in its
+// order.  The sum is rounded once and stored to the AllReduce or
+// ReduceScatter destination.  No partial goes to memory and no second
+// launch follows; the price is a smaller tile (128 x 256 instead of
+// 256 x 256: half the MFMAs per loaded byte), which the two accumulator sets
+// need to fit the register file.
+#if TPF_IN_PART(8)
+template <class Cfg, int OUT>
+__device__ __forceinline__ void store_sum(const Frag<Cfg>& s, const TileJob& j, const ReduceOut& ro) {
+  if (!ro.scatter) {
+    store_tile<Cfg, OUT>(s, j, ro.y[0], j.N);
+    return;
+  }
+  const int rps = ro.rows_per_slice;
+  const int sl = j.m0 / rps;
+  if ((j.m0 + j.rows - 1) / rps == sl) {   // the tile lies in one slice (uniform)
+    TileJob js = j;
+    js.m0 = j.m0 - sl * rps;
+    store_tile<Cfg, OUT>(s, js, ro.y[sl], j.N);
+    return;
+  }
+  // a tile that straddles two slices: element by element
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+  const int r32 = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < Cfg::TN; ++jn) {
+      const int col = j.n0 + wn * Cfg::WN + jn * 32 + r32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * Cfg::WM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (row < j.rows && col < j.N) {
+          const int gr = j.m0 + row, r_sl = gr / rps;
+          const int64_t off = (int64_t)(gr - r_sl * rps) * j.N + col;
+          if constexpr (OUT == OUT_F32)
+            reinterpret_cast<float*>(ro.y[r_sl])[off] = s.acc[i][jn][v];
+          else
+            reinterpret_cast<uint16_t*>(ro.y[r_sl])[off] = (uint16_t)f32_to_bf16_bits(s.acc[i][jn][v]);
+        }
+      }
+    }
+}
+
+template <class Cfg, int BL, int PB, int OUT>
+__global__ __launch_bounds__(Cfg::THREADS) void stationary_large_kernel(StatLargeArgs args) {
+  (void)args;
+  const StatLargeArgs& a = kernarg<StatLargeArgs>();
+  const int u = xcd_task(blockIdx.x, a.tiles_m * a.tiles_n);
+  int shard, tm, tn;
+  tile_coords(u, a.tiles_m, a.tiles_n, shard, tm, tn);   // shard = 0: one grid of output tiles
+  // The running sum starts at -0, the identity of fp32 addition for every
+  // value (also -0 itself), so after shard 0 it holds P_0 bit for bit.
+  Frag<Cfg> s;
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < Cfg::TN; ++jn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s.acc[i][jn][v] = -0.0f;
+  const TileJob j0 = make_job<Cfg>(a.g, 0, 0, a.g.M, tm, tn);
+  for (int k = 0; k < a.g.nshard; ++k) {
+    TileJob j = j0;
+    j.A = a.g.A[k];
+    j.B = a.g.B[k];
+    Frag<Cfg> f;
+    gemm_tile<Cfg, BL>(f, j);
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+      for (int jn = 0; jn < Cfg::TN; ++jn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s.acc[i][jn][v] += message_value<PB>(f.acc[i][jn][v]);
+  }
+  store_sum<Cfg, OUT>(s, j0, a.ro);
+}
+
+template <class Cfg, int BL>
+static void launch_stl(const StatLargeArgs& a, int grid, hipStream_t s) {
+  const dim3 g((unsigned)grid), b(Cfg::THREADS);
+  if (a.ro.pbf16) {
+    if (a.ro.dtype == OUT_F32) hipLaunchKernelGGL((stationary_large_kernel<Cfg, BL, 1, OUT_F32>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((stationary_large_kernel<Cfg, BL, 1, OUT_BF16>), g, b, 0, s, a);
+  } else {
+    if (a.ro.dtype == OUT_F32) hipLaunchKernelGGL((stationary_large_kernel<Cfg, BL, 0, OUT_F32>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((stationary_large_kernel<Cfg, BL, 0, OUT_BF16>), g, b, 0, s, a);
+  }
+}
+
+hipError_t launch_stationary_large(int bl, const StatLargeArgs& a0, hipStream_t s) {
+  StatLargeArgs a = a0;
+  if (a.g.nshard < 1 || a.g.nshard > kMaxShards || a.g.M <= 0 || a.g.N <= 0) return hipErrorInvalidValue;
+  a.tiles_m = (a.g.M + CfgStatLarge::BM - 1) / CfgStatLarge::BM;
+  a.tiles_n = (a.g.N + CfgStatLarge::BN - 1) / CfgStatLarge::BN;
+  const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  if (bl == B_KN) launch_stl<CfgStatLarge, B_KN>(a, (int)grid, s);
+  else if (bl == B_NK) launch_stl<CfgStatLarge, B_NK>(a, (int)grid, s);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 #endif
 

@@ -81,6 +81,9 @@ def test_workspace_size():
     assert ws(tp.OP_MATMUL_REDUCESCATTER, 8, 64, 8192, 1024, 2, "stationary", "bf16") == 0
     assert ws(tp.OP_MLP_SP, 8, 64, 8192, 1024, 1, "stationary") == 0
     assert ws(tp.OP_MATMUL_DX, 8, 64, 1024, 512, 1, "stationary") == 8 * 64 * 1024 * 4
+    # with more than 64 rows every reducing call (dX too) runs the large-tile single launch
+    assert ws(tp.OP_MATMUL_DX, 8, 65, 1024, 512, 1, "stationary") == 0
+    assert ws(tp.OP_MATMUL_ALLREDUCE, 4, 8192, 8192, 7168, 1, "stationary") == 0
     assert ws(tp.OP_MATMUL_ALLREDUCE, 8, 16, 8192, 1024, 1, "auto") == 8 * 16 * 8192 * 4
     assert ws(tp.OP_MATMUL_ALLREDUCE, 4, 64, 64, 64, 1, "fold") == 4 * 64 * 64 * 4
 

@@ -46,7 +46,7 @@ def test_allreduce_kstep(K):
     ref = O.matmul_allreduce(bits(Xh), bits(Wh))
     X, W = [t.to(DEV) for t in Xh], [t.to(DEV) for t in Wh]
     outs = {}
-    for sched in ("unfused", "fold", "tile", "persistent", "two_stream"):
+    for sched in ("unfused", "fold", "tile", "persistent", "two_stream", "stationary"):
         y = tp.matmul_allreduce(X, W, torch.float32, n_chunks=2, sched=sched)
         torch.cuda.synchronize()
         exact(y, ref, f"allreduce K={K} {sched}")
@@ -66,7 +66,7 @@ def test_dx_kstep(K):
     ref = O.matmul_dx(bits(dYh), bits(Wh))
     dY, W = [t.to(DEV) for t in dYh], [t.to(DEV) for t in Wh]
     outs = {}
-    for sched in ("unfused", "fold", "persistent"):
+    for sched in ("unfused", "fold", "persistent", "stationary"):
         y = tp.matmul_dx(dY, W, tp.ALLREDUCE, torch.float32, n_chunks=2, sched=sched)
         torch.cuda.synchronize()
         exact(y, ref, f"dx K={K} {sched}")
