@@ -535,7 +535,8 @@ def test_mlp_sp_parity(p, S, Hd, F):
 # MatMul -> ReduceScatter
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("p,M,N,K", [(4, 512, 264, 136), (8, 1024, 328, 72), (2, 64, 136, 264)])
+@pytest.mark.parametrize("p,M,N,K", [(4, 512, 264, 136), (8, 1024, 328, 72), (2, 64, 136, 264),
+                                     (3, 576, 264, 136)])   # 192-row slices: some tiles straddle two
 def test_reducescatter_parity(p, M, N, K):
     say(f"reducescatter p={p} M={M} N={N} K={K}")
     Xh = shards([(M, K)] * p, ("normal", 1.0), 51)
