@@ -46,17 +46,9 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset that is always out of range (operands < 2 GiB)
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int BK_ = 64, int L2PF_ = 1, int PP_ = 0,
-          int PPMODE_ = 0, int SWB_ = 2, int STAGES_A_ = 0, int STAGES_B_ = 0>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int BK_ = 64, int SWB_ = 2, int STAGES_A_ = 0,
+          int STAGES_B_ = 0>
 struct TileCfg {
-  // PP: ping-pong schedule (two wave groups one barrier phase apart; only
-  // group 0 issues global loads).  PPMODE selects how waves form the groups:
-  // 0: group = wave / (NW/2), 1: group = wave % 2.
-  static constexpr int PP = PP_;
-  static constexpr int PPMODE = PPMODE_;
-  // L2PF > 0: every K step also touches each 128-byte line of step
-  // (issued step + L2PF), so that step's LDS loads later hit in L2.
-  static constexpr int L2PF = L2PF_;
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
   static constexpr int KCH = BK / 8;              // 16-byte chunks per A row
@@ -83,18 +75,14 @@ struct TileCfg {
   static constexpr int LDS_BYTES = STAGES_A * LDS_A + STAGES_B * LDS_B;
   static constexpr int A_INSTR = LDS_A / 1024;   // 1 KiB load instructions per A tile
   static constexpr int B_INSTR = LDS_B / 1024;
-  static constexpr int NLW = PP ? NW / 2 : NW;      // waves that issue global loads
-  static_assert(A_INSTR % NLW == 0 && B_INSTR % NLW == 0, "loads must split evenly over waves");
-  static constexpr int A_PER_WAVE = A_INSTR / NLW;
-  static constexpr int B_PER_WAVE = B_INSTR / NLW;
-  static constexpr int TOUCH_LINES = (BM * BK * 2 + BN * BK * 2) / 128;
-  static constexpr int TOUCH_PER_WAVE = L2PF > 0 ? (TOUCH_LINES + THREADS - 1) / THREADS : 0;
-  static constexpr int LOADS_PER_WAVE = A_PER_WAVE + B_PER_WAVE + TOUCH_PER_WAVE;
+  static_assert(A_INSTR % NW == 0 && B_INSTR % NW == 0, "loads must split evenly over waves");
+  static constexpr int A_PER_WAVE = A_INSTR / NW;
+  static constexpr int B_PER_WAVE = B_INSTR / NW;
+  static constexpr int LOADS_PER_WAVE = A_PER_WAVE + B_PER_WAVE;
   static_assert(BN >= 128 && 1024 % (BN * 2 > 1024 ? 1024 : BN * 2) == 0 && (BN * 2) % 256 == 0,
                 "KN rows hold >= 8 swizzled 32-byte blocks and tile 1 KiB");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert((STAGES - 2) * LOADS_PER_WAVE + TOUCH_PER_WAVE <= 63, "vmcnt range");
-  static_assert(L2PF == 0 || (BK == 64 && BM % 64 == 0 && !PP), "line touches: 128-byte A rows, A/B split on a wave");
+  static_assert((STAGES - 2) * LOADS_PER_WAVE <= 63, "vmcnt range");
   // A stored [K][M] (transposed A) uses the KN-style layout: rows of BM
   // elements that tile 1 KiB.
   static constexpr bool KM_OK = BM >= 128 && (BM * 2) % 256 == 0 && 1024 % (BM * 2 > 1024 ? 1024 : BM * 2) == 0;
@@ -198,12 +186,9 @@ struct TileLoader {
   int K;
   uint32_t ldb_bytes;
   uint32_t lda_bytes;
-  // L2 touch: this lane's line (A row, or B row segment) at k0 = 0.
-  uint32_t t_off[Cfg::TOUCH_PER_WAVE > 0 ? Cfg::TOUCH_PER_WAVE : 1];
-  int t_isb[Cfg::TOUCH_PER_WAVE > 0 ? Cfg::TOUCH_PER_WAVE : 1];
 
   __device__ __forceinline__ void init(const TileJob& j) {
-    const int wave = loader_wave(), lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     K = j.K;
     ldb_bytes = (uint32_t)(j.ldb * 2);
     lda_bytes = (uint32_t)(j.lda * 2);
@@ -253,63 +238,8 @@ struct TileLoader {
         b_off[i] = gn < j.N ? (uint32_t)(((int64_t)k * j.ldb + gn) * 2) : kOOB;
       }
     }
-#pragma unroll
-    for (int i = 0; i < Cfg::TOUCH_PER_WAVE; ++i) {
-      const int line = threadIdx.x + i * Cfg::THREADS;
-      uint32_t off = kOOB;
-      int isb = 0;
-      if (line < Cfg::BM) {                       // A row `line`, 64 k = 128 bytes
-        const int gm = j.m0 + line;
-        if (!a_trans(BL) && gm < j.a_rows) off = (uint32_t)((int64_t)gm * j.lda * 2);
-      } else if (line < Cfg::TOUCH_LINES) {
-        const int bl = line - Cfg::BM;
-        isb = 1;
-        if constexpr (b_layout(BL) == B_NK) {     // B row n, 64 k = 128 bytes
-          const int gn = j.n0 + bl;
-          if (gn < j.b_rows) off = (uint32_t)((int64_t)gn * j.ldb * 2);
-        } else {                                  // B row k, segment of 64 n
-          constexpr int SEGS = Cfg::BN / 64;
-          const int k = bl / SEGS, gn = j.n0 + (bl % SEGS) * 64;
-          if (gn < j.N) off = (uint32_t)(((int64_t)k * j.ldb + gn) * 2);
-        }
-      }
-      t_off[i] = off;
-      t_isb[i] = isb;
-    }
   }
 
-  // Touch every line of the K step starting at k0 (4 bytes per lane into an
-  // LDS scratch that is never read) so that the step's later loads hit L2.
-  __device__ __forceinline__ void touch(char* scratch, int k0) const {
-    const int wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i < Cfg::TOUCH_PER_WAVE; ++i) {
-      uint32_t off = t_off[i];
-      if (off != kOOB) {
-        if (t_isb[i] && b_layout(BL) == B_KN)
-          off += (uint32_t)k0 * ldb_bytes;
-        else
-          off += (uint32_t)k0 * 2;
-      }
-      // A and B lines are split on a wave boundary (BM is a multiple of 64),
-      // so the operand choice is wave-uniform: select the resource in SGPRs.
-      if (__builtin_amdgcn_readfirstlane(t_isb[i]))
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(scratch + (i * Cfg::NW + wave) * 256), 4, off, 0, 0,
-                                                 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(scratch + (i * Cfg::NW + wave) * 256), 4, off, 0, 0,
-                                                 0);
-    }
-  }
-
-  // Issue the loads of K step starting at k0 into `stage`.
-  // Index of this wave among the waves that issue global loads.
-  __device__ __forceinline__ static int loader_wave() {
-    const int w = threadIdx.x >> 6;
-    if constexpr (!Cfg::PP) return w;
-    else if constexpr (Cfg::PPMODE == 0) return w;   // group 0 = waves 0 .. NW/2-1
-    else return w >> 1;                             // group 0 = even waves
-  }
 
   // Logical k chunk (A, NK B) of this lane's i-th A or B load, or (KN B) its
   // k row within the step.  Only the K tail step needs them, so they are
@@ -332,7 +262,7 @@ struct TileLoader {
   }
 
   __device__ __forceinline__ void issue(Stage st, int k0) const {
-    const int wave = loader_wave(), lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     char* la = st.a;
     char* lb = st.b;
     const bool tail = k0 + Cfg::BK > K;   // the same for the whole workgroup
@@ -495,28 +425,18 @@ __device__ __forceinline__ char* stage_ptr() {
   return a_slot<Cfg, S>();
 }
 
-template <class Cfg>
-__device__ __forceinline__ char* touch_scratch() {
-  __shared__ __attribute__((aligned(256))) char buf[Cfg::TOUCH_PER_WAVE > 0 ? Cfg::TOUCH_PER_WAVE * Cfg::THREADS * 4 : 4];
-  return buf;
-}
-
-// Loads of K step `step` into stage S, plus (L2PF > 0) the L2 touch of step
-// step + L2PF.  Every wave issues exactly LOADS_PER_WAVE vector-memory
-// instructions per call, so vmcnt arithmetic stays per-step.
+// Loads of K step `step` into stage S.  Every wave issues exactly
+// LOADS_PER_WAVE vector-memory instructions per call, so vmcnt arithmetic
+// stays per-step.
 template <class Cfg, int BL, int S>
-__device__ __forceinline__ void issue_stage(const TileLoader<Cfg, BL>& ld, int step, int nk) {
+__device__ __forceinline__ void issue_stage(const TileLoader<Cfg, BL>& ld, int step) {
   ld.issue(stage<Cfg, S>(), step * Cfg::BK);
-  if constexpr (Cfg::L2PF > 0) {
-    const int ts = step + Cfg::L2PF;
-    ld.touch(touch_scratch<Cfg>(), (ts < nk ? ts : nk - 1) * Cfg::BK);
-  }
 }
 
 template <class Cfg, int BL, int S>
 __device__ __forceinline__ void prefetch(const TileLoader<Cfg, BL>& ld, int nk) {
   if constexpr (S < Cfg::STAGES - 1) {
-    if (S < nk) issue_stage<Cfg, BL, S>(ld, S, nk);
+    if (S < nk) issue_stage<Cfg, BL, S>(ld, S);
     prefetch<Cfg, BL, S + 1>(ld, nk);
   }
 }
@@ -535,28 +455,22 @@ __device__ __forceinline__ void prefetch_all(const TileLoader<Cfg, BL>& ld, int 
 // step up to min(t + STAGES - 2, nk - 1) has been issued.
 template <class Cfg>
 __device__ __forceinline__ void wait_step(int t, int nk) {
-  wait_vmcnt(min(Cfg::STAGES - 2, nk - 1 - t) * Cfg::LOADS_PER_WAVE + Cfg::TOUCH_PER_WAVE);
+  wait_vmcnt(min(Cfg::STAGES - 2, nk - 1 - t) * Cfg::LOADS_PER_WAVE);
 }
 
-// Loads interleaved with the MFMAs: large two-stage tiles without line
-// touches or the ping-pong schedule, when K is a multiple of BK.  (The
-// decode-sized tiles measured 2 % slower with it: one MFMA per slice leaves
-// nothing to interleave with.)
+// Loads interleaved with the MFMAs: large two-stage tiles, when K is a
+// multiple of BK.  (The decode-sized tiles measured 2 % slower with it: one
+// MFMA per slice leaves nothing to interleave with.)
 #ifndef TPF_ILOAD
 #define TPF_ILOAD 1
 #endif
 
 template <class Cfg, int BL>
 __device__ __forceinline__ constexpr bool iload_ok() {
-  return TPF_ILOAD && !Cfg::PP && Cfg::BM >= 128 && Cfg::L2PF == 0;
+  return TPF_ILOAD && Cfg::BM >= 128;
 }
 
-
-
-// Loads of one K step on the interleaved path are numbered q = 0 .. NL-1;
-// IL_BFIRST puts the B tile's loads first.  IL_LATE of them (the last ones)
-// are issued in the first k slice of the next step instead of right after
-// the barrier.
+// Loads of one K step on the interleaved path are numbered q = 0 .. NL-1.
 
 // Scalar offsets of step kn (clamped to the last step) and its load q into
 // stage S.
@@ -637,7 +551,7 @@ __device__ __forceinline__ void kstep(Frag<Cfg>& f, const TileLoader<Cfg, BL>& l
   if (kt + 1 < nk) {
     wait_step<Cfg>(kt + 1, nk);
     lds_barrier();
-    if (kt + Cfg::STAGES < nk) issue_stage<Cfg, BL, S>(ld, kt + Cfg::STAGES, nk);
+    if (kt + Cfg::STAGES < nk) issue_stage<Cfg, BL, S>(ld, kt + Cfg::STAGES);
     read_operands<Cfg, BL>(o[0], stage<Cfg, (S + 1) % Cfg::STAGES>(), 0, wm, wn, lane);
   }
   mfma_step<Cfg>(f, o[1]);
@@ -679,7 +593,7 @@ __device__ __forceinline__ void kstep_ila(Frag<Cfg>& f, const TileLoader<Cfg, BL
                                           int nk, int wm, int wn, int lane) {
   constexpr int SUB = Cfg::BK / 16;
   static_assert(SUB % 2 == 0, "even number of k slices per step");
-  static_assert(Cfg::STAGES == 2 && Cfg::STAGES_A + Cfg::STAGES_B == 5 && Cfg::L2PF == 0,
+  static_assert(Cfg::STAGES == 2 && Cfg::STAGES_A + Cfg::STAGES_B == 5,
                 "two slots for one operand, three for the other");
   constexpr bool EB = Cfg::STAGES_B > Cfg::STAGES;     // B is the early operand
   constexpr int SA = T % Cfg::STAGES_A, SB = T % Cfg::STAGES_B;
@@ -735,100 +649,10 @@ __device__ __forceinline__ void ksteps(Frag<Cfg>& f, const TileLoader<Cfg, BL>& 
   }
 }
 
-// ---------------------------------------------------------------------------
-// Ping-pong schedule.  The waves form two groups, paired so that each SIMD
-// runs one wave of each.  Group 1 starts one barrier phase behind group 0,
-// and every wave alternates
-//   M(t): read all fragments of step t from LDS  (group 0 also issues the
-//         global loads of step t + STAGES - 1)
-//   C(t): the MFMAs of step t from registers     (group 0 then waits for its
-//         loads of step t + 1)
-// with a workgroup barrier after each phase.  While one wave of a SIMD is in
-// C, the other is in M, so the matrix core is fed back to back.  Stage t is
-// read by group 0 in phase 2t and by group 1 in phase 2t+1, so its refill
-// (step t + STAGES) is issued in group 0's M(t+1), phase 2t+2.
-// ---------------------------------------------------------------------------
-template <class Cfg>
-__device__ __forceinline__ int pp_group(int wave) {
-  if constexpr (Cfg::PPMODE == 0) return wave >= Cfg::NW / 2 ? 1 : 0;
-  else return wave & 1;
-}
-
-template <class Cfg, int BL, int S>
-__device__ __forceinline__ void pp_step(Frag<Cfg>& f, const TileLoader<Cfg, BL>& ld, int grp, int t, int nk, int wm,
-                                        int wn, int lane) {
-  constexpr int SUB = Cfg::BK / 16;
-  Operands<Cfg> o[SUB];
-  // ---- M(t)
-  if (grp == 0) {
-    constexpr int SL = (S + Cfg::STAGES - 1) % Cfg::STAGES;   // stage of step t-1 (== step t+STAGES-1)
-    if (t + Cfg::STAGES - 1 < nk) ld.issue(stage<Cfg, SL>(), (t + Cfg::STAGES - 1) * Cfg::BK);
-  }
-  const Stage cur = stage<Cfg, S>();
-#pragma unroll
-  for (int s = 0; s < SUB; ++s) read_operands<Cfg, BL>(o[s], cur, s, wm, wn, lane);
-  __syncthreads();
-  // ---- C(t)
-#pragma unroll
-  for (int s = 0; s < SUB; ++s) mfma_step<Cfg>(f, o[s]);
-  if (grp == 0 && t + 1 < nk) {
-    // loads issued after step t+1's: steps t+2 .. min(t+STAGES-1, nk-1)
-    wait_vmcnt(min(Cfg::STAGES - 2, nk - 2 - t) * Cfg::LOADS_PER_WAVE);
-  }
-  __syncthreads();
-}
-
-template <class Cfg, int BL, int S>
-__device__ __forceinline__ void pp_steps(Frag<Cfg>& f, const TileLoader<Cfg, BL>& ld, int grp, int t, int nk, int wm,
-                                         int wn, int lane) {
-  if constexpr (S < Cfg::STAGES) {
-    if (t + S < nk) {
-      pp_step<Cfg, BL, S>(f, ld, grp, t + S, nk, wm, wn, lane);
-      pp_steps<Cfg, BL, S + 1>(f, ld, grp, t, nk, wm, wn, lane);
-    }
-  }
-}
-
-template <class Cfg, int BL, int S>
-__device__ __forceinline__ void pp_prefetch(const TileLoader<Cfg, BL>& ld, int nk) {
-  if constexpr (S < Cfg::STAGES - 1) {
-    if (S < nk) ld.issue(stage<Cfg, S>(), S * Cfg::BK);
-    pp_prefetch<Cfg, BL, S + 1>(ld, nk);
-  }
-}
-
-template <class Cfg, int BL>
-__device__ __forceinline__ void gemm_tile_pp(Frag<Cfg>& f, const TileJob& j) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
-  const int grp = pp_group<Cfg>(wave);
-#pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i)
-#pragma unroll
-    for (int jn = 0; jn < Cfg::TN; ++jn)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) f.acc[i][jn][v] = 0.0f;
-  const int nk = (j.K + Cfg::BK - 1) / Cfg::BK;
-  TileLoader<Cfg, BL> ld;
-  if (grp == 0) {
-    ld.init(j);
-    pp_prefetch<Cfg, BL, 0>(ld, nk);
-    wait_vmcnt(min(Cfg::STAGES - 2, nk - 1) * Cfg::LOADS_PER_WAVE);
-  }
-  __syncthreads();                 // step 0 has landed
-  if (grp == 1) __syncthreads();   // group 1 starts one phase behind
-  for (int t = 0; t < nk; t += Cfg::STAGES) pp_steps<Cfg, BL, 0>(f, ld, grp, t, nk, wm, wn, lane);
-  if (grp == 0) __syncthreads();   // match group 1's phase count
-}
-
 // Full K loop of one tile into registers.  Ends with a barrier, so the
 // caller may reuse the stages (e.g. stage 0's first word) immediately.
 template <class Cfg, int BL>
 __device__ __forceinline__ void gemm_tile(Frag<Cfg>& f, const TileJob& j) {
-  if constexpr (Cfg::PP) {
-    gemm_tile_pp<Cfg, BL>(f, j);
-    return;
-  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
 #pragma unroll
@@ -872,7 +696,7 @@ __device__ __forceinline__ void gemm_tile(Frag<Cfg>& f, const TileJob& j) {
     prefetch<Cfg, BL, 0>(ld, nk);
     wait_step<Cfg>(0, nk);
     __syncthreads();
-    if (Cfg::STAGES - 1 < nk) issue_stage<Cfg, BL, Cfg::STAGES - 1>(ld, Cfg::STAGES - 1, nk);
+    if (Cfg::STAGES - 1 < nk) issue_stage<Cfg, BL, Cfg::STAGES - 1>(ld, Cfg::STAGES - 1);
   }
   Operands<Cfg> o[2];
   read_operands<Cfg, BL>(o[0], stage<Cfg, 0>(), 0, wm, wn, lane);

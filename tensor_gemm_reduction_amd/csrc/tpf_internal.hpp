@@ -148,18 +148,6 @@ enum CfgId : int { CFG_LARGE = 0, CFG_SMALL = 1, CFG_MID = 2 };
 #ifndef TPF_LARGE_BK
 #define TPF_LARGE_BK 64
 #endif
-#ifndef TPF_LARGE_L2PF
-#define TPF_LARGE_L2PF 0
-#endif
-#ifndef TPF_FUSED_L2PF
-#define TPF_FUSED_L2PF 0
-#endif
-#ifndef TPF_LARGE_PP
-#define TPF_LARGE_PP 0
-#endif
-#ifndef TPF_LARGE_PPMODE
-#define TPF_LARGE_PPMODE 0
-#endif
 #ifndef TPF_LARGE_WN
 #define TPF_LARGE_WN 4
 #endif
@@ -176,17 +164,17 @@ enum CfgId : int { CFG_LARGE = 0, CFG_SMALL = 1, CFG_MID = 2 };
 // one more LDS slot than B (3 x 32 KiB + 2 x 32 KiB = the whole 160 KiB):
 // each step's A loads then go out during the MFMAs before the barrier
 // (measured 3-7 % faster than two slots each, and the persistent kernel
-// 5-14 % faster than with two slots and the L2 line touch it used before).
-// Neither uses the L2 line touch any more (TileCfg's L2PF; an extra load
-// instruction per step measured 8-12 % slower with interleaved loads).
+// 5-14 % faster than with two slots and an L2 line touch of a later step,
+// which cost one extra load instruction per step: 8-12 % slower with the
+// interleaved loads).
 #ifndef TPF_LARGE_STAGES_A
 #define TPF_LARGE_STAGES_A 3
 #endif
 #ifndef TPF_LARGE_STAGES_B
 #define TPF_LARGE_STAGES_B 0
 #endif
-using CfgLarge = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN, TPF_LARGE_STAGES, TPF_LARGE_BK,
-                         TPF_LARGE_L2PF, TPF_LARGE_PP, TPF_LARGE_PPMODE, 2, TPF_LARGE_STAGES_A, TPF_LARGE_STAGES_B>;
+using CfgLarge = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN, TPF_LARGE_STAGES, TPF_LARGE_BK, 2,
+                         TPF_LARGE_STAGES_A, TPF_LARGE_STAGES_B>;
 #ifndef TPF_FUSED_STAGES
 #define TPF_FUSED_STAGES 2
 #endif
@@ -200,11 +188,11 @@ using CfgLarge = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN,
 // the running sum over the shards and the current shard's accumulators both
 // stay in registers; A has the third LDS slot (3 x 16 + 2 x 32 KiB).
 #ifndef TPF_STL_CFG
-#define TPF_STL_CFG TileCfg<128, 256, 2, 4, 2, 64, 0, 0, 0, 2, 3>
+#define TPF_STL_CFG TileCfg<128, 256, 2, 4, 2, 64, 2, 3>
 #endif
 using CfgStatLarge = TPF_STL_CFG;
 using CfgLargeFused = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARGE_WN, TPF_FUSED_STAGES,
-                              TPF_FUSED_BK, TPF_FUSED_L2PF, TPF_LARGE_PP, TPF_LARGE_PPMODE, 2, TPF_FUSED_STAGES_A>;
+                              TPF_FUSED_BK, 2, TPF_FUSED_STAGES_A>;
 #ifndef TPF_SMALL_BM
 #define TPF_SMALL_BM 32
 #endif
@@ -220,11 +208,11 @@ using CfgLargeFused = TileCfg<TPF_LARGE_BM, TPF_LARGE_BN, TPF_LARGE_WM, TPF_LARG
 //             and were 25 % slower);
 //   M <= 64:  64 x 256 tiles, 3 stages of 40 KiB: each weight tile is read by
 //             one workgroup instead of two (47 % -> 61 % of HBM bandwidth at M = 64).
-using CfgSmall = TileCfg<TPF_SMALL_BM, TPF_SMALL_BN, 1, 4, TPF_SMALL_STAGES, 64, 0>;
+using CfgSmall = TileCfg<TPF_SMALL_BM, TPF_SMALL_BN, 1, 4, TPF_SMALL_STAGES, 64>;
 #ifndef TPF_MID_STAGES
 #define TPF_MID_STAGES 3
 #endif
-using CfgMid = TileCfg<64, 256, 1, 4, TPF_MID_STAGES, 64, 0>;
+using CfgMid = TileCfg<64, 256, 1, 4, TPF_MID_STAGES, 64>;
 
 int cfg_bm(int cfg);
 int cfg_bn(int cfg);
