@@ -69,10 +69,12 @@ __device__ __forceinline__ void reduce_store4(const ReduceOut& o, int64_t e, int
   void* base;
   int64_t off;
   if (o.scatter) {
-    const int64_t row = e / N;
-    const int sl = (int)(row / o.rows_per_slice);
+    // Outputs hold fewer than 2^29 elements (each fp32 partial is below
+    // 2 GiB), so one 32-bit division finds the slice.
+    const uint32_t slice = (uint32_t)o.rows_per_slice * (uint32_t)N;
+    const uint32_t sl = (uint32_t)e / slice;
     base = o.y[sl];
-    off = e - (int64_t)sl * o.rows_per_slice * N;
+    off = (int64_t)((uint32_t)e - sl * slice);
   } else {
     base = o.y[0];
     off = e;
