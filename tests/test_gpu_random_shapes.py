@@ -50,7 +50,8 @@ def big_cases(seed, count):
         yield pytest.param(op, p, M, N, K, n, rng.randint(0, 1 << 30), id=f"big{seed}-{i}-{op}-p{p}-M{M}-N{N}-K{K}-n{n}")
 
 
-@pytest.mark.parametrize("op,p,M,N,K,n,seed", list(cases(1, 40)) + list(big_cases(2, 8)))
+@pytest.mark.parametrize("op,p,M,N,K,n,seed",
+                         list(cases(1, 40)) + list(cases(3, 60)) + list(big_cases(2, 8)) + list(big_cases(4, 8)))
 def test_random_shape(op, p, M, N, K, n, seed):
     print(f"random shape {op} p={p} M={M} N={N} K={K} n={n} seed={seed}", flush=True)
     g = torch.Generator().manual_seed(seed)
