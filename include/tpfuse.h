@@ -217,7 +217,8 @@ int tpf_matmul_allreduce(tpf_handle h, int p, int64_t M, int64_t N, int64_t K_sh
  * device (each GPU the library runs on holds it until the process ends; its
  * address is looked up when the first handle on that device is created).
  * A call whose scheduler needs more than that (tpf_workspace_size of the same
- * arguments) fails with TPF_ERR_UNSUPPORTED before anything is enqueued.  The
+ * arguments) fails with TPF_ERR_UNSUPPORTED before anything is enqueued;
+ * TPF_SCHED_STATIONARY needs none and runs at any size.  The
  * call makes no allocation of any kind.  Every call on one device shares that
  * device's array, which keeps the last call's partials: calls that overlap on
  * one device (other streams, other handles, other threads) race and must be

@@ -75,6 +75,29 @@ def test_noalloc_refuses_beyond_its_workspace_and_allocates_nothing():
     h.close()
 
 
+def test_noalloc_single_launch_needs_no_workspace_at_any_size():
+    # the output-stationary scheduler keeps the partials on chip, so a call
+    # whose partials (p = 4, [1536, 512] x [512, 4096]: 96 MiB) exceed the
+    # static workspace still runs, bit-identical to the existing entry point
+    h = tp.Handle(0)
+    p, M, K, N = 4, 1536, 512, 4096
+    g = torch.Generator().manual_seed(5)
+    X = [(torch.randn((M, K), generator=g)).to(torch.bfloat16).cuda() for _ in range(p)]
+    W = [(0.05 * torch.randn((K, N), generator=g)).to(torch.bfloat16).cuda() for _ in range(p)]
+    say(f"noalloc stationary p={p} M={M} N={N} K={K}")
+    ref = tp.matmul_allreduce(X, W, torch.bfloat16, sched="unfused", handle=h)
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    assert noalloc(h, X, W, Y, 1, "stationary") == tp.OK, tp.load().tpf_last_error()
+    torch.cuda.synchronize()
+    assert_bitwise(Y, ref, "noalloc stationary vs allreduce")
+    # the same call with a scheduler that needs the partials in memory is refused
+    Y2 = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    assert noalloc(h, X, W, Y2, 1, "unfused") == tp.ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert bool((Y2 == 7.0).all())
+    h.close()
+
+
 @pytest.mark.parametrize("sched", ["unfused", "persistent"])
 def test_noalloc_call_replays_from_a_graph(sched):
     """Captured in a HIP graph (the calls enqueue only kernels), several
